@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs for the CSA2 hot path.
+
+This module is the only code shared by the HIP path's callers and the CPU
+oracle's callers.  It draws random bytes and nothing else: it holds none of the
+method's arithmetic (no scoring, selection, decoding or attention).
+
+All draws use numpy's PCG64 (``numpy.random.default_rng(seed)``) in a fixed
+order, as float32, and are narrowed to bf16 by torch (round to nearest even).
+The identical CPU tensors are handed to the oracle and copied to the GPU.
+
+Distributions (the workloads are the pages' 128K-1M-token agentic contexts,
+for which no dataset is named; these stand in for them):
+  * indexer queries / keys, attention queries, main KV: N(0, 1)
+  * indexer head weights: U(0, 1)
+  * FP4 main-KV rows: each channel value drawn N(0, 1) and stored as the code
+    of the nearest E2M1 magnitude (0, .5, 1, 1.5, 2, 3, 4, 6; sign kept,
+    saturating at 6); one scale byte per 16 channels, 2^u with u ~ U(-4, 4),
+    written as an E4M3 byte with the mantissa truncated (values in
+    [2^-4, 2^4)).
+  * compression projection W_z and bias B: N(0, 0.02)
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+# Nearest-magnitude boundaries between consecutive E2M1 magnitudes
+# 0, .5, 1, 1.5, 2, 3, 4, 6 (midpoints); code magnitude index = number of
+# boundaries below |x|.
+_E2M1_BOUNDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+
+_CHUNK = 1 << 24  # draw in chunks to bound host memory
+
+
+def _normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    if std != 1.0:
+        out *= np.float32(std)
+    return out.reshape(shape)
+
+
+def normal_bf16(rng, shape, std: float = 1.0) -> torch.Tensor:
+    t = torch.empty(tuple(shape), dtype=torch.bfloat16)
+    flat = t.view(-1)
+    n = flat.numel()
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        a = rng.standard_normal(e - s, dtype=np.float32)
+        if std != 1.0:
+            a *= np.float32(std)
+        flat[s:e] = torch.from_numpy(a).to(torch.bfloat16)
+    return t
+
+
+def normal_f32(rng, shape, std: float = 1.0) -> torch.Tensor:
+    return torch.from_numpy(_normal(rng, shape, std))
+
+
+def uniform_f32(rng, shape, lo: float = 0.0, hi: float = 1.0) -> torch.Tensor:
+    return torch.from_numpy(rng.uniform(lo, hi, size=shape).astype(np.float32))
+
+
+def fp4_rows(rng, lead_shape, D: int) -> torch.Tensor:
+    """uint8 rows [..., D/2 + D/16]: D/2 code bytes (even channel in the low
+    nibble) then D/16 scale bytes."""
+    assert D % 16 == 0
+    rows = int(np.prod(lead_shape))
+    out = np.empty((rows, D // 2 + D // 16), dtype=np.uint8)
+    step = max(1, _CHUNK // D)
+    for s in range(0, rows, step):
+        e = min(rows, s + step)
+        x = rng.standard_normal((e - s, D), dtype=np.float32)
+        mag = np.searchsorted(_E2M1_BOUNDS, np.abs(x), side="right").astype(np.uint8)
+        code = mag | (np.signbit(x).astype(np.uint8) << 3)
+        out[s:e, : D // 2] = code[:, 0::2] | (code[:, 1::2] << 4)
+        u = rng.uniform(-4.0, 4.0, size=(e - s, D // 16))
+        ex = np.floor(u)
+        mant = np.floor((np.exp2(u - ex) - 1.0) * 8.0).clip(0, 7)
+        out[s:e, D // 2:] = ((ex + 7).astype(np.uint8) << 3) | mant.astype(np.uint8)
+    return torch.from_numpy(out.reshape(*lead_shape, D // 2 + D // 16))
+
+
+# --------------------------------------------------------------- workloads
+
+@dataclass
+class Decode:
+    """A decode workload: B sequences, Q query tokens each, N compressed entries."""
+    B: int
+    Q: int
+    N: int
+    HI: int
+    dI: int
+    H: int
+    D: int
+    k: int
+    idx_dtype: str = "bf16"  # "bf16" or "f32"
+    kv_fmt: str = "bf16"     # "bf16", "f32" or "fp4"
+    m: int = 4
+    P: int = 0
+    seed: int = 0
+    layers: list = field(default_factory=lambda: ["FULL"])
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+def make_decode(spec: Decode) -> dict:
+    """Draw, in this order: kI, kv, then per layer (qI, w if the layer runs the
+    indexer) and q."""
+    rng = np.random.default_rng(spec.seed)
+    idx_draw = normal_bf16 if spec.idx_dtype == "bf16" else normal_f32
+    out = {"spec": spec}
+    out["kI"] = idx_draw(rng, (spec.B, spec.N, spec.dI))
+    if spec.kv_fmt == "fp4":
+        out["kv"] = fp4_rows(rng, (spec.B, spec.N), spec.D)
+    elif spec.kv_fmt == "bf16":
+        out["kv"] = normal_bf16(rng, (spec.B, spec.N, spec.D))
+    else:
+        out["kv"] = normal_f32(rng, (spec.B, spec.N, spec.D))
+    q_draw = normal_f32 if spec.kv_fmt == "f32" else normal_bf16
+    out["layers"] = []
+    for mode in spec.layers:
+        lay = {"mode": mode}
+        if mode in ("FULL", "REINDEX"):
+            lay["qI"] = idx_draw(rng, (spec.B, spec.Q, spec.HI, spec.dI))
+            lay["w"] = uniform_f32(rng, (spec.B, spec.Q, spec.HI))
+        lay["q"] = q_draw(rng, (spec.B, spec.Q, spec.H, spec.D))
+        out["layers"].append(lay)
+    return out
+
+
+def tiny_full(seed: int = 0) -> Decode:
+    """Tiny Full-mode decode: 2048 tokens at m=4 -> 512 entries; indexer 4 x 64
+    fp32; top-64; 8 heads x 128 fp32; scale 1/sqrt(128)."""
+    return Decode(B=1, Q=1, N=512, HI=4, dI=64, H=8, D=128, k=64, idx_dtype="f32", kv_fmt="f32", seed=seed)
+
+
+def decode_128k(seed: int = 1, B: int = 16, N: int = 32768) -> Decode:
+    """128K-token decode (32,768 entries at m=4), bf16 indexer 64 x 128, top-2048,
+    64 heads x 512 bf16."""
+    return Decode(B=B, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=2048, seed=seed)
+
+
+def decode_128k_fp4_group(seed: int = 2, B: int = 16, N: int = 32768) -> Decode:
+    """As decode_128k with FP4 main KV, one group of 1 Full + 5 Reuse layers."""
+    return Decode(B=B, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=2048, kv_fmt="fp4", seed=seed,
+                  layers=["FULL"] + ["REUSE"] * 5)
+
+
+def decode_1m_hier(seed: int = 3, B: int = 4, N: int = 262144, P: int = 16384) -> Decode:
+    """1M-token decode (262,144 entries at m=4): a Full layer picks a
+    16,384-position pool and its own top-2048, then 3 Reindex layers rescore
+    only the pool; FP4 main KV, 64 heads x 512."""
+    return Decode(B=B, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=2048, kv_fmt="fp4", P=P, seed=seed,
+                  layers=["FULL"] + ["REINDEX"] * 3)
+
+
+@dataclass
+class Prefill:
+    """A causal prefill chunk of Qc query tokens at the end of a T-token context."""
+    T: int = 65536
+    Qc: int = 4096
+    m: int = 4
+    D: int = 512
+    dI: int = 128
+    HI: int = 64
+    H: int = 64
+    k: int = 2048
+    seed: int = 4
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+def make_prefill(spec: Prefill) -> dict:
+    """Draw, in this order: X, X_I, W_z, W_z^I, B, B^I, qI, q, w; q_pos."""
+    rng = np.random.default_rng(spec.seed)
+    out = {"spec": spec}
+    out["x"] = normal_bf16(rng, (spec.T, spec.D))
+    out["xI"] = normal_bf16(rng, (spec.T, spec.dI))
+    out["wz"] = normal_bf16(rng, (spec.D, spec.D), std=0.02)
+    out["wzI"] = normal_bf16(rng, (spec.dI, spec.dI), std=0.02)
+    out["bias"] = normal_f32(rng, (2 * spec.m, spec.D), std=0.02)
+    out["biasI"] = normal_f32(rng, (2 * spec.m, spec.dI), std=0.02)
+    out["qI"] = normal_bf16(rng, (1, spec.Qc, spec.HI, spec.dI))
+    out["q"] = normal_bf16(rng, (1, spec.Qc, spec.H, spec.D))
+    out["w"] = uniform_f32(rng, (1, spec.Qc, spec.HI))
+    out["q_pos"] = torch.arange(spec.T - spec.Qc, spec.T, dtype=torch.int64).view(1, spec.Qc)
+    return out

@@ -1,0 +1,69 @@
+"""Pins for the oracle's FP4 / E4M3 decoding (format of the FP4 main KV on
+"Recall之王 祭出Reuse", section "把KV Cache压到极致的几把杀手锏")."""
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from oracle_helpers import decode_fp4_independent, e2m1_table, e4m3_table
+from sparse_long_context_csa2_amd import synth
+
+
+def test_e4m3_every_byte_matches_torch_float8():
+    ref = e4m3_table()
+    for b in range(256):
+        v = oracle.e4m3(b)
+        if math.isnan(ref[b]):
+            assert math.isnan(v), b
+        else:
+            assert v == ref[b] and math.copysign(1, v) == math.copysign(1, ref[b]), (b, v, ref[b])
+
+
+def test_e2m1_every_code_matches_ocp_table():
+    ref = e2m1_table()
+    for c in range(16):
+        v = oracle.e2m1(c)
+        assert v == ref[c] and math.copysign(1, v) == math.copysign(1, ref[c]), (c, v, ref[c])
+
+
+def test_fp4_row_byte_layout_worked_example():
+    # D = 32: 16 code bytes then 2 scale bytes.  Byte 0 = 0x21: channel 0 is
+    # the low nibble (code 1 = 0.5), channel 1 the high nibble (code 2 = 1.0).
+    # Byte 7 = 0xF7: channel 14 = code 7 (6.0), channel 15 = code 15 (-6.0).
+    # Byte 8 = 0x9B: channel 16 = code 11 (-1.5), channel 17 = code 9 (-0.5).
+    # Scale 0 = 0x38 (1.0) covers channels 0..15; scale 1 = 0x44 (2^1 * 1.5 = 3.0)
+    # covers channels 16..31.
+    row = np.zeros(18, dtype=np.uint8)
+    row[0], row[7], row[8] = 0x21, 0xF7, 0x9B
+    row[16], row[17] = 0x38, 0x44
+    got = oracle.decode_rows(row[None, :], 32)[0]
+    want = np.zeros(32)
+    want[0], want[1], want[14], want[15] = 0.5, 1.0, 6.0, -6.0
+    want[16], want[17] = -1.5 * 3.0, -0.5 * 3.0
+    assert np.array_equal(got, want)
+
+
+def test_fp4_rows_match_independent_table_decode():
+    rng = np.random.default_rng(11)
+    rows = synth.fp4_rows(rng, (3, 40), 64).numpy()
+    got = oracle.decode_rows(rows, 64)
+    want = decode_fp4_independent(rows, 64)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_and_f32_rows_decode_exactly():
+    rng = np.random.default_rng(5)
+    x = synth.normal_bf16(rng, (4, 48))
+    got = oracle.decode_rows(x, 48)
+    assert np.array_equal(got, x.to(torch.float64).numpy())
+    y = synth.normal_f32(rng, (2, 16))
+    assert np.array_equal(oracle.decode_rows(y, 16), y.numpy().astype(np.float64))
+
+
+def test_synth_fp4_scales_in_range():
+    rng = np.random.default_rng(0)
+    rows = synth.fp4_rows(rng, (200,), 512).numpy()
+    sc = e4m3_table()[rows[:, 256:]]
+    assert sc.min() >= 2.0 ** -4 and sc.max() < 2.0 ** 4
+    assert rows.shape == (200, 288)
