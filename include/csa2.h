@@ -1,0 +1,222 @@
+/*
+ * csa2.h -- C ABI of the MI355X (gfx950) CSA2 hot-path library, libcsa2.so.
+ *
+ * CSA2 (Compressed Sparse Attention 2) step of DeepSeek V4.1 Flash's global
+ * attention branch: for each query token, score every compressed KV entry with
+ * the lightning indexer, keep the top-k, gather those entries (optionally
+ * decoding FP4 E2M1 values with one E4M3 scale per 16 channels) and run softmax
+ * attention of every query head over that one shared entry set.  Layers run in
+ * Full, Reindex or Reuse mode.
+ *
+ * Conventions for every entry point
+ *  - Tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *    contiguous (last dimension fastest), 16-byte aligned.  The library never
+ *    allocates, frees or keeps them after the call returns.
+ *  - Temporary memory comes only from the caller's workspace (ws, ws_bytes),
+ *    sized by the matching *_workspace_size function; NULL with 0 bytes is
+ *    allowed when that function returns 0.  Workspace must be 256-byte aligned.
+ *  - `stream` is the caller's hipStream_t (NULL = the default stream).  Work is
+ *    enqueued asynchronously on it; no call synchronises with the host, and no
+ *    call records a memset node, so a call may be captured into a HIP graph.
+ *  - Return value: CSA2_OK, or an error status.  Arguments are validated before
+ *    anything is enqueued, so a call that fails validation has no effect.
+ *    CSA2_EHIP means a launch failed (state of the outputs undefined).  The
+ *    message of the last failure on the calling thread is csa2_last_error().
+ *    No C++ exception crosses this interface.
+ *  - Preconditions that are documented but not checked: floating inputs are
+ *    finite; E4M3 scale bytes are not NaN; outputs do not alias inputs; the
+ *    stream is valid on the current device.
+ *  - Calls that overlap on one stream are ordered by that stream; concurrent
+ *    calls on different streams must use different workspaces.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_API __attribute__((visibility("default")))
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_EINVAL = 1,       /* bad argument (null pointer, size, alignment, mode/pointer mismatch) */
+    CSA2_EUNSUPPORTED = 2, /* valid request with no kernel (e.g. dtype/shape combination) */
+    CSA2_EWORKSPACE = 3,   /* workspace smaller than *_workspace_size */
+    CSA2_EHIP = 4,         /* a HIP launch or runtime call failed */
+    CSA2_EINTERNAL = 5     /* unexpected internal failure */
+} csa2_status;
+
+/* Element formats.
+ * CSA2_F32, CSA2_BF16: plain rows of D elements.
+ * CSA2_FP4: a row of D channels is D/2 + D/16 bytes: D/2 bytes of 4-bit E2M1
+ *   codes (channel 2i in the low nibble of byte i, channel 2i+1 in the high
+ *   nibble), then D/16 E4M3 ("FN", OCP 8-bit float) scale bytes, scale b
+ *   covering channels 16b..16b+15.  Value = e2m1(code) * e4m3(scale), which
+ *   is exactly representable in bf16.  ("Recall之王 祭出Reuse", section
+ *   "把KV Cache压到极致的几把杀手锏": FP4 main KV cache, E2M1 with one E4M3
+ *   scale per 16 channels.)  Main KV only. */
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_FP4 = 2 } csa2_dtype;
+
+/* Layer modes (V4.1 Flash video transcript on prism.simon-ai.net, the passage
+ * introducing CSA2's three modes; "Recall之王 祭出Reuse", same section):
+ *   CSA2_FULL    -- run the indexer over every visible entry, keep top-k (and
+ *                   optionally the top-P candidate pool), attend.
+ *   CSA2_REINDEX -- reuse the shared main KV and indexer keys; score only the
+ *                   candidate pool with this layer's own indexer queries, keep
+ *                   top-k of the pool, attend.
+ *   CSA2_REUSE   -- reuse main KV and the previous top-k indices; no indexer,
+ *                   attention only. */
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
+
+/* ---------------------------------------------------------------------------
+ * csa2_compress -- token compression into compressed entries.
+ *
+ * "读完这篇，你就搞懂 DeepSeek v4 了" (note.crab.center): the HCA "压缩机制"
+ * paragraphs (eqs. 10, 11) define CSA's compression by contrast -- groups of m
+ * tokens, two consecutive groups concatenated, a per-channel softmax weight
+ * over a projection Z plus a learnable bias B.  Reading taken: entry i pools
+ * the previous and its own group (2m tokens); for channel c and window
+ * position r (0..2m-1, token t):
+ *     l_r[c] = sum_d x_t[d] * wz[d][c] + bias[r][c]
+ *     out_i[c] = sum_r softmax_r(l[c]) * x_t[c]
+ * Window positions before token 0 are dropped.
+ *
+ * x:    [rows, D] in dt (CSA2_F32 or CSA2_BF16).  halo = 0: rows = n_out*m and
+ *       x starts at token 0.  halo = 1: rows = (n_out+1)*m, the first m rows
+ *       are the previous group of the first output entry.
+ * wz:   [D, D] in dt.  bias: [2m, D] fp32.  out: [n_out, D] in dt (fp32 math,
+ *       rounded to nearest even on store).
+ * Limits: 1 <= m <= 16, D % 16 == 0, n_out >= 1.
+ * ------------------------------------------------------------------------- */
+CSA2_API size_t csa2_compress_workspace_size(int dt, int64_t n_out, int32_t D, int32_t m, int32_t halo);
+CSA2_API int csa2_compress(const void *x, int dt, int64_t n_out, int32_t D, int32_t m, int32_t halo,
+                           const void *wz, const float *bias, void *out, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* ---------------------------------------------------------------------------
+ * csa2_index_score -- lightning-indexer scores.
+ *
+ * "读完这篇，你就搞懂 DeepSeek v4 了", section "闪电索引机制（对应步骤二）", eq. (8):
+ * every compressed entry is scored against the query token per indexer head,
+ * head scores are weighted and summed (DSA of V3.2, with its per-head ReLU):
+ *     s(j) = sum_h w_h * ReLU(qI_h . kI_j)
+ * One key row per entry is shared by all heads.
+ *
+ * qI [B,Q,HI,dI] and kI [B,N,dI] in dt (CSA2_F32 or CSA2_BF16); w [B,Q,HI] fp32.
+ * q_pos [B,Q] absolute token positions, or NULL: with q_pos, entry j is visible
+ *   to the query only if (j+1)*m <= q_pos+1 (complete groups); without it all
+ *   N entries are visible.
+ * cand [B,Q,P] or NULL: with cand, slot p scores entry cand[p]; -1 = empty.
+ * scores [B,Q,N] (or [B,Q,P]) fp32 out; invisible entries and empty slots get
+ *   -inf.  Accumulation order is the kernel's (matrix cores for bf16).
+ * err [B,Q] fp32 out or NULL: a rigorous per-query bound E with
+ *   |scores - s_exact| <= E for every scored entry, where s_exact is the
+ *   binary64 value of the formula in its sequential order.
+ * ------------------------------------------------------------------------- */
+CSA2_API size_t csa2_index_score_workspace_size(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t N,
+                                                int32_t P);
+CSA2_API int csa2_index_score(const void *qI, const float *w, const void *kI, int dt, int32_t B, int32_t Q,
+                              int32_t HI, int32_t dI, int64_t N, const int64_t *q_pos, int32_t m,
+                              const int32_t *cand, int32_t P, float *scores, float *err, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * csa2_topk -- exact top-k of given fp32 scores.
+ *
+ * Same section of the same page: keep the k highest-scoring entries.  Order is
+ * (score descending, entry index ascending); slots scoring -inf, and slots
+ * whose cand entry is -1, are never kept.  Output: the kept entry indices in
+ * ascending order, then -1 padding; count = number kept = min(k, selectable).
+ *
+ * scores [B,Q,n] fp32; cand [B,Q,n] or NULL (entry index of slot p is cand[p],
+ *   else p; cand rows must be strictly ascending over their non-negative
+ *   entries, which the pool produced by csa2_layer is).
+ * idx [B,Q,k] int32 out; count [B,Q] int32 out or NULL.  1 <= k.
+ * The result is bit-exact (pure comparison, no arithmetic on the scores).
+ * ------------------------------------------------------------------------- */
+CSA2_API size_t csa2_topk_workspace_size(int32_t B, int32_t Q, int64_t n, int32_t k);
+CSA2_API int csa2_topk(const float *scores, int32_t B, int32_t Q, int64_t n, const int32_t *cand, int32_t k,
+                       int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * csa2_sparse_attn -- gather + (FP4 decode) + shared-KV attention.
+ *
+ * Same page, section "注意力计算（对应步骤三）", eq. (9): standard attention
+ * with shared KV -- the k entries kept by the indexer form one matrix C that
+ * every query head uses as both keys and values:
+ *     a_j = scale * q_h . C_j,  o_h = sum_j softmax(a)_j C_j,  lse_h = logsumexp(a)
+ *
+ * q [B,Q,H,D] in q_dt (CSA2_F32 or CSA2_BF16); kv [B,N,row] in kv_dt
+ *   (CSA2_F32, CSA2_BF16 or CSA2_FP4; FP4 needs q_dt = CSA2_BF16).
+ * idx [B,Q,k] int32 entry indices in [0, N) or -1 (skipped).
+ * out [B,Q,H,D] in q_dt; lse [B,Q,H] fp32 or NULL.  A query with no listed
+ *   entry gets out = 0 and lse = -inf.
+ * The result for one query does not depend on B, Q or the other queries
+ *   (fixed split of the k entries, fixed reduction order).
+ * ------------------------------------------------------------------------- */
+CSA2_API size_t csa2_sparse_attn_workspace_size(int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H, int32_t D,
+                                                int32_t k);
+CSA2_API int csa2_sparse_attn(const void *q, const void *kv, int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H,
+                              int32_t D, int64_t N, const int32_t *idx, int32_t k, float scale, void *out,
+                              float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * csa2_layer -- one CSA2 layer (FULL, REINDEX or REUSE), selection certified
+ * bit-exact.
+ *
+ * FULL    = index score over all visible entries -> top-k (+ top-P pool) ->
+ *           attention.
+ * REINDEX = index score of the P pool slots (shared kI, own qI/w) -> top-k of
+ *           the pool (ties by entry index) -> attention on the shared kv.
+ *           "Recall之王 祭出Reuse", same section: the hierarchical indexer --
+ *           the first Full layer picks a candidate pool of at most 16,384
+ *           positions and later Reindex layers score only inside it.
+ * REUSE   = attention with the given idx.
+ * The selection (idx, pool, count) equals the top-k of the binary64 scores of
+ * the formula in csa2_index_score, taken in sequential order, exactly: entries
+ * whose fp32 score is within the error bound of the k-th are rescored in
+ * binary64 on the GPU before the cut.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    int32_t mode;         /* csa2_mode */
+    int32_t B, Q;         /* sequences, query tokens per sequence */
+    int64_t N;            /* compressed entries per sequence */
+    int32_t m;            /* group size (for q_pos visibility) */
+    int32_t HI, dI;       /* indexer heads and dim */
+    int32_t idx_dt;       /* dtype of qI and kI (CSA2_F32 or CSA2_BF16) */
+    int32_t k;            /* top-k (>= 1) */
+    int32_t P;            /* FULL: pool size (0 = no pool); REINDEX: pool slots */
+    int32_t H, D;         /* attention heads and dim (kv row width D) */
+    int32_t q_dt, kv_dt;  /* dtype of q/out; format of kv */
+    float scale;          /* softmax scale */
+    const int64_t *q_pos; /* [B,Q] or NULL (decode: all N visible) */
+    const void *qI;       /* [B,Q,HI,dI] (FULL, REINDEX) */
+    const float *w;       /* [B,Q,HI]    (FULL, REINDEX) */
+    const void *kI;       /* [B,N,dI]    (FULL: own; REINDEX: the Full layer's, shared) */
+    int32_t *pool;        /* [B,Q,P] FULL out (if P > 0) / REINDEX in; ascending, -1 padded */
+    int32_t *idx;         /* [B,Q,k] FULL/REINDEX out, REUSE in; ascending, -1 padded */
+    int32_t *count;       /* [B,Q] out, or NULL (number of valid idx entries) */
+    float *scores;        /* [B,Q,N] (FULL) or [B,Q,P] (REINDEX) fp32 out, or NULL */
+    const void *q;        /* [B,Q,H,D] */
+    const void *kv;       /* [B,N,row] (shared across layers of a group) */
+    void *out;            /* [B,Q,H,D] in q_dt */
+    float *lse;           /* [B,Q,H] or NULL */
+} csa2_layer_args;
+
+CSA2_API size_t csa2_layer_workspace_size(const csa2_layer_args *a);
+CSA2_API int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream);
+
+/* Message of the last non-OK status returned on the calling thread. */
+CSA2_API const char *csa2_last_error(void);
+/* Library version string. */
+CSA2_API const char *csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

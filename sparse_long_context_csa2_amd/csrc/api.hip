@@ -1,0 +1,279 @@
+// C ABI of the CSA2 hot path (include/csa2.h): argument validation before any
+// launch, workspace carving and the Full / Reindex / Reuse mode sequencing.
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+using csa2::Error;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void need_ptr(const void *p, const char *name) {
+    if (!p) throw Error(CSA2_EINVAL, std::string(name) + " is NULL");
+    if (!aligned16(p)) throw Error(CSA2_EINVAL, std::string(name) + " is not 16-byte aligned");
+}
+void opt_ptr(const void *p, const char *name) {
+    if (p && !aligned16(p)) throw Error(CSA2_EINVAL, std::string(name) + " is not 16-byte aligned");
+}
+void need_ws(void *ws, size_t ws_bytes, size_t need) {
+    if (ws_bytes < need) throw Error(CSA2_EWORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                                          std::to_string(need));
+    if (need && !ws) throw Error(CSA2_EINVAL, "workspace is NULL");
+    if (ws && (reinterpret_cast<uintptr_t>(ws) & 255u)) throw Error(CSA2_EINVAL, "workspace is not 256-byte aligned");
+}
+void need_plain_dt(int dt, const char *name) {
+    if (dt != CSA2_F32 && dt != CSA2_BF16) throw Error(CSA2_EINVAL, std::string(name) + " must be CSA2_F32 or CSA2_BF16");
+}
+
+template <class F>
+int guarded(F &&f) {
+    try {
+        f();
+        return CSA2_OK;
+    } catch (const Error &e) {
+        g_last_error = e.what();
+        return e.code;
+    } catch (const std::exception &e) {
+        g_last_error = e.what();
+        return CSA2_EINTERNAL;
+    } catch (...) {
+        g_last_error = "unknown failure";
+        return CSA2_EINTERNAL;
+    }
+}
+
+// ------------------------------------------------------------- indexer
+void check_index_args(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t N, int32_t P) {
+    need_plain_dt(dt, "indexer dtype");
+    if (B < 1 || Q < 1 || HI < 1 || dI < 1 || N < 1) throw Error(CSA2_EINVAL, "B, Q, HI, dI and N must be >= 1");
+    if (N > INT32_MAX || P < 0) throw Error(CSA2_EINVAL, "N must fit int32 and P must be >= 0");
+    if (!csa2::index_mfma_supported(dt, HI, dI) && !csa2::index_valu_supported(HI, dI))
+        throw Error(CSA2_EUNSUPPORTED, "no indexer kernel for HI*dI > 16384 with this shape");
+    if (dt == CSA2_BF16 && dI % 8) throw Error(CSA2_EINVAL, "bf16 indexer rows need dI % 8 == 0");
+}
+
+size_t index_ws(int32_t B, int32_t Q, int64_t n) {
+    csa2::Carve c(nullptr, 0);
+    c.take<csa2::TileStat>((size_t)B * Q * ((n + csa2::TILE - 1) / csa2::TILE));
+    return c.used;
+}
+
+// --------------------------------------------------------------- layer
+struct LayerSizes {
+    int64_t n;  // scored slots per query
+    csa2::SelPlan sel;
+    csa2::AttnPlan att;
+    size_t scores, stats, err, selws, attws, total;
+};
+
+LayerSizes layer_sizes(const csa2_layer_args *a) {
+    LayerSizes z{};
+    const int BQ = a->B * a->Q;
+    z.att = csa2::attn_plan(a->q_dt, a->kv_dt, a->B, a->Q, a->H, a->D, a->N, a->k);
+    z.attws = csa2::attn_workspace(z.att);
+    if (a->mode == CSA2_REUSE) {
+        z.total = z.attws;
+        return z;
+    }
+    z.n = a->mode == CSA2_FULL ? a->N : a->P;
+    z.sel = csa2::sel_plan(BQ, z.n, a->k, a->mode == CSA2_FULL ? a->P : 0, true);
+    csa2::Carve c(nullptr, 0);
+    z.scores = a->scores ? 0 : (c.take<float>((size_t)BQ * z.n), (size_t)BQ * z.n * 4);
+    size_t before = c.used;
+    c.take<csa2::TileStat>((size_t)BQ * z.sel.ntiles);
+    z.stats = c.used - before;
+    before = c.used;
+    c.take<double>((size_t)BQ);
+    z.err = c.used - before;
+    z.selws = csa2::sel_workspace(z.sel, false);
+    z.total = c.used + z.selws + z.attws;
+    return z;
+}
+
+void check_layer(const csa2_layer_args *a) {
+    if (!a) throw Error(CSA2_EINVAL, "args is NULL");
+    if (a->mode != CSA2_FULL && a->mode != CSA2_REINDEX && a->mode != CSA2_REUSE)
+        throw Error(CSA2_EINVAL, "unknown mode");
+    if (a->B < 1 || a->Q < 1 || a->N < 1 || a->k < 1 || a->H < 1 || a->D < 1)
+        throw Error(CSA2_EINVAL, "B, Q, N, k, H and D must be >= 1");
+    need_ptr(a->q, "q");
+    need_ptr(a->kv, "kv");
+    need_ptr(a->out, "out");
+    opt_ptr(a->lse, "lse");
+    opt_ptr(a->count, "count");
+    need_ptr(a->idx, "idx");
+    need_plain_dt(a->q_dt, "q dtype");
+    if (a->kv_dt != CSA2_F32 && a->kv_dt != CSA2_BF16 && a->kv_dt != CSA2_FP4)
+        throw Error(CSA2_EINVAL, "unknown kv format");
+    if (a->kv_dt == CSA2_FP4 && (a->D % 16 || a->q_dt != CSA2_BF16))
+        throw Error(CSA2_EINVAL, "FP4 kv needs D % 16 == 0 and bf16 queries");
+    if (a->kv_dt == CSA2_BF16 && a->D % 8) throw Error(CSA2_EINVAL, "bf16 kv rows need D % 8 == 0");
+    if (!csa2::attn_supported(csa2::attn_plan(a->q_dt, a->kv_dt, a->B, a->Q, a->H, a->D, a->N, a->k)))
+        throw Error(CSA2_EUNSUPPORTED, "no attention kernel for this shape (vector path needs D + k <= 16384)");
+    if (a->mode == CSA2_REUSE) return;
+    need_ptr(a->qI, "qI");
+    need_ptr(a->w, "w");
+    need_ptr(a->kI, "kI");
+    opt_ptr(a->scores, "scores");
+    opt_ptr(a->q_pos, "q_pos");
+    if (a->q_pos && a->m < 1) throw Error(CSA2_EINVAL, "m must be >= 1 with q_pos");
+    if (a->mode == CSA2_FULL) {
+        if (a->P < 0) throw Error(CSA2_EINVAL, "P must be >= 0");
+        if (a->P > 0) need_ptr(a->pool, "pool");
+        check_index_args(a->idx_dt, a->B, a->Q, a->HI, a->dI, a->N, a->P);
+    } else {
+        if (a->P < 1) throw Error(CSA2_EINVAL, "REINDEX needs P >= 1 pool slots");
+        need_ptr(a->pool, "pool");
+        check_index_args(a->idx_dt, a->B, a->Q, a->HI, a->dI, a->N, a->P);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *csa2_last_error(void) { return g_last_error.c_str(); }
+const char *csa2_version(void) { return "csa2-mi355x 0.1 (gfx950)"; }
+
+size_t csa2_compress_workspace_size(int dt, int64_t n_out, int32_t D, int32_t m, int32_t halo) {
+    if (n_out < 1 || D < 1 || m < 1) return 0;
+    return csa2::compress_workspace(dt, n_out, D, m, halo);
+}
+
+int csa2_compress(const void *x, int dt, int64_t n_out, int32_t D, int32_t m, int32_t halo, const void *wz,
+                  const float *bias, void *out, void *ws, size_t ws_bytes, void *stream) {
+    return guarded([&] {
+        need_plain_dt(dt, "dtype");
+        if (n_out < 1 || D < 1 || m < 1 || m > 16 || (halo != 0 && halo != 1))
+            throw Error(CSA2_EINVAL, "need n_out >= 1, D >= 1, 1 <= m <= 16, halo in {0,1}");
+        if (D % 16) throw Error(CSA2_EINVAL, "D must be a multiple of 16");
+        need_ptr(x, "x");
+        need_ptr(wz, "wz");
+        need_ptr(bias, "bias");
+        need_ptr(out, "out");
+        need_ws(ws, ws_bytes, csa2::compress_workspace(dt, n_out, D, m, halo));
+        csa2::compress_run(x, dt, n_out, D, m, halo, wz, bias, out, ws, ws_bytes, (hipStream_t)stream);
+    });
+}
+
+size_t csa2_index_score_workspace_size(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t N, int32_t P) {
+    (void)dt;
+    (void)HI;
+    (void)dI;
+    if (B < 1 || Q < 1) return 0;
+    return index_ws(B, Q, P > 0 ? P : N);
+}
+
+int csa2_index_score(const void *qI, const float *w, const void *kI, int dt, int32_t B, int32_t Q, int32_t HI,
+                     int32_t dI, int64_t N, const int64_t *q_pos, int32_t m, const int32_t *cand, int32_t P,
+                     float *scores, float *err, void *ws, size_t ws_bytes, void *stream) {
+    return guarded([&] {
+        check_index_args(dt, B, Q, HI, dI, N, P);
+        need_ptr(qI, "qI");
+        need_ptr(w, "w");
+        need_ptr(kI, "kI");
+        need_ptr(scores, "scores");
+        opt_ptr(err, "err");
+        opt_ptr(q_pos, "q_pos");
+        opt_ptr(cand, "cand");
+        if (cand && P < 1) throw Error(CSA2_EINVAL, "cand needs P >= 1");
+        if (q_pos && m < 1) throw Error(CSA2_EINVAL, "m must be >= 1 with q_pos");
+        const int64_t n = cand ? P : N;
+        need_ws(ws, ws_bytes, index_ws(B, Q, n));
+        hipStream_t s = (hipStream_t)stream;
+        csa2::Carve c(ws, ws_bytes);
+        const int ntiles = (int)((n + csa2::TILE - 1) / csa2::TILE);
+        auto *stats = c.take<csa2::TileStat>((size_t)B * Q * ntiles);
+        csa2::launch_index_score(qI, dt, w, kI, B, Q, HI, dI, N, q_pos, m, cand, cand ? P : 0, scores, stats, s);
+        if (err) csa2::launch_err_bound(qI, dt, w, B * Q, HI, dI, stats, ntiles, err, nullptr, s);
+    });
+}
+
+size_t csa2_topk_workspace_size(int32_t B, int32_t Q, int64_t n, int32_t k) {
+    if (B < 1 || Q < 1 || n < 1 || k < 1) return 0;
+    return csa2::sel_workspace(csa2::sel_plan(B * Q, n, k, 0, false), true);
+}
+
+int csa2_topk(const float *scores, int32_t B, int32_t Q, int64_t n, const int32_t *cand, int32_t k, int32_t *idx,
+              int32_t *count, void *ws, size_t ws_bytes, void *stream) {
+    return guarded([&] {
+        if (B < 1 || Q < 1 || n < 1 || k < 1) throw Error(CSA2_EINVAL, "B, Q, n and k must be >= 1");
+        if (n > INT32_MAX) throw Error(CSA2_EINVAL, "n must fit int32");
+        need_ptr(scores, "scores");
+        need_ptr(idx, "idx");
+        opt_ptr(cand, "cand");
+        opt_ptr(count, "count");
+        const csa2::SelPlan p = csa2::sel_plan(B * Q, n, k, 0, false);
+        need_ws(ws, ws_bytes, csa2::sel_workspace(p, true));
+        csa2::sel_run(p, scores, cand, nullptr, nullptr, nullptr, idx, count, nullptr, ws, ws_bytes,
+                      (hipStream_t)stream);
+    });
+}
+
+size_t csa2_sparse_attn_workspace_size(int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H, int32_t D, int32_t k) {
+    if (B < 1 || Q < 1 || H < 1 || D < 1 || k < 1) return 0;
+    return csa2::attn_workspace(csa2::attn_plan(q_dt, kv_dt, B, Q, H, D, 1, k));
+}
+
+int csa2_sparse_attn(const void *q, const void *kv, int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H, int32_t D,
+                     int64_t N, const int32_t *idx, int32_t k, float scale, void *out, float *lse, void *ws,
+                     size_t ws_bytes, void *stream) {
+    return guarded([&] {
+        if (B < 1 || Q < 1 || H < 1 || D < 1 || N < 1 || k < 1)
+            throw Error(CSA2_EINVAL, "B, Q, H, D, N and k must be >= 1");
+        need_plain_dt(q_dt, "q dtype");
+        if (kv_dt != CSA2_F32 && kv_dt != CSA2_BF16 && kv_dt != CSA2_FP4) throw Error(CSA2_EINVAL, "unknown kv format");
+        if (kv_dt == CSA2_FP4 && (D % 16 || q_dt != CSA2_BF16))
+            throw Error(CSA2_EINVAL, "FP4 kv needs D % 16 == 0 and bf16 queries");
+        if (kv_dt == CSA2_BF16 && D % 8) throw Error(CSA2_EINVAL, "bf16 kv rows need D % 8 == 0");
+        need_ptr(q, "q");
+        need_ptr(kv, "kv");
+        need_ptr(idx, "idx");
+        need_ptr(out, "out");
+        opt_ptr(lse, "lse");
+        const csa2::AttnPlan p = csa2::attn_plan(q_dt, kv_dt, B, Q, H, D, N, k);
+        if (!csa2::attn_supported(p))
+            throw Error(CSA2_EUNSUPPORTED, "no attention kernel for this shape (vector path needs D + k <= 16384)");
+        need_ws(ws, ws_bytes, csa2::attn_workspace(p));
+        csa2::attn_run(p, q, kv, idx, scale, out, lse, ws, ws_bytes, (hipStream_t)stream);
+    });
+}
+
+size_t csa2_layer_workspace_size(const csa2_layer_args *a) {
+    if (!a || a->B < 1 || a->Q < 1 || a->k < 1 || a->H < 1 || a->D < 1) return 0;
+    return layer_sizes(a).total;
+}
+
+int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream) {
+    return guarded([&] {
+        check_layer(a);
+        const LayerSizes z = layer_sizes(a);
+        need_ws(ws, ws_bytes, z.total);
+        hipStream_t s = (hipStream_t)stream;
+        csa2::Carve c(ws, ws_bytes);
+        if (a->mode != CSA2_REUSE) {
+            const int BQ = a->B * a->Q;
+            float *scores = a->scores ? a->scores : c.take<float>((size_t)BQ * z.n);
+            auto *stats = c.take<csa2::TileStat>((size_t)BQ * z.sel.ntiles);
+            auto *err = c.take<double>((size_t)BQ);
+            void *selws = c.base + c.used;
+            c.used += z.selws;
+            const int32_t *cand = a->mode == CSA2_REINDEX ? a->pool : nullptr;
+            csa2::launch_index_score(a->qI, a->idx_dt, a->w, a->kI, a->B, a->Q, a->HI, a->dI, a->N, a->q_pos, a->m,
+                                     cand, cand ? a->P : 0, scores, stats, s);
+            csa2::launch_err_bound(a->qI, a->idx_dt, a->w, BQ, a->HI, a->dI, stats, z.sel.ntiles, nullptr, err, s);
+            const csa2::RescoreArgs rs{a->qI, a->idx_dt, a->w, a->kI, a->Q, a->HI, a->dI, a->N};
+            csa2::sel_run(z.sel, scores, cand, stats, err, &rs, a->idx, a->count,
+                          a->mode == CSA2_FULL && a->P > 0 ? a->pool : nullptr, selws, z.selws, s);
+        }
+        void *attws = c.base + c.used;
+        csa2::attn_run(z.att, a->q, a->kv, a->idx, a->scale, a->out, a->lse, attws, z.attws, s);
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,314 @@
+// Lightning-indexer score kernels for gfx950.
+//
+// "读完这篇，你就搞懂 DeepSeek v4 了", section "闪电索引机制（对应步骤二）", eq. (8):
+// every compressed entry j is scored against the query token per indexer head,
+// the head scores are weighted and summed -- with DSA's per-head ReLU:
+//     s(j) = sum_h w_h * ReLU(q_h . k_j)
+//
+// Decode streams the whole key cache once per query (HBM-bound), but the
+// 64-head contraction is 64 FLOP per key byte, above the fp32 VALU ridge, so
+// the bf16 kernel runs it on the matrix cores: v_mfma_f32_16x16x32_bf16 with
+// the query heads as the A operand (resident in registers for the block) and
+// 16 key rows per B operand, loaded straight from HBM with 64-byte coalesced
+// row segments.  The epilogue (ReLU, head weights, head sum) and the per-entry
+// squared key norm used by the error bound are fused; each block also writes
+// min/max/count statistics of its 256 scores for the selection that follows.
+#include "internal.h"
+
+namespace csa2 {
+
+namespace {
+
+constexpr float NEG_INF = -__builtin_inff();
+constexpr float POS_INF = __builtin_inff();
+
+__device__ __forceinline__ int64_t visible_entries(const int64_t *q_pos, int bq, int m, int64_t N) {
+    if (!q_pos) return N;
+    int64_t t = q_pos[bq];
+    if (t < 0) return 0;
+    int64_t v = (t + 1) / m;
+    return v < N ? v : N;
+}
+
+// Block-wide reduction of per-thread tile statistics; thread 0 writes.
+__device__ void reduce_tile_stat(float smin, float smax, uint32_t nval, float kmax2, TileStat *dst) {
+    __shared__ float r_min[4], r_max[4], r_k[4];
+    __shared__ uint32_t r_n[4];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    smin = wave_min(smin);
+    smax = wave_max(smax);
+    kmax2 = wave_max(kmax2);
+    nval = wave_sum_u32(nval);
+    if (lane == 0) {
+        r_min[wave] = smin;
+        r_max[wave] = smax;
+        r_k[wave] = kmax2;
+        r_n[wave] = nval;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        TileStat t;
+        t.smin = fminf(fminf(r_min[0], r_min[1]), fminf(r_min[2], r_min[3]));
+        t.smax = fmaxf(fmaxf(r_max[0], r_max[1]), fmaxf(r_max[2], r_max[3]));
+        t.kmax2 = fmaxf(fmaxf(r_k[0], r_k[1]), fmaxf(r_k[2], r_k[3]));
+        t.nvalid = r_n[0] + r_n[1] + r_n[2] + r_n[3];
+        *dst = t;
+    }
+}
+
+// --------------------------------------------------------------- MFMA path
+// Block = 4 waves = 256 slots (one statistics tile); each wave scores 4
+// groups of 16 slots.  MFMA operand layouts (16x16x32, wave64): lane l holds
+// A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16]; the result tile has
+// D[4*(l/16) + r][l%16] in element r.  Both operands use the same lane ->
+// k mapping, so every product pairs q[h][d] with k[j][d] for the same d.
+template <int HI, int DI>
+__global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restrict__ qI, const float *__restrict__ w,
+                                                       const uint16_t *__restrict__ kI, int Q, int64_t N,
+                                                       const int64_t *__restrict__ q_pos, int m,
+                                                       const int32_t *__restrict__ cand, int P,
+                                                       float *__restrict__ scores, TileStat *__restrict__ stats,
+                                                       int ntiles) {
+    constexpr int HT = HI / 16;  // head tiles
+    constexpr int KS = DI / 32;  // contraction steps
+    constexpr int G = 4;         // 16-slot groups per wave
+    const int bq = blockIdx.y;
+    const int b = bq / Q;
+    const int tile = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, kg = lane >> 4;
+    const int64_t n = cand ? (int64_t)P : N;
+    const int64_t nvis = visible_entries(q_pos, bq, m, N);
+
+    // Row indices of this wave's 4 x 16 slots.
+    const int64_t slot0 = (int64_t)tile * TILE + wave * 64;
+    int64_t jrow[G];
+    bool valid[G];
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        int64_t slot = slot0 + g * 16 + col;
+        int64_t j = -1;
+        if (slot < n) j = cand ? (int64_t)cand[(int64_t)bq * P + slot] : slot;
+        valid[g] = (j >= 0) && (j < nvis);
+        jrow[g] = valid[g] ? j : 0;
+    }
+    // Issue every key load of the wave first (64 B per lane per group).
+    u32x4 kb[G][KS];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const uint16_t *krow = kI + ((size_t)b * N + jrow[g]) * DI + 8 * kg;
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+            kb[g][s] = valid[g] ? *reinterpret_cast<const u32x4 *>(krow + 32 * s) : zero;
+    }
+    // Query heads (A operand) and the weights of the result rows this lane holds.
+    u32x4 qa[HT][KS];
+    const uint16_t *qrow = qI + (size_t)bq * HI * DI;
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+            qa[ht][s] = *reinterpret_cast<const u32x4 *>(qrow + (ht * 16 + col) * DI + 32 * s + 8 * kg);
+    float wv[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) wv[ht][r] = w[(size_t)bq * HI + ht * 16 + 4 * kg + r];
+
+    float smin = POS_INF, smax = NEG_INF, kmax2 = 0.f;
+    uint32_t nval = 0;
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        f32x4 acc[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++)
+                acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ht][s]),
+                                                                  __builtin_bit_cast(bf16x8, kb[g][s]), acc[ht], 0, 0,
+                                                                  0);
+        float part = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        // squared norm of key row (l%16), from the B fragments already in registers
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                bf16x2 v = __builtin_bit_cast(bf16x2, kb[g][s][e]);
+                ss = __builtin_amdgcn_fdot2_f32_bf16(v, v, ss, false);
+            }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const int64_t slot = slot0 + g * 16 + col;
+        if (kg == 0 && slot < n) scores[(int64_t)bq * n + slot] = valid[g] ? part : NEG_INF;
+        if (valid[g]) {
+            smin = fminf(smin, part);
+            smax = fmaxf(smax, part);
+            kmax2 = fmaxf(kmax2, ss);
+            nval += (kg == 0);
+        }
+    }
+    reduce_tile_stat(smin, smax, nval, kmax2, stats + (size_t)bq * ntiles + tile);
+}
+
+// ---------------------------------------------------------------- VALU path
+// Any head count / dim / dtype: one slot per thread, fp32 FMA in sequential
+// order, query heads staged in LDS as fp32.
+__global__ __launch_bounds__(256) void k_index_valu(const void *__restrict__ qI, int dt, const float *__restrict__ w,
+                                                    const void *__restrict__ kI, int Q, int HI, int dI, int64_t N,
+                                                    const int64_t *__restrict__ q_pos, int m,
+                                                    const int32_t *__restrict__ cand, int P,
+                                                    float *__restrict__ scores, TileStat *__restrict__ stats,
+                                                    int ntiles) {
+    extern __shared__ float qs[];  // [HI * dI]
+    const int bq = blockIdx.y;
+    const int b = bq / Q;
+    const int64_t n = cand ? (int64_t)P : N;
+    const int64_t nvis = visible_entries(q_pos, bq, m, N);
+    const int HD = HI * dI;
+    for (int i = threadIdx.x; i < HD; i += blockDim.x) {
+        size_t off = (size_t)bq * HD + i;
+        qs[i] = dt == CSA2_F32 ? static_cast<const float *>(qI)[off] : bf16_to_f32(static_cast<const uint16_t *>(qI)[off]);
+    }
+    __syncthreads();
+    const int64_t slot = (int64_t)blockIdx.x * TILE + threadIdx.x;
+    int64_t j = -1;
+    if (slot < n) j = cand ? (int64_t)cand[(int64_t)bq * P + slot] : slot;
+    const bool valid = (j >= 0) && (j < nvis);
+    float s = 0.f, ss = 0.f;
+    if (valid) {
+        const size_t base = ((size_t)b * N + j) * dI;
+        for (int h = 0; h < HI; h++) {
+            float dot = 0.f;
+            for (int d = 0; d < dI; d++) {
+                float kv = dt == CSA2_F32 ? static_cast<const float *>(kI)[base + d]
+                                          : bf16_to_f32(static_cast<const uint16_t *>(kI)[base + d]);
+                dot = fmaf(qs[h * dI + d], kv, dot);
+                if (h == 0) ss = fmaf(kv, kv, ss);
+            }
+            s = fmaf(w[(size_t)bq * HI + h], fmaxf(dot, 0.f), s);
+        }
+    }
+    if (slot < n) scores[(int64_t)bq * n + slot] = valid ? s : NEG_INF;
+    reduce_tile_stat(valid ? s : POS_INF, valid ? s : NEG_INF, valid ? 1u : 0u, valid ? ss : 0.f,
+                     stats + (size_t)bq * ntiles + blockIdx.x);
+}
+
+// ------------------------------------------------------------- error bound
+// E = 2^-22 (dI + HI + 2) * max_j ||k_j|| * sum_h |w_h| ||q_h||  (+ tiny).
+// Derivation: each fp32 product of bf16/fp32 inputs is exact; each fp32
+// accumulation in the dot product (<= dI steps, any order, rounding or
+// truncating) and in the weighted head sum (<= HI + 2 steps) is charged a
+// relative error of 2^-23; the total is bounded through Cauchy-Schwarz by
+// (dI + HI + 1) 2^-23 sum_h |w_h| ||q_h|| ||k_j||, and the binary64 reference
+// differs from the exact value by far less.  2^-22 doubles the whole budget.
+// max ||k||^2 comes from fp32 sums (relative error < dI 2^-23) and is widened
+// by 2^-10 before the square root.
+__global__ __launch_bounds__(256) void k_err_bound(const void *__restrict__ qI, int dt, const float *__restrict__ w,
+                                                   int HI, int dI, const TileStat *__restrict__ stats, int ntiles,
+                                                   float *__restrict__ err32, double *__restrict__ err64) {
+    __shared__ double red[256];
+    __shared__ float kred[256];
+    const int bq = blockIdx.x;
+    float km = 0.f;
+    for (int t = threadIdx.x; t < ntiles; t += 256) km = fmaxf(km, stats[(size_t)bq * ntiles + t].kmax2);
+    double acc = 0.0;
+    for (int h = threadIdx.x; h < HI; h += 256) {
+        double q2 = 0.0;
+        for (int d = 0; d < dI; d++) {
+            size_t off = ((size_t)bq * HI + h) * dI + d;
+            double v = dt == CSA2_F32 ? (double)static_cast<const float *>(qI)[off]
+                                      : (double)bf16_to_f32(static_cast<const uint16_t *>(qI)[off]);
+            q2 += v * v;
+        }
+        acc += fabs((double)w[(size_t)bq * HI + h]) * sqrt(q2);
+    }
+    red[threadIdx.x] = acc;
+    kred[threadIdx.x] = km;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) {
+            red[threadIdx.x] += red[threadIdx.x + o];
+            kred[threadIdx.x] = fmaxf(kred[threadIdx.x], kred[threadIdx.x + o]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        double kmax = sqrt((double)kred[0] * (1.0 + ldexp(1.0, -10)));
+        double E = score_bound(kmax, red[0] * (1.0 + ldexp(1.0, -30)), HI, dI);
+        if (err64) err64[bq] = E;
+        if (err32) {
+            float e = (float)E;
+            if ((double)e < E) e = nextafterf(e, POS_INF);
+            err32[bq] = e;
+        }
+    }
+}
+
+template <int HI, int DI>
+void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, int64_t N, const int64_t *q_pos,
+                 int m, const int32_t *cand, int P, float *scores, TileStat *stats, int ntiles, hipStream_t s) {
+    dim3 grid(ntiles, B * Q);
+    hipLaunchKernelGGL((k_index_mfma<HI, DI>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
+                       static_cast<const uint16_t *>(kI), Q, N, q_pos, m, cand, P, scores, stats, ntiles);
+}
+
+}  // namespace
+
+bool index_mfma_supported(int dt, int HI, int dI) {
+    if (dt != CSA2_BF16) return false;
+    switch (HI * 1000 + dI) {
+        case 16032: case 16064: case 16128: case 16256:
+        case 32032: case 32064: case 32128: case 32256:
+        case 64032: case 64064: case 64128:
+        case 128064:
+            return true;
+        default:
+            return false;
+    }
+}
+
+bool index_valu_supported(int HI, int dI) { return (int64_t)HI * dI <= 16384; }
+
+void launch_index_score(const void *qI, int dt, const float *w, const void *kI, int B, int Q, int HI, int dI,
+                        int64_t N, const int64_t *q_pos, int m, const int32_t *cand, int P, float *scores,
+                        TileStat *stats, hipStream_t s) {
+    const int64_t n = cand ? (int64_t)P : N;
+    const int ntiles = (int)((n + TILE - 1) / TILE);
+    if (index_mfma_supported(dt, HI, dI)) {
+#define CSA2_IDX_CASE(h, d)                                                                        \
+    case h * 1000 + d:                                                                              \
+        launch_mfma<h, d>(qI, w, kI, B, Q, N, q_pos, m, cand, P, scores, stats, ntiles, s);      \
+        break;
+        switch (HI * 1000 + dI) {
+            CSA2_IDX_CASE(16, 32) CSA2_IDX_CASE(16, 64) CSA2_IDX_CASE(16, 128) CSA2_IDX_CASE(16, 256)
+            CSA2_IDX_CASE(32, 32) CSA2_IDX_CASE(32, 64) CSA2_IDX_CASE(32, 128) CSA2_IDX_CASE(32, 256)
+            CSA2_IDX_CASE(64, 32) CSA2_IDX_CASE(64, 64) CSA2_IDX_CASE(64, 128)
+            CSA2_IDX_CASE(128, 64)
+        }
+#undef CSA2_IDX_CASE
+    } else {
+        dim3 grid(ntiles, B * Q);
+        size_t lds = sizeof(float) * (size_t)HI * dI;
+        hipLaunchKernelGGL(k_index_valu, grid, dim3(256), lds, s, qI, dt, w, kI, Q, HI, dI, N, q_pos, m, cand, P,
+                           scores, stats, ntiles);
+    }
+    check_launch("index score");
+}
+
+void launch_err_bound(const void *qI, int dt, const float *w, int BQ, int HI, int dI, const TileStat *stats,
+                      int ntiles, float *err32, double *err64, hipStream_t s) {
+    hipLaunchKernelGGL(k_err_bound, dim3(BQ), dim3(256), 0, s, qI, dt, w, HI, dI, stats, ntiles, err32, err64);
+    check_launch("error bound");
+}
+
+}  // namespace csa2

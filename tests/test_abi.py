@@ -1,0 +1,98 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+entry point include/csa2.h declares, sizes workspaces, and rejects bad
+arguments before anything is launched (fake but aligned pointers are passed:
+validation fails first, so they are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+b = pytest.importorskip("sparse_long_context_csa2_amd.binding",
+                        reason="libcsa2.so not built (python -m sparse_long_context_csa2_amd.build)")
+
+A = ctypes.c_void_p(0x10000)  # aligned, never dereferenced
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)  # misaligned
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"CSA2_API\s+[^;(]*?\b(csa2_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert len(names) == 12, names
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(b.EXPORTS) == names
+    assert "gfx950" in b.version()
+
+
+def test_workspace_sizes_grow_with_problem():
+    assert b._topk_ws(1, 1, 1000, 10) < b._topk_ws(1, 1, 100000, 10) < b._topk_ws(4, 1, 100000, 10)
+    assert b._index_ws(b.BF16, 16, 1, 64, 128, 32768, 0) > 0
+    assert b._attn_ws(b.BF16, b.BF16, 16, 1, 64, 512, 2048) > 0       # split over 4 blocks of 512
+    assert b._attn_ws(b.BF16, b.BF16, 16, 1, 64, 512, 512) == 0       # one split: no partials
+    assert b._compress_ws(b.BF16, 1024, 512, 4, 1) >= 4100 * 512 * 4
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+def test_topk_rejects_bad_arguments_without_launching():
+    ws = ctypes.c_size_t(1 << 40)
+    assert _rc(b._topk, A, 1, 1, 100, None, 0, A2, None, A, ws, None) == 1          # k = 0
+    assert _rc(b._topk, None, 1, 1, 100, None, 5, A2, None, A, ws, None) == 1       # scores NULL
+    assert _rc(b._topk, MIS, 1, 1, 100, None, 5, A2, None, A, ws, None) == 1        # misaligned
+    assert _rc(b._topk, A, 1, 1, 100, None, 5, A2, None, A, 16, None) == 3          # workspace too small
+    assert "workspace" in b._last_error().decode()
+
+
+def test_index_score_rejects_and_reports_unsupported():
+    ws = 1 << 30
+    # dtype not f32/bf16
+    assert b._index(A, A, A, 2, 1, 1, 4, 64, 100, None, 1, None, 0, A2, None, A, ws, None) == 1
+    # HI * dI beyond every kernel
+    assert b._index(A, A, A, 0, 1, 1, 512, 512, 100, None, 1, None, 0, A2, None, A, ws, None) == 2
+    # cand with P = 0
+    assert b._index(A, A, A, 1, 1, 1, 64, 128, 100, None, 1, A, 0, A2, None, A, ws, None) == 1
+    # q_pos with m = 0
+    assert b._index(A, A, A, 1, 1, 1, 64, 128, 100, A, 0, None, 0, A2, None, A, ws, None) == 1
+
+
+def test_attention_and_compress_validation():
+    ws = 1 << 30
+    # FP4 kv with fp32 queries
+    assert b._attn(A, A, 0, 2, 1, 1, 16, 512, 10, A, 4, 1.0, A2, None, A, ws, None) == 1
+    # FP4 kv with D % 16 != 0
+    assert b._attn(A, A, 1, 2, 1, 1, 16, 40, 10, A, 4, 1.0, A2, None, A, ws, None) == 1
+    # vector path beyond its LDS limit (fp32 q, k huge)
+    assert b._attn(A, A, 0, 0, 1, 1, 8, 128, 10, A, 20000, 1.0, A2, None, A, ws, None) == 2
+    # compress: m > 16, D % 16
+    assert b._compress(A, 1, 4, 512, 17, 0, A, A, A2, A, ws, None) == 1
+    assert b._compress(A, 1, 4, 40, 4, 0, A, A, A2, A, ws, None) == 1
+
+
+def test_layer_mode_pointer_mismatch():
+    a = b.LayerArgs()
+    a.mode, a.B, a.Q, a.N, a.m, a.HI, a.dI, a.idx_dt = b.REINDEX, 1, 1, 1000, 4, 64, 128, b.BF16
+    a.k, a.P, a.H, a.D, a.q_dt, a.kv_dt, a.scale = 64, 0, 64, 512, b.BF16, b.BF16, 0.04
+    a.qI, a.w, a.kI, a.idx, a.q, a.kv, a.out = A, A, A, A, A, A, A2
+    assert b._layer(ctypes.byref(a), A, 1 << 40, None) == 1      # REINDEX without pool slots
+    a.P = 128
+    assert b._layer(ctypes.byref(a), A, 1 << 40, None) == 1      # ... and without the pool pointer
+    a.mode, a.P = 99, 0
+    assert b._layer(ctypes.byref(a), A, 1 << 40, None) == 1      # unknown mode
+    a.mode, a.idx = b.REUSE, None
+    assert b._layer(ctypes.byref(a), A, 1 << 40, None) == 1      # REUSE without indices
+    a.mode, a.idx = b.FULL, A
+    need = b._layer_ws(ctypes.byref(a))
+    assert need > 0
+    assert b._layer(ctypes.byref(a), A, need - 256, None) == 3   # workspace one block short

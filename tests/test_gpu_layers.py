@@ -1,0 +1,99 @@
+"""Layer-mode parity (FULL / REINDEX / REUSE) of csa2_layer against the oracle:
+index sets and pools bit-exact, outputs within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import ATOL_BF16, ATOL_F32, RTOL_BF16, RTOL_F32, assert_close, dev, host
+from sparse_long_context_csa2_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_long_context_csa2_amd import binding
+    return binding
+
+
+def run_group(b, d, q_pos=None):
+    """Run the spec's layer list on the GPU and in the oracle; compare each layer."""
+    spec = d["spec"]
+    kv, kI = dev(d["kv"]), dev(d["kI"])
+    g_pool = g_idx = None
+    r_pool = r_idx = None
+    atol, rtol = (ATOL_F32, RTOL_F32) if spec.kv_fmt == "f32" else (ATOL_BF16, RTOL_BF16)
+    for li, lay in enumerate(d["layers"]):
+        mode = lay["mode"]
+        kw = dict(q=dev(lay["q"]), kv=kv, k=spec.k, scale=spec.scale)
+        rkw = dict(q=lay["q"], kv=d["kv"], k=spec.k, scale=spec.scale)
+        if mode in ("FULL", "REINDEX"):
+            kw.update(qI=dev(lay["qI"]), w=dev(lay["w"]), kI=kI, q_pos=dev(q_pos), m=spec.m)
+            rkw.update(qI=lay["qI"], w=lay["w"], kI=d["kI"], q_pos=q_pos, m=spec.m)
+        if mode == "FULL":
+            kw["P"] = rkw["P"] = spec.P
+        elif mode == "REINDEX":
+            kw["pool"], rkw["pool"] = g_pool, r_pool
+        else:
+            kw["idx"], rkw["idx"] = g_idx, r_idx
+        g = b.layer(mode, **kw)
+        torch.cuda.synchronize()
+        r = oracle.layer(mode, **rkw)
+        if mode != "REUSE":
+            assert np.array_equal(host(g["idx"]).numpy(), r["idx"]), f"layer {li} ({mode}): idx differs"
+            assert np.array_equal(host(g["count"]).numpy(), r["count"]), f"layer {li}: count differs"
+            g_idx, r_idx = g["idx"], r["idx"]
+        if mode == "FULL" and spec.P > 0:
+            assert np.array_equal(host(g["pool"]).numpy(), r["pool"]), f"layer {li}: pool differs"
+            g_pool, r_pool = g["pool"], r["pool"]
+        assert_close(g["out"], r["out"], atol, rtol, f"layer {li} ({mode}) output")
+        assert_close(g["lse"], r["lse"], atol, rtol, f"layer {li} ({mode}) lse")
+
+
+def test_tiny_full_layer(b):
+    run_group(b, synth.make_decode(synth.tiny_full(seed=0)))
+
+
+def test_decode_bf16_reduced(b):
+    run_group(b, synth.make_decode(synth.decode_128k(seed=1, B=2, N=5000)))
+
+
+def test_decode_fp4_full_plus_five_reuse_reduced(b):
+    run_group(b, synth.make_decode(synth.decode_128k_fp4_group(seed=2, B=2, N=4100)))
+
+
+def test_hierarchical_full_pool_plus_reindex_reduced(b):
+    spec = synth.Decode(B=2, Q=1, N=20000, HI=64, dI=128, H=64, D=512, k=512, kv_fmt="fp4", P=2048, seed=3,
+                        layers=["FULL", "REINDEX", "REINDEX", "REUSE"])
+    run_group(b, synth.make_decode(spec))
+
+
+def test_causal_queries_reduced(b):
+    spec = synth.Decode(B=1, Q=6, N=3000, HI=64, dI=128, H=16, D=128, k=256, P=1024, seed=5,
+                        layers=["FULL", "REINDEX", "REUSE"])
+    pos = torch.tensor([[0, 3, 4, 1500, 11000, 11999]], dtype=torch.int64)
+    run_group(b, synth.make_decode(spec), q_pos=pos)
+
+
+def test_small_shapes_and_edge_k(b):
+    # k above the number of entries; H = 16 heads; tiny N; vector attention for an odd D
+    for spec in [synth.Decode(B=1, Q=1, N=40, HI=16, dI=64, H=16, D=64, k=64, seed=6),
+                 synth.Decode(B=3, Q=1, N=1, HI=16, dI=32, H=16, D=128, k=4, seed=7),
+                 synth.Decode(B=1, Q=2, N=300, HI=4, dI=64, H=8, D=128, k=50, idx_dtype="f32", kv_fmt="f32",
+                              P=100, seed=8, layers=["FULL", "REINDEX", "REUSE"])]:
+        run_group(b, synth.make_decode(spec))
+
+
+def test_rerun_is_bitwise_deterministic(b):
+    d = synth.make_decode(synth.decode_128k(seed=9, B=2, N=3000))
+    lay = d["layers"][0]
+    kw = dict(q=dev(lay["q"]), kv=dev(d["kv"]), k=256, scale=d["spec"].scale, qI=dev(lay["qI"]), w=dev(lay["w"]),
+              kI=dev(d["kI"]))
+    g1 = b.layer("FULL", **kw)
+    g2 = b.layer("FULL", **kw)
+    torch.cuda.synchronize()
+    for key in ("idx", "out", "lse"):
+        assert torch.equal(g1[key], g2[key]), key
