@@ -11,8 +11,9 @@
 // Matrix-core kernel: a block serves 16 heads of one query over a fixed split
 // of 512 selected entries (the split depends only on k, so a query's result
 // does not depend on the batch).  Each wave takes 32-entry sub-tiles: the
-// gathered rows are staged in LDS as bf16 (FP4 rows decoded on the way in),
-// S^T = C Q^T runs on v_mfma_f32_16x16x32_bf16 with the rows as the A
+// gathered rows are staged in LDS as bf16 (FP4 rows decoded on the way in,
+// to fp16, where they are also exact), S^T = C Q^T runs on the 16x16x32
+// matrix-core instruction of that type with the rows as the A
 // operand, the online softmax keeps one running max per head, and
 // O^T = C^T P^T reuses the same LDS rows (read transposed) with P^T taken
 // straight from the S^T result registers.  Waves merge through LDS; splits are
@@ -54,6 +55,38 @@ __device__ __forceinline__ u32x4 fp4_dequant8(uint32_t word, float sc) {
         r[p] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xffff0000u);
     }
     return r;
+}
+
+// Same, packed as fp16 pairs: the products (<= 5 significant bits, magnitude
+// in [2^-10, 2688]) are exact fp16 normals, so the conversion is exact.
+__device__ __forceinline__ u32x4 fp4_dequant8_f16(uint32_t word, float sc) {
+    u32x4 r;
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const uint32_t byte = (word >> (8 * p)) & 0xffu;
+        const float v0 = __uint_as_float(e2m1_bits(byte & 15u)) * sc;
+        const float v1 = __uint_as_float(e2m1_bits(byte >> 4)) * sc;
+        r[p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v0, v1));
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    return uint32_t(__builtin_bit_cast(uint16_t, ha)) | (uint32_t(__builtin_bit_cast(uint16_t, hb)) << 16);
+}
+
+// One 16x16x32 matrix-core step in the operand type of the staged rows:
+// bf16 for bf16 KV, fp16 for FP4 KV (decoded FP4 values are exact in both;
+// fp16 keeps three more bits of the softmax weights).
+template <int FMT>
+__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (FMT == CSA2_FP4)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float kv_elem(const uint8_t *row, int fmt, int D, int d) {
@@ -105,6 +138,27 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
     const uint16_t *qrow = q + ((size_t)bq * H + hg * 16 + col) * D + 8 * kg;
 #pragma unroll
     for (int s = 0; s < KS; s++) qf[s] = *reinterpret_cast<const u32x4 *>(qrow + 32 * s);
+    float qscale = scale;
+    if constexpr (FMT == CSA2_FP4) {
+        // bf16 queries -> fp16 operands, pre-scaled by a power of two when their
+        // magnitude would overflow fp16 (the scale moves into the logits).
+        float amax = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(qf[s][e] & 0xffffu)), fabsf(bf16_to_f32(qf[s][e] >> 16))));
+        amax = wave_max(amax);
+        int ex = 0;
+        if (amax > 32768.f) ex = (int)ceilf(log2f(amax / 32768.f));
+        const float down = ldexpf(1.f, -ex);
+        qscale = ldexpf(scale, ex);
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                qf[s][e] = pack_f16_rne(bf16_to_f32(qf[s][e] & 0xffffu) * down, bf16_to_f32(qf[s][e] >> 16) * down);
+    }
 
     f32x4 o[DT];
 #pragma unroll
@@ -118,7 +172,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
 
     for (int e0 = e_begin + wave * ATT_SUB; e0 < e_end; e0 += 4 * ATT_SUB) {
         const int my_e = e0 + (lane & 31);
-        const int jr = my_e < e_end ? irow[my_e] : -1;
+        int jr = my_e < e_end ? irow[my_e] : -1;
+        if (jr >= N) jr = -1;  // out-of-range entries are skipped like -1
         // ---- gather the 32 rows into LDS as bf16
         if constexpr (FMT == CSA2_BF16) {
             constexpr int CPR = D / 8;  // 16-byte chunks per row
@@ -145,10 +200,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
                 }
                 const float s0 = e4m3_val(sc2 & 0xffu), s1 = e4m3_val(sc2 >> 8);
                 uint16_t *dst = T + r * LS + cc * 32;
-                *reinterpret_cast<u32x4 *>(dst) = fp4_dequant8(codes[0], s0);
-                *reinterpret_cast<u32x4 *>(dst + 8) = fp4_dequant8(codes[1], s0);
-                *reinterpret_cast<u32x4 *>(dst + 16) = fp4_dequant8(codes[2], s1);
-                *reinterpret_cast<u32x4 *>(dst + 24) = fp4_dequant8(codes[3], s1);
+                *reinterpret_cast<u32x4 *>(dst) = fp4_dequant8_f16(codes[0], s0);
+                *reinterpret_cast<u32x4 *>(dst + 8) = fp4_dequant8_f16(codes[1], s0);
+                *reinterpret_cast<u32x4 *>(dst + 16) = fp4_dequant8_f16(codes[2], s1);
+                *reinterpret_cast<u32x4 *>(dst + 24) = fp4_dequant8_f16(codes[3], s1);
             }
         }
         wave_lds_sync();
@@ -161,8 +216,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
 #pragma unroll
             for (int s = 0; s < KS; s++) {
                 const u32x4 a = *reinterpret_cast<const u32x4 *>(arow + 32 * s);
-                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                __builtin_bit_cast(bf16x8, qf[s]), st[t], 0, 0, 0);
+                st[t] = mma<FMT>(a, qf[s], st[t]);
             }
         }
         // ---- online softmax for head col; this lane holds entries 16t + 4kg + i
@@ -173,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int j = __shfl(jr, t * 16 + 4 * kg + i);
-                const float v = j >= 0 ? st[t][i] * scale : NEG_INF;
+                const float v = j >= 0 ? st[t][i] * qscale : NEG_INF;
                 a[t * 4 + i] = v;
                 mt = fmaxf(mt, v);
             }
@@ -188,7 +242,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
             const float p0 = a[x] == NEG_INF ? 0.f : __expf(a[x] - m_new);
             const float p1 = a[x + 1] == NEG_INF ? 0.f : __expf(a[x + 1] - m_new);
             psum += p0 + p1;
-            pk[x / 2] = uint32_t(f32_to_bf16_rne(p0)) | (uint32_t(f32_to_bf16_rne(p1)) << 16);
+            if constexpr (FMT == CSA2_FP4) pk[x / 2] = pack_f16_rne(p0, p1);
+            else pk[x / 2] = uint32_t(f32_to_bf16_rne(p0)) | (uint32_t(f32_to_bf16_rne(p1)) << 16);
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
@@ -206,8 +261,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
             }
             const u32x4 av = {w4[0], w4[1], w4[2], w4[3]};
             o[t] = o[t] * alpha;
-            o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                           __builtin_bit_cast(bf16x8, pb), o[t], 0, 0, 0);
+            o[t] = mma<FMT>(av, pb, o[t]);
         }
         wave_lds_sync();
     }
@@ -313,7 +367,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
     for (int t = threadIdx.x; t < k; t += 256) {
         const int32_t j = irow[t];
         float a = NEG_INF;
-        if (j >= 0) {
+        if (j >= 0 && j < N) {
             const uint8_t *row = kvb + (size_t)j * rb;
             float dot = 0.f;
             for (int d = 0; d < D; d++) dot = fmaf(qs[d], kv_elem(row, kv_dt, D, d), dot);
@@ -347,7 +401,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
         float acc = 0.f;
         for (int t = 0; t < k; t++) {
             const int32_t j = irow[t];
-            if (j >= 0 && as[t] != 0.f) acc = fmaf(as[t], kv_elem(kvb + (size_t)j * rb, kv_dt, D, d), acc);
+            if (j >= 0 && j < N && as[t] != 0.f) acc = fmaf(as[t], kv_elem(kvb + (size_t)j * rb, kv_dt, D, d), acc);
         }
         const float v = Z > 0.f ? acc / Z : 0.f;
         if (q_dt == CSA2_F32) static_cast<float *>(out)[qoff + d] = v;

@@ -31,6 +31,7 @@ struct RescoreArgs {
     int Q, HI, dI;
     int64_t N;
 };
+size_t rescore_lds_bytes(int HI, int dI);  // must stay <= 64 KiB
 SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified);
 size_t sel_workspace(const SelPlan &p, bool own_stats);
 void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats, const double *ebound,

@@ -331,7 +331,8 @@ __global__ __launch_bounds__(256) void k_sel_rescore(const void *__restrict__ qI
     const int qstride = dI + 1;  // padded row: lane h reads bank (h + d) % 64
     float *qs = lds;
     float *ks = lds + HI * qstride + wave * dI;
-    double *ts = reinterpret_cast<double *>(lds + HI * qstride + 4 * dI) + wave * 64;
+    const int toff = (HI * qstride + 4 * dI + 1) & ~1;  // 8-byte aligned start of the per-wave fp64 buffers
+    double *ts = reinterpret_cast<double *>(lds + toff) + wave * 64;
     for (int i = threadIdx.x; i < HI * dI; i += 256) {
         int h = i / dI, d = i % dI;
         size_t off = (size_t)bq * HI * dI + i;
@@ -486,6 +487,11 @@ __global__ __launch_bounds__(1024) void k_sel_finish(const float *__restrict__ s
 
 // ------------------------------------------------------------------ host
 
+size_t rescore_lds_bytes(int HI, int dI) {
+    const size_t floats = ((size_t)HI * (dI + 1) + 4 * (size_t)dI + 1) & ~size_t(1);
+    return sizeof(float) * floats + sizeof(double) * 4 * 64;
+}
+
 SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified) {
     SelPlan p;
     p.BQ = BQ;
@@ -542,7 +548,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     if (p.certified) {
         int per_q = 4096 / p.BQ;
         per_q = per_q < 1 ? 1 : (per_q > 64 ? 64 : per_q);
-        size_t lds = sizeof(float) * ((size_t)rs->HI * (rs->dI + 1) + 4 * (size_t)rs->dI) + sizeof(double) * 4 * 64;
+        const size_t lds = rescore_lds_bytes(rs->HI, rs->dI);
         hipLaunchKernelGGL(k_sel_rescore, dim3(per_q, p.BQ, p.ntgt), dim3(256), lds, s, rs->qI, rs->dt, rs->w, rs->kI,
                            rs->Q, rs->HI, rs->dI, rs->N, cand, p.n, sq, band, p.band_cap, band_score);
         check_launch("selection rescore");
