@@ -68,7 +68,7 @@ struct LayerSizes {
     int64_t n;  // scored slots per query
     csa2::SelPlan sel;
     csa2::AttnPlan att;
-    size_t scores, stats, err, selws, attws, total;
+    size_t scores, stats, selws, attws, total;
 };
 
 LayerSizes layer_sizes(const csa2_layer_args *a) {
@@ -86,10 +86,8 @@ LayerSizes layer_sizes(const csa2_layer_args *a) {
     z.scores = a->scores ? 0 : (c.take<float>((size_t)BQ * z.n), (size_t)BQ * z.n * 4);
     size_t before = c.used;
     c.take<csa2::TileStat>((size_t)BQ * z.sel.ntiles);
+    c.take<double>((size_t)BQ);  // sum_h |w_h| ||q_h||
     z.stats = c.used - before;
-    before = c.used;
-    c.take<double>((size_t)BQ);
-    z.err = c.used - before;
     z.selws = csa2::sel_workspace(z.sel, false);
     z.total = c.used + z.selws + z.attws;
     return z;
@@ -191,7 +189,8 @@ int csa2_index_score(const void *qI, const float *w, const void *kI, int dt, int
         csa2::Carve c(ws, ws_bytes);
         const int ntiles = (int)((n + csa2::TILE - 1) / csa2::TILE);
         auto *stats = c.take<csa2::TileStat>((size_t)B * Q * ntiles);
-        csa2::launch_index_score(qI, dt, w, kI, B, Q, HI, dI, N, q_pos, m, cand, cand ? P : 0, scores, stats, s);
+        csa2::launch_index_score(qI, dt, w, kI, B, Q, HI, dI, N, q_pos, m, cand, cand ? P : 0, scores, stats, nullptr,
+                                 s);
         if (err) csa2::launch_err_bound(qI, dt, w, B * Q, HI, dI, stats, ntiles, err, nullptr, s);
     });
 }
@@ -212,7 +211,7 @@ int csa2_topk(const float *scores, int32_t B, int32_t Q, int64_t n, const int32_
         opt_ptr(count, "count");
         const csa2::SelPlan p = csa2::sel_plan(B * Q, n, k, 0, false);
         need_ws(ws, ws_bytes, csa2::sel_workspace(p, true));
-        csa2::sel_run(p, scores, cand, nullptr, nullptr, nullptr, idx, count, nullptr, ws, ws_bytes,
+        csa2::sel_run(p, scores, cand, nullptr, nullptr, idx, count, nullptr, ws, ws_bytes,
                       (hipStream_t)stream);
     });
 }
@@ -262,15 +261,14 @@ int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream
             const int BQ = a->B * a->Q;
             float *scores = a->scores ? a->scores : c.take<float>((size_t)BQ * z.n);
             auto *stats = c.take<csa2::TileStat>((size_t)BQ * z.sel.ntiles);
-            auto *err = c.take<double>((size_t)BQ);
+            auto *sumwq = c.take<double>((size_t)BQ);
             void *selws = c.base + c.used;
             c.used += z.selws;
             const int32_t *cand = a->mode == CSA2_REINDEX ? a->pool : nullptr;
             csa2::launch_index_score(a->qI, a->idx_dt, a->w, a->kI, a->B, a->Q, a->HI, a->dI, a->N, a->q_pos, a->m,
-                                     cand, cand ? a->P : 0, scores, stats, s);
-            csa2::launch_err_bound(a->qI, a->idx_dt, a->w, BQ, a->HI, a->dI, stats, z.sel.ntiles, nullptr, err, s);
-            const csa2::RescoreArgs rs{a->qI, a->idx_dt, a->w, a->kI, a->Q, a->HI, a->dI, a->N};
-            csa2::sel_run(z.sel, scores, cand, stats, err, &rs, a->idx, a->count,
+                                     cand, cand ? a->P : 0, scores, stats, sumwq, s);
+            const csa2::RescoreArgs rs{a->qI, a->idx_dt, a->w, a->kI, a->Q, a->HI, a->dI, a->N, sumwq};
+            csa2::sel_run(z.sel, scores, cand, stats, &rs, a->idx, a->count,
                           a->mode == CSA2_FULL && a->P > 0 ? a->pool : nullptr, selws, z.selws, s);
         }
         void *attws = c.base + c.used;

@@ -8,22 +8,20 @@
 // may be stored as FP4 E2M1 with one E4M3 scale per 16 channels; the decoded
 // value e2m1 * e4m3 has at most 5 significant bits and is exact in bf16.
 //
-// Matrix-core kernel: a block serves 16 heads of one query over a fixed split
-// of 512 selected entries (the split depends only on k, so a query's result
-// does not depend on the batch).  Each wave takes 32-entry sub-tiles: the
-// gathered rows are staged in LDS as bf16 (FP4 rows decoded on the way in,
-// to fp16, where they are also exact), S^T = C Q^T runs on the 16x16x32
-// matrix-core instruction of that type with the rows as the A
-// operand, the online softmax keeps one running max per head, and
-// O^T = C^T P^T reuses the same LDS rows (read transposed) with P^T taken
-// straight from the S^T result registers.  Waves merge through LDS; splits are
-// merged by a small combine kernel.  Blocks of one (query, split) are placed
-// on one XCD so the head groups share the gathered rows in L2.
+// Matrix-core kernel: a block serves all heads of one query over a fixed split
+// of 128 selected entries (the split depends only on k, so a query's result
+// does not depend on the batch), one wave per 16 heads.  The gathered rows are
+// staged once per block in LDS as bf16 (FP4 rows decoded on the way in, to
+// fp16, where they are also exact), S^T = C Q^T runs on the 16x16x32
+// matrix-core instruction of that type with the rows as the A operand, the
+// online softmax keeps one running max per head, and O^T = C^T P^T reuses the
+// same LDS rows (read transposed) with P^T taken straight from the S^T result
+// registers.  Splits are merged by a small combine kernel.
 #include "internal.h"
 
 namespace csa2 {
 
-constexpr int ATT_SPLIT = 512;  // selected entries per block (fixed)
+constexpr int ATT_SPLIT = 128;  // selected entries per block (fixed)
 constexpr int ATT_SUB = 32;     // entries per wave iteration
 
 namespace {
@@ -42,35 +40,6 @@ __device__ __forceinline__ float e4m3_val(uint32_t s) {
     const float mag = e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0.001953125f;
     return (s & 0x80u) ? -mag : mag;
 }
-// Eight channels (one 32-bit code word, channel 2i in the low nibble of byte
-// i) times one scale -> four packed bf16 pairs.  The products are exact in
-// bf16, so dropping the low 16 bits of the fp32 product loses nothing.
-__device__ __forceinline__ u32x4 fp4_dequant8(uint32_t word, float sc) {
-    u32x4 r;
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-        const uint32_t byte = (word >> (8 * p)) & 0xffu;
-        const float v0 = __uint_as_float(e2m1_bits(byte & 15u)) * sc;
-        const float v1 = __uint_as_float(e2m1_bits(byte >> 4)) * sc;
-        r[p] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xffff0000u);
-    }
-    return r;
-}
-
-// Same, packed as fp16 pairs: the products (<= 5 significant bits, magnitude
-// in [2^-10, 2688]) are exact fp16 normals, so the conversion is exact.
-__device__ __forceinline__ u32x4 fp4_dequant8_f16(uint32_t word, float sc) {
-    u32x4 r;
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-        const uint32_t byte = (word >> (8 * p)) & 0xffu;
-        const float v0 = __uint_as_float(e2m1_bits(byte & 15u)) * sc;
-        const float v1 = __uint_as_float(e2m1_bits(byte >> 4)) * sc;
-        r[p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v0, v1));
-    }
-    return r;
-}
-
 __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
     const _Float16 ha = (_Float16)a, hb = (_Float16)b;
     return uint32_t(__builtin_bit_cast(uint16_t, ha)) | (uint32_t(__builtin_bit_cast(uint16_t, hb)) << 16);
@@ -107,41 +76,146 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ------------------------------------------------------------ MFMA kernel
-template <int D, int FMT>
-__global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
-                                                      int Q, int H, int64_t N, const int32_t *__restrict__ idx, int k,
-                                                      float scale, int nsplit, uint16_t *__restrict__ out,
-                                                      float *__restrict__ lse, float *__restrict__ part_o,
-                                                      float2 *__restrict__ part_ml) {
-    constexpr int KS = D / 32;  // contraction steps of S
-    constexpr int DT = D / 16;  // 16-wide d tiles of O
-    constexpr int ROWB = FMT == CSA2_FP4 ? D / 2 + D / 16 : 2 * D;
-    constexpr int LS = D + 8;  // LDS row stride in bf16 (16 B pad)
-    __shared__ __attribute__((aligned(16))) uint16_t tile[4 * ATT_SUB * LS];
-    __shared__ float m_sh[4][16], l_sh[4][16], M_h[16], L_h[16];
+// Block = one query x one split of ATT_SPLIT selected entries; wave w serves
+// heads 16 (w % HGS) .. +15 and, with DS = 2, half of the output channels (the
+// two waves of a head group both compute that group's logits).  Per 32-entry tile: all threads gather the rows into an
+// LDS buffer (bf16 rows as is, FP4 rows decoded to fp16), the next tile's rows
+// are already in flight in registers; each wave computes S^T = C Q^T (rows as
+// the A operand), the online softmax of its 16 heads, and O^T += C^T P^T with
+// the C^T operand read by the LDS transpose load: lane r of each 16-lane group
+// points at 4 consecutive channels of one row, and lane i receives channel i
+// of 4 consecutive rows.
 
-    const int HG = H / 16;
-    const int id = blockIdx.x, nb = gridDim.x;
-    const int L = (nb % 8 == 0) ? (id % 8) * (nb / 8) + id / 8 : id;
-    const int hg = L % HG;
-    const int unit = L / HG;
-    const int split = unit % nsplit;
-    const int bq = unit / nsplit;
+typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef _Float16 __attribute__((ext_vector_type(2))) f16x2;
+
+// FP4 chunk (32 channels: 16 code bytes) with the two E4M3 scales of its
+// 16-channel halves -> 32 fp16 values.  The conversion instruction applies the
+// scale's power of two; the scale's mantissa (1 + m/8, at most 3 bits) is
+// applied by an fp16 multiply.  Every product has <= 5 significant bits and a
+// magnitude in [2^-10, 3072], so both steps are exact.
+__device__ __forceinline__ void fp4_chunk_to_f16(u32x4 codes, uint32_t sc2, uint32_t *dst16) {
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+        const float s = e4m3_val((sc2 >> (8 * half)) & 0xffu);
+        const uint32_t sb = __float_as_uint(s);
+        float pow2 = __uint_as_float(sb & 0x7f800000u);
+        uint32_t fbits = 0x3c00u | ((sb >> 13) & 0x3ffu) | ((sb >> 16) & 0x8000u);
+        if (s == 0.f) {
+            pow2 = 1.f;
+            fbits = 0u;
+        }
+        const f16x2 f = __builtin_bit_cast(f16x2, fbits | (fbits << 16));
+#pragma unroll
+        for (int wi = 0; wi < 2; wi++) {
+            const uint32_t word = codes[half * 2 + wi];
+            f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 0) * f;
+            f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 1) * f;
+            f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 2) * f;
+            f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 3) * f;
+            uint32_t *o = dst16 + (half * 2 + wi) * 4;
+            o[0] = __builtin_bit_cast(uint32_t, v0);
+            o[1] = __builtin_bit_cast(uint32_t, v1);
+            o[2] = __builtin_bit_cast(uint32_t, v2);
+            o[3] = __builtin_bit_cast(uint32_t, v3);
+        }
+    }
+}
+
+template <int D, int FMT>
+struct TileGather {
+    // bf16: a row is D/8 16-byte chunks; FP4: a row is D/32 chunks of 16 code
+    // bytes (32 channels) plus 2 scale bytes each.
+    static constexpr int CPR = FMT == CSA2_FP4 ? D / 32 : D / 8;
+    static constexpr int CHUNKS = ATT_SUB * CPR;
+    static constexpr int ROWB = FMT == CSA2_FP4 ? D / 2 + D / 16 : 2 * D;
+};
+
+template <int D, int FMT, int NT>
+__device__ __forceinline__ void gather_issue(const uint8_t *kvb, const int32_t *jt, u32x4 *buf, uint32_t *sbuf) {
+    using G = TileGather<D, FMT>;
+    constexpr int PER = (G::CHUNKS + NT - 1) / NT;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        const int c = threadIdx.x + u * NT;
+        buf[u] = zero;
+        sbuf[u] = 0;
+        if (c < G::CHUNKS) {
+            const int r = c / G::CPR, cc = c % G::CPR;
+            const int j = jt[r];
+            if (j >= 0) {
+                const uint8_t *row = kvb + (size_t)j * G::ROWB;
+                buf[u] = *reinterpret_cast<const u32x4 *>(row + cc * 16);
+                if constexpr (FMT == CSA2_FP4) sbuf[u] = *reinterpret_cast<const uint16_t *>(row + D / 2 + cc * 2);
+            }
+        }
+    }
+}
+
+template <int D, int FMT, int NT>
+__device__ __forceinline__ void gather_store(uint16_t *T, const u32x4 *buf, const uint32_t *sbuf) {
+    using G = TileGather<D, FMT>;
+    constexpr int PER = (G::CHUNKS + NT - 1) / NT;
+    constexpr int LS = D + 8;
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        const int c = threadIdx.x + u * NT;
+        if (c >= G::CHUNKS) continue;
+        const int r = c / G::CPR, cc = c % G::CPR;
+        if constexpr (FMT == CSA2_FP4) {
+            uint32_t o[16];
+            fp4_chunk_to_f16(buf[u], sbuf[u], o);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(T + r * LS + cc * 32);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++)
+                reinterpret_cast<u32x4 *>(dst)[q4] = u32x4{o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]};
+        } else {
+            *reinterpret_cast<u32x4 *>(T + r * LS + cc * 8) = buf[u];
+        }
+    }
+}
+
+template <int D, int FMT, int HGS, int DS>
+__global__ __launch_bounds__(64 * HGS * DS, 1) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
+                                                          int Q, int H, int64_t N, const int32_t *__restrict__ idx,
+                                                          int k, float scale, int nsplit, uint16_t *__restrict__ out,
+                                                          float *__restrict__ lse, float *__restrict__ part_o,
+                                                          float2 *__restrict__ part_ml) {
+    constexpr int NT = 64 * HGS * DS;
+    constexpr int KS = D / 32;       // contraction steps of S
+    constexpr int DT = D / 16 / DS;  // 16-wide d tiles of O owned by this wave
+    constexpr int LS = D + 8;   // LDS row stride in 16-bit elements (16-byte pad)
+    using G = TileGather<D, FMT>;
+    constexpr int PER = (G::CHUNKS + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][ATT_SUB * LS];
+    __shared__ int32_t jsh[ATT_SPLIT];
+
+    const int split = blockIdx.x % nsplit;
+    const int bq = blockIdx.x / nsplit;
     const int b = bq / Q;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 15, kg = lane >> 4;
-    uint16_t *T = tile + wave * ATT_SUB * LS;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int hg = wave % HGS;  // this wave's 16 heads
+    const int dt0 = (wave / HGS) * DT;  // first d tile of this wave (S is computed by every d part)
 
-    // Query heads hg*16 + col as the B operand of S^T = C Q^T.
+    const int e_begin = split * ATT_SPLIT;
+    const int e_end = min(k, e_begin + ATT_SPLIT);
+    const int ne = e_end - e_begin;
+    const int32_t *irow = idx + (size_t)bq * k + e_begin;
+    for (int e = threadIdx.x; e < ATT_SPLIT; e += NT) {
+        int j = e < ne ? irow[e] : -1;
+        jsh[e] = (j >= 0 && j < N) ? j : -1;  // out-of-range entries are skipped like -1
+    }
+    const uint8_t *kvb = kv + (size_t)b * N * G::ROWB;
+
+    // Query heads as the B operand of S^T = C Q^T (fp16 for FP4 rows).
     u32x4 qf[KS];
     const uint16_t *qrow = q + ((size_t)bq * H + hg * 16 + col) * D + 8 * kg;
 #pragma unroll
     for (int s = 0; s < KS; s++) qf[s] = *reinterpret_cast<const u32x4 *>(qrow + 32 * s);
     float qscale = scale;
     if constexpr (FMT == CSA2_FP4) {
-        // bf16 queries -> fp16 operands, pre-scaled by a power of two when their
-        // magnitude would overflow fp16 (the scale moves into the logits).
         float amax = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; s++)
@@ -165,70 +239,40 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
     for (int t = 0; t < DT; t++) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = NEG_INF, l_run = 0.f;
 
-    const int e_begin = split * ATT_SPLIT;
-    const int e_end = min(k, e_begin + ATT_SPLIT);
-    const int32_t *irow = idx + (size_t)bq * k;
-    const uint8_t *kvb = kv + (size_t)b * N * ROWB;
-
-    for (int e0 = e_begin + wave * ATT_SUB; e0 < e_end; e0 += 4 * ATT_SUB) {
-        const int my_e = e0 + (lane & 31);
-        int jr = my_e < e_end ? irow[my_e] : -1;
-        if (jr >= N) jr = -1;  // out-of-range entries are skipped like -1
-        // ---- gather the 32 rows into LDS as bf16
-        if constexpr (FMT == CSA2_BF16) {
-            constexpr int CPR = D / 8;  // 16-byte chunks per row
-
-            for (int c = lane; c < ATT_SUB * CPR; c += 64) {
-                const int r = c / CPR, cc = c % CPR;
-                const int j = __shfl(jr, r);
-                u32x4 v = zero;
-                if (j >= 0) v = *reinterpret_cast<const u32x4 *>(kvb + (size_t)j * ROWB + cc * 16);
-                *reinterpret_cast<u32x4 *>(T + r * LS + cc * 8) = v;
-            }
-        } else {
-            constexpr int CPR = D / 32;  // 16-byte code chunks (32 channels) per row
-
-            for (int c = lane; c < ATT_SUB * CPR; c += 64) {
-                const int r = c / CPR, cc = c % CPR;
-                const int j = __shfl(jr, r);
-                u32x4 codes = zero;
-                uint32_t sc2 = 0;
-                if (j >= 0) {
-                    const uint8_t *row = kvb + (size_t)j * ROWB;
-                    codes = *reinterpret_cast<const u32x4 *>(row + cc * 16);
-                    sc2 = *reinterpret_cast<const uint16_t *>(row + D / 2 + cc * 2);
-                }
-                const float s0 = e4m3_val(sc2 & 0xffu), s1 = e4m3_val(sc2 >> 8);
-                uint16_t *dst = T + r * LS + cc * 32;
-                *reinterpret_cast<u32x4 *>(dst) = fp4_dequant8_f16(codes[0], s0);
-                *reinterpret_cast<u32x4 *>(dst + 8) = fp4_dequant8_f16(codes[1], s0);
-                *reinterpret_cast<u32x4 *>(dst + 16) = fp4_dequant8_f16(codes[2], s1);
-                *reinterpret_cast<u32x4 *>(dst + 24) = fp4_dequant8_f16(codes[3], s1);
-            }
-        }
-        wave_lds_sync();
+    const int ntiles = (ne + ATT_SUB - 1) / ATT_SUB;
+    u32x4 buf[PER];
+    uint32_t sbuf[PER];
+    __syncthreads();  // jsh ready
+    if (ntiles > 0) {
+        gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf);
+        gather_store<D, FMT, NT>(tile[0], buf, sbuf);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; t++) {
+        const uint16_t *T = tile[t & 1];
+        if (t + 1 < ntiles) gather_issue<D, FMT, NT>(kvb, jsh + (t + 1) * ATT_SUB, buf, sbuf);
+        const int32_t *jt = jsh + t * ATT_SUB;
         // ---- S^T[e][h] for the two 16-entry halves
         f32x4 st[2];
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t *arow = T + (t * 16 + col) * LS + 8 * kg;
+        for (int h2 = 0; h2 < 2; h2++) {
+            st[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint16_t *arow = T + (h2 * 16 + col) * LS + 8 * kg;
 #pragma unroll
             for (int s = 0; s < KS; s++) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(arow + 32 * s);
-                st[t] = mma<FMT>(a, qf[s], st[t]);
+                const u32x4 av = *reinterpret_cast<const u32x4 *>(arow + 32 * s);
+                st[h2] = mma<FMT>(av, qf[s], st[h2]);
             }
         }
-        // ---- online softmax for head col; this lane holds entries 16t + 4kg + i
+        // ---- online softmax for head col; this lane holds entries 16 h2 + 4 kg + i
         float a[8];
         float mt = NEG_INF;
 #pragma unroll
-        for (int t = 0; t < 2; t++)
+        for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int j = __shfl(jr, t * 16 + 4 * kg + i);
-                const float v = j >= 0 ? st[t][i] * qscale : NEG_INF;
-                a[t * 4 + i] = v;
+                const float v = jt[h2 * 16 + 4 * kg + i] >= 0 ? st[h2][i] * qscale : NEG_INF;
+                a[h2 * 4 + i] = v;
                 mt = fmaxf(mt, v);
             }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -248,100 +292,105 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(const uint16_t *__restrict
         l_run = l_run * alpha + psum;
         m_run = m_new;
         const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
-        // ---- O^T[d][h] += C^T[d][e] P^T[e][h]; element x of the A operand is
-        // row 16(x/4) + 4kg + x%4 of the staged tile, matching pb element x.
-        const uint16_t *cb = T + (4 * kg) * LS + col;
+        // ---- O^T[d][h] += C^T[d][e] P^T[e][h]: A operand element x is row
+        // 16 (x/4) + 4 kg + x%4, channel 16 dt + col (two transpose loads).
+        const uint16_t *tr0 = T + (4 * kg + (col >> 2)) * LS + 4 * (col & 3);
+        const uint16_t *tr1 = tr0 + 16 * LS;
 #pragma unroll
-        for (int t = 0; t < DT; t++) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int x = 0; x < 8; x += 2) {
-                const int r0 = 16 * (x / 4) + (x % 4);
-                w4[x / 2] = uint32_t(cb[r0 * LS + 16 * t]) | (uint32_t(cb[(r0 + 1) * LS + 16 * t]) << 16);
-            }
-            const u32x4 av = {w4[0], w4[1], w4[2], w4[3]};
-            o[t] = o[t] * alpha;
-            o[t] = mma<FMT>(av, pb, o[t]);
+        for (int dt = 0; dt < DT; dt++) {
+            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)(tr0 + 16 * (dt0 + dt)));
+            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)(tr1 + 16 * (dt0 + dt)));
+            const u32x4 av = {__builtin_bit_cast(uint32_t, s16x2{lo4[0], lo4[1]}),
+                              __builtin_bit_cast(uint32_t, s16x2{lo4[2], lo4[3]}),
+                              __builtin_bit_cast(uint32_t, s16x2{hi4[0], hi4[1]}),
+                              __builtin_bit_cast(uint32_t, s16x2{hi4[2], hi4[3]})};
+            o[dt] = o[dt] * alpha;
+            o[dt] = mma<FMT>(av, pb, o[dt]);
         }
-        wave_lds_sync();
-    }
-
-    // ---- merge the four waves (same heads, disjoint entries)
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (kg == 0) {
-        m_sh[wave][col] = m_run;
-        l_sh[wave][col] = l_run;
-    }
-    __syncthreads();
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < 4; w++) M = fmaxf(M, m_sh[w][col]);
-    float Ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; w++) Ls += m_sh[w][col] == NEG_INF ? 0.f : l_sh[w][col] * __expf(m_sh[w][col] - M);
-    const float mine = m_run == NEG_INF ? 0.f : __expf(m_run - M);
-    if (wave == 0 && kg == 0) {
-        M_h[col] = M;
-        L_h[col] = Ls;
-    }
-    float *ob = reinterpret_cast<float *>(tile);  // [16 heads][D]
-    for (int w = 0; w < 4; w++) {
-        if (wave == w) {
-#pragma unroll
-            for (int t = 0; t < DT; t++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int i = col * D + 16 * t + 4 * kg + r;
-                    const float v = o[t][r] * mine;
-                    ob[i] = w == 0 ? v : ob[i] + v;
-                }
-        }
+        if (t + 1 < ntiles) gather_store<D, FMT, NT>(tile[(t + 1) & 1], buf, sbuf);
         __syncthreads();
     }
+
+    // ---- write this wave's 16 heads: lane holds O^T[16 dt + 4 kg + r][col]
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    const int h = hg * 16 + col;
     if (nsplit == 1) {
-        for (int i = threadIdx.x; i < 16 * D; i += 256) {
-            const int h = i / D, d = i % D;
-            const float Lh = L_h[h];
-            const float v = Lh > 0.f ? ob[i] / Lh : 0.f;
-            out[((size_t)bq * H + hg * 16 + h) * D + d] = f32_to_bf16_rne(v);
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        uint16_t *orow = out + ((size_t)bq * H + h) * D + 16 * dt0 + 4 * kg;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const uint32_t w0 = uint32_t(f32_to_bf16_rne(o[dt][0] * inv)) | (uint32_t(f32_to_bf16_rne(o[dt][1] * inv)) << 16);
+            const uint32_t w1 = uint32_t(f32_to_bf16_rne(o[dt][2] * inv)) | (uint32_t(f32_to_bf16_rne(o[dt][3] * inv)) << 16);
+            *reinterpret_cast<uint2 *>(orow + 16 * dt) = make_uint2(w0, w1);
         }
-        if (lse && threadIdx.x < 16) {
-            const float Lh = L_h[threadIdx.x];
-            lse[(size_t)bq * H + hg * 16 + threadIdx.x] = Lh > 0.f ? M_h[threadIdx.x] + logf(Lh) : NEG_INF;
-        }
+        if (lse && kg == 0 && dt0 == 0) lse[(size_t)bq * H + h] = l_run > 0.f ? m_run + logf(l_run) : NEG_INF;
     } else {
-        const size_t pbase = ((size_t)bq * nsplit + split) * H + hg * 16;
-        for (int i = threadIdx.x; i < 16 * D; i += 256) part_o[pbase * D + i] = ob[i];
-        if (threadIdx.x < 16) part_ml[pbase + threadIdx.x] = make_float2(M_h[threadIdx.x], L_h[threadIdx.x]);
+        const size_t pi = ((size_t)bq * nsplit + split) * H + h;
+        float *prow = part_o + pi * D + 16 * dt0 + 4 * kg;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4 *>(prow + 16 * dt) = o[dt];
+        if (kg == 0 && dt0 == 0) part_ml[pi] = make_float2(m_run, l_run);
     }
 }
 
 // ----------------------------------------------------------- split merge
+// One thread per 4 channels of one head: the split maxima and sums are read
+// first (all loads in flight), then the 4-channel partial rows of every split.
+constexpr int COMB_UNROLL = 16;
+
 __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ part_o,
-                                                      const float2 *__restrict__ part_ml, int H, int D, int nsplit,
-                                                      void *__restrict__ out, int out_dt, float *__restrict__ lse) {
-    const int bq = blockIdx.y, h = blockIdx.x;
+                                                      const float2 *__restrict__ part_ml, int BQ, int H, int D,
+                                                      int nsplit, void *__restrict__ out, int out_dt,
+                                                      float *__restrict__ lse) {
+    const int tpr = D / 4;  // threads per head row
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / tpr;  // (bq, h)
+    const int c4 = (int)(gid % tpr);
+    if (row >= (int64_t)BQ * H) return;
+    const int64_t bq = row / H, h = row % H;
     float M = NEG_INF;
-    for (int s = 0; s < nsplit; s++) M = fmaxf(M, part_ml[((size_t)bq * nsplit + s) * H + h].x);
+    for (int s0 = 0; s0 < nsplit; s0 += COMB_UNROLL) {
+        float2 ml[COMB_UNROLL];
+#pragma unroll
+        for (int u = 0; u < COMB_UNROLL; u++)
+            if (s0 + u < nsplit) ml[u] = part_ml[((size_t)bq * nsplit + s0 + u) * H + h];
+#pragma unroll
+        for (int u = 0; u < COMB_UNROLL; u++)
+            if (s0 + u < nsplit) M = fmaxf(M, ml[u].x);
+    }
     float Ls = 0.f;
-    for (int s = 0; s < nsplit; s++) {
-        const float2 ml = part_ml[((size_t)bq * nsplit + s) * H + h];
-        Ls += ml.x == NEG_INF ? 0.f : ml.y * __expf(ml.x - M);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += COMB_UNROLL) {
+        float2 ml[COMB_UNROLL];
+        f32x4 po[COMB_UNROLL];
+#pragma unroll
+        for (int u = 0; u < COMB_UNROLL; u++)
+            if (s0 + u < nsplit) {
+                const size_t pi = ((size_t)bq * nsplit + s0 + u) * H + h;
+                ml[u] = part_ml[pi];
+                po[u] = reinterpret_cast<const f32x4 *>(part_o + pi * D)[c4];
+            }
+#pragma unroll
+        for (int u = 0; u < COMB_UNROLL; u++)
+            if (s0 + u < nsplit && ml[u].x != NEG_INF) {
+                const float f = __expf(ml[u].x - M);
+                Ls += ml[u].y * f;
+                acc = acc + po[u] * f;
+            }
     }
-    for (int d = threadIdx.x; d < D; d += 256) {
-        float acc = 0.f;
-        for (int s = 0; s < nsplit; s++) {
-            const size_t pi = ((size_t)bq * nsplit + s) * H + h;
-            const float mx = part_ml[pi].x;
-            if (mx != NEG_INF) acc += part_o[pi * D + d] * __expf(mx - M);
-        }
-        const float v = Ls > 0.f ? acc / Ls : 0.f;
-        const size_t oi = ((size_t)bq * H + h) * D + d;
-        if (out_dt == CSA2_F32) static_cast<float *>(out)[oi] = v;
-        else static_cast<uint16_t *>(out)[oi] = f32_to_bf16_rne(v);
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    const size_t oi = ((size_t)bq * H + h) * D + 4 * c4;
+    if (out_dt == CSA2_F32) {
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + oi) = acc * inv;
+    } else {
+        const uint32_t w0 = uint32_t(f32_to_bf16_rne(acc[0] * inv)) | (uint32_t(f32_to_bf16_rne(acc[1] * inv)) << 16);
+        const uint32_t w1 = uint32_t(f32_to_bf16_rne(acc[2] * inv)) | (uint32_t(f32_to_bf16_rne(acc[3] * inv)) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + oi) = make_uint2(w0, w1);
     }
-    if (lse && threadIdx.x == 0) lse[(size_t)bq * H + h] = Ls > 0.f ? M + logf(Ls) : NEG_INF;
+    if (lse && c4 == 0) lse[row] = Ls > 0.f ? M + logf(Ls) : NEG_INF;
 }
 
 // ------------------------------------------------------------ VALU kernel
@@ -410,21 +459,37 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
     if (lse && threadIdx.x == 0) lse[(size_t)bq * H + h] = Z > 0.f ? M + logf(Z) : NEG_INF;
 }
 
+template <int D, int FMT, int HGS>
+void launch_mfma_nw(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
+                    float *lse, float *part_o, float2 *part_ml, hipStream_t s) {
+    const int blocks = p.B * p.Q * p.nsplit;
+    // two waves per head group (each owns half of the channels) while that
+    // stays within 512 threads
+    constexpr int DS = (HGS <= 4 && D >= 128) ? 2 : 1;
+    hipLaunchKernelGGL((k_attn_mfma<D, FMT, HGS, DS>), dim3(blocks), dim3(64 * HGS * DS), 0, s,
+                       static_cast<const uint16_t *>(q),
+                       static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k, scale, p.nsplit,
+                       static_cast<uint16_t *>(out), lse, part_o, part_ml);
+}
+
 template <int D, int FMT>
 void launch_mfma(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
                  float *lse, float *part_o, float2 *part_ml, hipStream_t s) {
-    const int blocks = p.B * p.Q * p.nsplit * (p.H / 16);
-    hipLaunchKernelGGL((k_attn_mfma<D, FMT>), dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t *>(q),
-                       static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k, scale, p.nsplit,
-                       static_cast<uint16_t *>(out), lse, part_o, part_ml);
+    switch (p.H / 16) {
+        case 1: launch_mfma_nw<D, FMT, 1>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        case 2: launch_mfma_nw<D, FMT, 2>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        case 4: launch_mfma_nw<D, FMT, 4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        case 8: launch_mfma_nw<D, FMT, 8>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        default: throw Error(CSA2_EUNSUPPORTED, "matrix-core attention needs H in {16, 32, 64, 128}");
+    }
 }
 
 }  // namespace
 
 AttnPlan attn_plan(int q_dt, int kv_dt, int B, int Q, int H, int D, int64_t N, int k) {
     AttnPlan p{q_dt, kv_dt, B, Q, H, D, N, k, false, 1};
-    p.mfma = q_dt == CSA2_BF16 && (kv_dt == CSA2_BF16 || kv_dt == CSA2_FP4) && H % 16 == 0 &&
-             (D == 64 || D == 128 || D == 256 || D == 512);
+    p.mfma = q_dt == CSA2_BF16 && (kv_dt == CSA2_BF16 || kv_dt == CSA2_FP4) &&
+             (H == 16 || H == 32 || H == 64 || H == 128) && (D == 64 || D == 128 || D == 256 || D == 512);
     p.nsplit = p.mfma ? (k + ATT_SPLIT - 1) / ATT_SPLIT : 1;
     return p;
 }
@@ -471,8 +536,9 @@ void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *i
 #undef CSA2_ATT_CASE
     check_launch("attention");
     if (p.nsplit > 1) {
-        hipLaunchKernelGGL(k_attn_combine, dim3(p.H, BQ), dim3(256), 0, s, part_o, part_ml, p.H, p.D, p.nsplit, out,
-                           p.q_dt, lse);
+        const int64_t threads = (int64_t)BQ * p.H * (p.D / 4);
+        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part_o, part_ml,
+                           BQ, p.H, p.D, p.nsplit, out, p.q_dt, lse);
         check_launch("attention combine");
     }
 }

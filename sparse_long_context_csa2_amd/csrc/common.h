@@ -20,6 +20,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef short __attribute__((ext_vector_type(2))) s16x2;
 
 constexpr int WAVE = 64;
 
@@ -128,6 +129,51 @@ struct TileStat {
 // worst rounding of a truncating adder; see the indexer kernels).
 __host__ __device__ inline double score_bound(double kmax, double sumwq, int HI, int dI) {
     return ldexp(1.0, -22) * double(dI + HI + 2) * kmax * sumwq * (1.0 + ldexp(1.0, -20)) + ldexp(1.0, -100);
+}
+
+// sum_h |w_h| ||q_h|| in binary64 with a fixed reduction order: groups of 16
+// threads take heads g, g + NT/16, ...; the 16 threads of a group split the
+// head's row into 16 runs (one 16-byte load each when the row allows), square
+// and sum them, and the group folds its 16 partial sums by a fixed tree.
+template <int NT>
+__device__ inline double block_sumwq(const void *qI, int dt, const float *w, int HI, int dI, int bq, double *dred) {
+    const int g = threadIdx.x >> 4, r = threadIdx.x & 15;
+    const int esz = dt == CSA2_F32 ? 4 : 2;
+    const bool vec = (dI * esz == 256) && ((reinterpret_cast<uintptr_t>(qI) & 15) == 0);
+    double acc = 0.0;
+    for (int h = g; h < HI; h += NT / 16) {
+        const size_t row = ((size_t)bq * HI + h) * dI;
+        double q2 = 0.0;
+        if (vec) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(static_cast<const char *>(qI) + row * esz)[r];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                if (dt == CSA2_F32) {
+                    const double x = (double)__uint_as_float(v[e]);
+                    q2 = fma(x, x, q2);
+                } else {
+                    const double x0 = (double)bf16_to_f32((uint16_t)(v[e] & 0xffffu));
+                    const double x1 = (double)bf16_to_f32((uint16_t)(v[e] >> 16));
+                    q2 = fma(x0, x0, q2);
+                    q2 = fma(x1, x1, q2);
+                }
+            }
+        } else {
+            for (int d = r; d < dI; d += 16) {
+                const double x = dt == CSA2_F32 ? (double)static_cast<const float *>(qI)[row + d]
+                                                : (double)bf16_to_f32(static_cast<const uint16_t *>(qI)[row + d]);
+                q2 = fma(x, x, q2);
+            }
+        }
+        for (int o = 8; o > 0; o >>= 1) q2 += __shfl_xor(q2, o, 16);
+        acc += fabs((double)w[(size_t)bq * HI + h]) * sqrt(q2);
+    }
+    if (r == 0) dred[g] = acc;
+    __syncthreads();
+    double t = 0.0;
+    for (int i = 0; i < NT / 16; i++) t += dred[i];
+    __syncthreads();
+    return t;
 }
 
 }  // namespace csa2

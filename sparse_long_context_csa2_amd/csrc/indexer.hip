@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
                                                        const int64_t *__restrict__ q_pos, int m,
                                                        const int32_t *__restrict__ cand, int P,
                                                        float *__restrict__ scores, TileStat *__restrict__ stats,
-                                                       int ntiles) {
+                                                       int ntiles, double *__restrict__ sumwq) {
     constexpr int HT = HI / 16;  // head tiles
     constexpr int KS = DI / 32;  // contraction steps
     constexpr int G = 4;         // 16-slot groups per wave
@@ -158,6 +158,11 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
         }
     }
     reduce_tile_stat(smin, smax, nval, kmax2, stats + (size_t)bq * ntiles + tile);
+    if (sumwq && tile == 0) {
+        __shared__ double dred[256 / 16];
+        const double v = block_sumwq<256>(qI, CSA2_BF16, w, HI, DI, bq, dred);
+        if (threadIdx.x == 0) sumwq[bq] = v;
+    }
 }
 
 // ---------------------------------------------------------------- VALU path
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(256) void k_index_valu(const void *__restrict__ qI,
                                                     const int64_t *__restrict__ q_pos, int m,
                                                     const int32_t *__restrict__ cand, int P,
                                                     float *__restrict__ scores, TileStat *__restrict__ stats,
-                                                    int ntiles) {
+                                                    int ntiles, double *__restrict__ sumwq) {
     extern __shared__ float qs[];  // [HI * dI]
     const int bq = blockIdx.y;
     const int b = bq / Q;
@@ -201,6 +206,11 @@ __global__ __launch_bounds__(256) void k_index_valu(const void *__restrict__ qI,
     if (slot < n) scores[(int64_t)bq * n + slot] = valid ? s : NEG_INF;
     reduce_tile_stat(valid ? s : POS_INF, valid ? s : NEG_INF, valid ? 1u : 0u, valid ? ss : 0.f,
                      stats + (size_t)bq * ntiles + blockIdx.x);
+    if (sumwq && blockIdx.x == 0) {
+        __shared__ double dred[256 / 16];
+        const double v = block_sumwq<256>(qI, dt, w, HI, dI, bq, dred);
+        if (threadIdx.x == 0) sumwq[bq] = v;
+    }
 }
 
 // ------------------------------------------------------------- error bound
@@ -216,35 +226,17 @@ __global__ __launch_bounds__(256) void k_index_valu(const void *__restrict__ qI,
 __global__ __launch_bounds__(256) void k_err_bound(const void *__restrict__ qI, int dt, const float *__restrict__ w,
                                                    int HI, int dI, const TileStat *__restrict__ stats, int ntiles,
                                                    float *__restrict__ err32, double *__restrict__ err64) {
-    __shared__ double red[256];
-    __shared__ float kred[256];
+    __shared__ double dred[256 / 16];
+    __shared__ float kred[4];
     const int bq = blockIdx.x;
     float km = 0.f;
     for (int t = threadIdx.x; t < ntiles; t += 256) km = fmaxf(km, stats[(size_t)bq * ntiles + t].kmax2);
-    double acc = 0.0;
-    for (int h = threadIdx.x; h < HI; h += 256) {
-        double q2 = 0.0;
-        for (int d = 0; d < dI; d++) {
-            size_t off = ((size_t)bq * HI + h) * dI + d;
-            double v = dt == CSA2_F32 ? (double)static_cast<const float *>(qI)[off]
-                                      : (double)bf16_to_f32(static_cast<const uint16_t *>(qI)[off]);
-            q2 += v * v;
-        }
-        acc += fabs((double)w[(size_t)bq * HI + h]) * sqrt(q2);
-    }
-    red[threadIdx.x] = acc;
-    kred[threadIdx.x] = km;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (threadIdx.x < o) {
-            red[threadIdx.x] += red[threadIdx.x + o];
-            kred[threadIdx.x] = fmaxf(kred[threadIdx.x], kred[threadIdx.x + o]);
-        }
-        __syncthreads();
-    }
+    km = wave_max(km);
+    if ((threadIdx.x & 63) == 0) kred[threadIdx.x >> 6] = km;
+    const double sumwq = block_sumwq<256>(qI, dt, w, HI, dI, bq, dred);  // has barriers
     if (threadIdx.x == 0) {
-        double kmax = sqrt((double)kred[0] * (1.0 + ldexp(1.0, -10)));
-        double E = score_bound(kmax, red[0] * (1.0 + ldexp(1.0, -30)), HI, dI);
+        const float k2 = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
+        const double E = score_bound(sqrt((double)k2 * (1.0 + ldexp(1.0, -10))), sumwq * (1.0 + ldexp(1.0, -30)), HI, dI);
         if (err64) err64[bq] = E;
         if (err32) {
             float e = (float)E;
@@ -254,12 +246,29 @@ __global__ __launch_bounds__(256) void k_err_bound(const void *__restrict__ qI, 
     }
 }
 
+__global__ __launch_bounds__(256) void k_err_from_norms(const double *__restrict__ sumwq, int HI, int dI,
+                                                       const TileStat *__restrict__ stats, int ntiles,
+                                                       double *__restrict__ err64) {
+    __shared__ float kred[4];
+    const int bq = blockIdx.x;
+    float km = 0.f;
+    for (int t = threadIdx.x; t < ntiles; t += 256) km = fmaxf(km, stats[(size_t)bq * ntiles + t].kmax2);
+    km = wave_max(km);
+    if ((threadIdx.x & 63) == 0) kred[threadIdx.x >> 6] = km;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float k2 = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
+        err64[bq] = score_bound(sqrt((double)k2 * (1.0 + ldexp(1.0, -10))), sumwq[bq] * (1.0 + ldexp(1.0, -30)), HI, dI);
+    }
+}
+
 template <int HI, int DI>
 void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, int64_t N, const int64_t *q_pos,
-                 int m, const int32_t *cand, int P, float *scores, TileStat *stats, int ntiles, hipStream_t s) {
+                 int m, const int32_t *cand, int P, float *scores, TileStat *stats, int ntiles, double *sumwq,
+                 hipStream_t s) {
     dim3 grid(ntiles, B * Q);
     hipLaunchKernelGGL((k_index_mfma<HI, DI>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
-                       static_cast<const uint16_t *>(kI), Q, N, q_pos, m, cand, P, scores, stats, ntiles);
+                       static_cast<const uint16_t *>(kI), Q, N, q_pos, m, cand, P, scores, stats, ntiles, sumwq);
 }
 
 }  // namespace
@@ -281,13 +290,13 @@ bool index_valu_supported(int HI, int dI) { return (int64_t)HI * dI <= 16384; }
 
 void launch_index_score(const void *qI, int dt, const float *w, const void *kI, int B, int Q, int HI, int dI,
                         int64_t N, const int64_t *q_pos, int m, const int32_t *cand, int P, float *scores,
-                        TileStat *stats, hipStream_t s) {
+                        TileStat *stats, double *sumwq, hipStream_t s) {
     const int64_t n = cand ? (int64_t)P : N;
     const int ntiles = (int)((n + TILE - 1) / TILE);
     if (index_mfma_supported(dt, HI, dI)) {
 #define CSA2_IDX_CASE(h, d)                                                                        \
     case h * 1000 + d:                                                                              \
-        launch_mfma<h, d>(qI, w, kI, B, Q, N, q_pos, m, cand, P, scores, stats, ntiles, s);      \
+        launch_mfma<h, d>(qI, w, kI, B, Q, N, q_pos, m, cand, P, scores, stats, ntiles, sumwq, s); \
         break;
         switch (HI * 1000 + dI) {
             CSA2_IDX_CASE(16, 32) CSA2_IDX_CASE(16, 64) CSA2_IDX_CASE(16, 128) CSA2_IDX_CASE(16, 256)
@@ -300,9 +309,15 @@ void launch_index_score(const void *qI, int dt, const float *w, const void *kI, 
         dim3 grid(ntiles, B * Q);
         size_t lds = sizeof(float) * (size_t)HI * dI;
         hipLaunchKernelGGL(k_index_valu, grid, dim3(256), lds, s, qI, dt, w, kI, Q, HI, dI, N, q_pos, m, cand, P,
-                           scores, stats, ntiles);
+                           scores, stats, ntiles, sumwq);
     }
     check_launch("index score");
+}
+
+void launch_err_bound_from_norms(const double *sumwq, int BQ, int HI, int dI, const TileStat *stats, int ntiles,
+                                 double *err64, hipStream_t s) {
+    hipLaunchKernelGGL(k_err_from_norms, dim3(BQ), dim3(256), 0, s, sumwq, HI, dI, stats, ntiles, err64);
+    check_launch("error bound");
 }
 
 void launch_err_bound(const void *qI, int dt, const float *w, int BQ, int HI, int dI, const TileStat *stats,

@@ -10,9 +10,11 @@ bool index_mfma_supported(int dt, int HI, int dI);
 bool index_valu_supported(int HI, int dI);
 void launch_index_score(const void *qI, int dt, const float *w, const void *kI, int B, int Q, int HI, int dI,
                         int64_t N, const int64_t *q_pos, int m, const int32_t *cand, int P, float *scores,
-                        TileStat *stats, hipStream_t s);
+                        TileStat *stats, double *sumwq, hipStream_t s);
 void launch_err_bound(const void *qI, int dt, const float *w, int BQ, int HI, int dI, const TileStat *stats,
                       int ntiles, float *err32, double *err64, hipStream_t s);
+void launch_err_bound_from_norms(const double *sumwq, int BQ, int HI, int dI, const TileStat *stats, int ntiles,
+                                 double *err64, hipStream_t s);
 
 // -------------------------------------------------------------- selection
 struct SelPlan {
@@ -30,11 +32,12 @@ struct RescoreArgs {
     const void *kI;
     int Q, HI, dI;
     int64_t N;
+    const double *sumwq;  // [BQ] sum_h |w_h| ||q_h|| written by the indexer
 };
 size_t rescore_lds_bytes(int HI, int dI);  // must stay <= 64 KiB
 SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified);
 size_t sel_workspace(const SelPlan &p, bool own_stats);
-void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats, const double *ebound,
+void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats,
              const RescoreArgs *rs, int32_t *out0, int32_t *count0, int32_t *out1, void *ws, size_t ws_bytes,
              hipStream_t s);
 

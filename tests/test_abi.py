@@ -37,8 +37,8 @@ def test_every_declared_symbol_is_exported():
 def test_workspace_sizes_grow_with_problem():
     assert b._topk_ws(1, 1, 1000, 10) < b._topk_ws(1, 1, 100000, 10) < b._topk_ws(4, 1, 100000, 10)
     assert b._index_ws(b.BF16, 16, 1, 64, 128, 32768, 0) > 0
-    assert b._attn_ws(b.BF16, b.BF16, 16, 1, 64, 512, 2048) > 0       # split over 4 blocks of 512
-    assert b._attn_ws(b.BF16, b.BF16, 16, 1, 64, 512, 512) == 0       # one split: no partials
+    assert b._attn_ws(b.BF16, b.BF16, 16, 1, 64, 512, 2048) > 0       # split over blocks of 128 entries
+    assert b._attn_ws(b.BF16, b.BF16, 16, 1, 64, 512, 128) == 0       # one split: no partials
     assert b._compress_ws(b.BF16, 1024, 512, 4, 1) >= 4100 * 512 * 4
 
 
