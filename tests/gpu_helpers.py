@@ -2,6 +2,8 @@
 import numpy as np
 import torch
 
+import oracle
+
 ATOL_BF16, RTOL_BF16 = 1e-2, 2e-2   # bf16 / FP4 attention outputs
 ATOL_F32, RTOL_F32 = 1e-5, 1e-5     # fp32 configuration
 
@@ -36,3 +38,37 @@ def assert_scores_within_bound(scores, err, ref):
     worst = (diff / e[..., None]).max()
     assert worst <= 1.0, f"fp32 score outside its bound: max |s - ref| / E = {worst}"
     return worst
+
+
+def run_group(b, d, q_pos=None):
+    """Run the spec's layer list on the GPU and in the oracle; compare each layer."""
+    spec = d["spec"]
+    kv, kI = dev(d["kv"]), dev(d["kI"])
+    g_pool = g_idx = None
+    r_pool = r_idx = None
+    atol, rtol = (ATOL_F32, RTOL_F32) if spec.kv_fmt == "f32" else (ATOL_BF16, RTOL_BF16)
+    for li, lay in enumerate(d["layers"]):
+        mode = lay["mode"]
+        kw = dict(q=dev(lay["q"]), kv=kv, k=spec.k, scale=spec.scale)
+        rkw = dict(q=lay["q"], kv=d["kv"], k=spec.k, scale=spec.scale)
+        if mode in ("FULL", "REINDEX"):
+            kw.update(qI=dev(lay["qI"]), w=dev(lay["w"]), kI=kI, q_pos=dev(q_pos), m=spec.m)
+            rkw.update(qI=lay["qI"], w=lay["w"], kI=d["kI"], q_pos=q_pos, m=spec.m)
+        if mode == "FULL":
+            kw["P"] = rkw["P"] = spec.P
+        elif mode == "REINDEX":
+            kw["pool"], rkw["pool"] = g_pool, r_pool
+        else:
+            kw["idx"], rkw["idx"] = g_idx, r_idx
+        g = b.layer(mode, **kw)
+        torch.cuda.synchronize()
+        r = oracle.layer(mode, **rkw)
+        if mode != "REUSE":
+            assert np.array_equal(host(g["idx"]).numpy(), r["idx"]), f"layer {li} ({mode}): idx differs"
+            assert np.array_equal(host(g["count"]).numpy(), r["count"]), f"layer {li}: count differs"
+            g_idx, r_idx = g["idx"], r["idx"]
+        if mode == "FULL" and spec.P > 0:
+            assert np.array_equal(host(g["pool"]).numpy(), r["pool"]), f"layer {li}: pool differs"
+            g_pool, r_pool = g["pool"], r["pool"]
+        assert_close(g["out"], r["out"], atol, rtol, f"layer {li} ({mode}) output")
+        assert_close(g["lse"], r["lse"], atol, rtol, f"layer {li} ({mode}) lse")

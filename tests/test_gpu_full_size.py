@@ -1,0 +1,109 @@
+"""Parity at the workloads' full sizes.
+
+* 128K-token decode (16 x 32,768 entries, bf16 KV), one Full layer: every
+  output compared with the oracle, on the seeded inputs and on the inputs the
+  benchmark draws, through the same prepared-layer launch the benchmark times.
+* 128K-token decode with FP4 KV: one Full layer and five Reuse layers.
+* 1M-token decode (4 x 262,144 entries): Full layer with its 16,384-entry pool,
+  then three Reindex layers inside the pool.
+* Prefill chunk (4,096 causal queries at the end of a 65,536-token context):
+  compression of the whole context on the GPU, then one Full layer over all
+  4,096 rows; 64 rows (first and last included) compared with the oracle, and
+  the compressed entries compared on samples.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import ATOL_BF16, RTOL_BF16, assert_close, dev, host, run_group
+from sparse_long_context_csa2_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_long_context_csa2_amd import binding
+    return binding
+
+
+def test_decode_128k_full_layer(b):
+    run_group(b, synth.make_decode(synth.decode_128k(seed=1)))
+
+
+def test_decode_128k_benchmark_inputs(b):
+    """The benchmark's own GPU-drawn inputs and prepared Layer, checked whole."""
+    sys.path.insert(0, ROOT)
+    import bench
+    W = bench.WORKLOAD
+    s = bench.make_sets(torch, 1)[0]
+    scale = W["D"] ** -0.5
+    L = b.Layer("FULL", q=s["q"], kv=s["kv"], k=W["k"], scale=scale, qI=s["qI"], w=s["w"], kI=s["kI"])
+    L.run()
+    L.run()  # a second launch on the same workspace must give the same answer
+    torch.cuda.synchronize()
+    cpu = {k: host(v) for k, v in s.items()}
+    r = oracle.layer("FULL", k=W["k"], scale=scale, q=cpu["q"], kv=cpu["kv"], qI=cpu["qI"], w=cpu["w"],
+                     kI=cpu["kI"])
+    assert np.array_equal(host(L.idx).numpy(), r["idx"])
+    assert np.array_equal(host(L.count).numpy(), r["count"])
+    assert_close(L.out, r["out"], ATOL_BF16, RTOL_BF16, "output")
+    assert_close(L.lse, r["lse"], ATOL_BF16, RTOL_BF16, "lse")
+
+
+def test_decode_128k_fp4_full_plus_five_reuse(b):
+    run_group(b, synth.make_decode(synth.decode_128k_fp4_group(seed=2)))
+
+
+def test_decode_1m_pool_and_three_reindex(b):
+    run_group(b, synth.make_decode(synth.decode_1m_hier(seed=3)))
+
+
+def test_prefill_chunk_sampled_rows(b):
+    spec = synth.Prefill(seed=4)
+    d = synth.make_prefill(spec)
+    T, m, Qc = spec.T, spec.m, spec.Qc
+    n_ent = T // m
+    x, xI = dev(d["x"]), dev(d["xI"])
+    wz, wzI, bias, biasI = dev(d["wz"]), dev(d["wzI"]), dev(d["bias"]), dev(d["biasI"])
+    kv = b.compress(x, n_ent, m, 0, wz, bias)
+    kI = b.compress(xI, n_ent, m, 0, wzI, biasI)
+    # the chunk's own entries, compressed from the chunk and a one-group halo
+    first = (T - Qc) // m
+    kv_chunk = b.compress(x[(T - Qc - m):].contiguous(), Qc // m, m, 1, wz, bias)
+    torch.cuda.synchronize()
+    assert torch.equal(kv_chunk, kv[first:]), "chunked compression differs from whole-context compression"
+
+    # compressed entries on samples: the first entries (masked previous group) and the last ones
+    for lo, hi in ((0, 48), (n_ent - 48, n_ent)):
+        halo = 0 if lo == 0 else 1
+        t0 = lo * m - halo * m
+        xs = d["x"][t0: hi * m]
+        ref = oracle.compress(xs, hi - lo, m, halo, d["wz"], d["bias"])
+        assert_close(kv[lo:hi], ref, ATOL_BF16, RTOL_BF16, f"compressed KV entries {lo}..{hi}")
+        xsI = d["xI"][t0: hi * m]
+        refI = oracle.compress(xsI, hi - lo, m, halo, d["wzI"], d["biasI"])
+        assert_close(kI[lo:hi], refI, ATOL_BF16, RTOL_BF16, f"compressed indexer keys {lo}..{hi}")
+
+    # one Full layer over all queries of the chunk
+    q_pos = d["q_pos"]
+    L = b.Layer("FULL", q=dev(d["q"]), kv=kv.view(1, n_ent, spec.D), k=spec.k, scale=spec.scale, qI=dev(d["qI"]),
+                w=dev(d["w"]), kI=kI.view(1, n_ent, spec.dI), q_pos=dev(q_pos), m=m)
+    L.run()
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, Qc - 1, 64).round().astype(np.int64))
+    kv_h, kI_h = host(kv).view(1, n_ent, spec.D), host(kI).view(1, n_ent, spec.dI)
+    r = oracle.layer("FULL", k=spec.k, scale=spec.scale, q=d["q"][:, rows], kv=kv_h, qI=d["qI"][:, rows],
+                     w=d["w"][:, rows], kI=kI_h, q_pos=q_pos[:, rows], m=m)
+    assert np.array_equal(host(L.idx)[:, rows].numpy(), r["idx"])
+    assert np.array_equal(host(L.count)[:, rows].numpy(), r["count"])
+    assert_close(host(L.out)[:, rows], r["out"], ATOL_BF16, RTOL_BF16, "prefill output rows")
+    assert_close(host(L.lse)[:, rows], r["lse"], ATOL_BF16, RTOL_BF16, "prefill lse rows")
