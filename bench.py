@@ -26,6 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+COPY_BYTES = 1 << 30  # counter calibration: bytes read and written by one plain copy
 WORKLOAD = dict(B=16, Q=1, N=32768, HI=64, dI=128, H=64, D=512, k=2048, m=4, ctx_tokens=131072)
 
 
@@ -37,8 +38,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["indexer", "attention", "layer"], default=None,
-                    help="launch only this part, for counter collection (prints no JSON)")
+    ap.add_argument("--only", choices=["indexer", "attention", "layer", "copy"], default=None,
+                    help="launch only this part, for counter collection (prints no JSON); 'copy' is a plain "
+                         "1 GiB device-to-device copy that calibrates the byte counters")
     return ap.parse_args()
 
 
@@ -124,6 +126,15 @@ def main():
         sys.exit(2)
     import torch
     from sparse_long_context_csa2_amd import binding as b
+
+    if a.only == "copy":
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(a.warmup + a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {COPY_BYTES} bytes {a.warmup + a.steps} times", flush=True)
+        return
 
     W = WORKLOAD
     scale = W["D"] ** -0.5
