@@ -165,6 +165,142 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
     }
 }
 
+// ----------------------------------------------------------- streaming path
+// Same contraction and operand layouts as k_index_mfma, for full scans with
+// many tiles: each wave owns one 256-slot tile and walks it in 4 steps of 64
+// slots.  The key fragments of a 16-slot group are reloaded with the next
+// step's rows as soon as the group's matrix-core products are issued, so a
+// wave keeps about 16 KiB of keys in flight from start to end with a single
+// register buffer.  The query fragments and head weights are loaded once per
+// wave.  A step's 64 scores leave in one coalesced store (lane l writes slot
+// 64 * step + l), and the tile statistics are a wave reduction.
+template <int HI, int DI>
+__global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restrict__ qI, const float *__restrict__ w,
+                                                         const uint16_t *__restrict__ kI, int Q, int64_t N,
+                                                         const int64_t *__restrict__ q_pos, int m,
+                                                         float *__restrict__ scores, TileStat *__restrict__ stats,
+                                                         int ntiles, double *__restrict__ sumwq) {
+    constexpr int HT = HI / 16;
+    constexpr int KS = DI / 32;
+    constexpr int G = 4;           // 16-slot groups per step
+    constexpr int IT = TILE / 64;  // steps per tile
+    const int bq = blockIdx.y;
+    const int b = bq / Q;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, kg = lane >> 4;
+    const int64_t nvis = visible_entries(q_pos, bq, m, N);  // slots >= nvis are not scored
+    const int tile = blockIdx.x * 4 + wave;
+
+    if (tile < ntiles) {
+        const int64_t slot0 = (int64_t)tile * TILE;
+        // Rows past the visible range are clamped to the last row of the key
+        // cache and loaded anyway (no branch around the loads); their scores
+        // are replaced by -inf and they take no part in the statistics.
+        const uint16_t *kb0 = kI + (size_t)b * N * DI + 8 * kg;
+        const int64_t last = N - 1;
+        auto krow = [&](int64_t r) {
+            const int64_t j = slot0 + r + col;
+            return kb0 + (size_t)(j < last ? j : last) * DI;
+        };
+        u32x4 kb[G][KS];
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            const uint16_t *kr = krow(g * 16);
+#pragma unroll
+            for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
+        }
+        u32x4 qa[HT][KS];
+        const uint16_t *qrow = qI + (size_t)bq * HI * DI;
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+            for (int s = 0; s < KS; s++)
+                qa[ht][s] = *reinterpret_cast<const u32x4 *>(qrow + (ht * 16 + col) * DI + 32 * s + 8 * kg);
+        f32x4 wv[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++)
+            wv[ht] = *reinterpret_cast<const f32x4 *>(w + (size_t)bq * HI + ht * 16 + 4 * kg);
+
+        float smin = POS_INF, smax = NEG_INF, kmax2 = 0.f;
+        uint32_t nval = 0;
+#pragma unroll
+        for (int it = 0; it < IT; it++) {
+            float part[G], ss[G];
+#pragma unroll
+            for (int g = 0; g < G; g++) {
+                f32x4 acc[HT];
+#pragma unroll
+                for (int ht = 0; ht < HT; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; s++)
+#pragma unroll
+                    for (int ht = 0; ht < HT; ht++)
+                        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ht][s]),
+                                                                          __builtin_bit_cast(bf16x8, kb[g][s]),
+                                                                          acc[ht], 0, 0, 0);
+                float q2 = 0.f;
+#pragma unroll
+                for (int s = 0; s < KS; s++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        bf16x2 v = __builtin_bit_cast(bf16x2, kb[g][s][e]);
+                        q2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, q2, false);
+                    }
+                ss[g] = q2;
+                if (it + 1 < IT) {  // this group's rows of the next step
+                    const uint16_t *kr = krow((it + 1) * 64 + g * 16);
+#pragma unroll
+                    for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
+                }
+                float p = 0.f;
+#pragma unroll
+                for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) p = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), p);
+                part[g] = p;
+                // keep each group's reload where it is: hoisting them all would need a second buffer
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int g = 0; g < G; g++) {
+                part[g] += __shfl_xor(part[g], 16);
+                part[g] += __shfl_xor(part[g], 32);
+                ss[g] += __shfl_xor(ss[g], 16);
+                ss[g] += __shfl_xor(ss[g], 32);
+            }
+            // lane l = 16 kg + col stores slot 64 it + l, i.e. group kg's row col
+            const float mine = kg == 0 ? part[0] : kg == 1 ? part[1] : kg == 2 ? part[2] : part[3];
+            const float mss = kg == 0 ? ss[0] : kg == 1 ? ss[1] : kg == 2 ? ss[2] : ss[3];
+            const int64_t slot = slot0 + it * 64 + lane;
+            const bool ok = slot < nvis;
+            if (slot < N) scores[(int64_t)bq * N + slot] = ok ? mine : NEG_INF;
+            if (ok) {
+                smin = fminf(smin, mine);
+                smax = fmaxf(smax, mine);
+                kmax2 = fmaxf(kmax2, mss);
+                nval++;
+            }
+        }
+        smin = wave_min(smin);
+        smax = wave_max(smax);
+        kmax2 = wave_max(kmax2);
+        nval = wave_sum_u32(nval);
+        if (lane == 0) {
+            TileStat t;
+            t.smin = smin;
+            t.smax = smax;
+            t.kmax2 = kmax2;
+            t.nvalid = nval;
+            stats[(size_t)bq * ntiles + tile] = t;
+        }
+    }
+    if (sumwq && blockIdx.x == 0) {
+        __shared__ double dred[256 / 16];
+        const double v = block_sumwq<256>(qI, CSA2_BF16, w, HI, DI, bq, dred);
+        if (threadIdx.x == 0) sumwq[bq] = v;
+    }
+}
+
 // ---------------------------------------------------------------- VALU path
 // Any head count / dim / dtype: one slot per thread, fp32 FMA in sequential
 // order, query heads staged in LDS as fp32.
@@ -262,10 +398,23 @@ __global__ __launch_bounds__(256) void k_err_from_norms(const double *__restrict
     }
 }
 
+// Registers of the streaming kernel: query fragments HI*DI/128 plus key
+// fragments DI/2.
+constexpr bool stream_fits(int HI, int DI) { return HI * DI / 128 + DI / 2 <= 128; }
+constexpr int64_t STREAM_MIN_TILES = 1024;  // below this, one tile per block fills the chip better
+
 template <int HI, int DI>
 void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, int64_t N, const int64_t *q_pos,
                  int m, const int32_t *cand, int P, float *scores, TileStat *stats, int ntiles, double *sumwq,
                  hipStream_t s) {
+    if constexpr (stream_fits(HI, DI)) {
+        if (!cand && (int64_t)B * Q * ntiles >= STREAM_MIN_TILES) {
+            dim3 grid((ntiles + 3) / 4, B * Q);
+            hipLaunchKernelGGL((k_index_stream<HI, DI>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
+                               static_cast<const uint16_t *>(kI), Q, N, q_pos, m, scores, stats, ntiles, sumwq);
+            return;
+        }
+    }
     dim3 grid(ntiles, B * Q);
     hipLaunchKernelGGL((k_index_mfma<HI, DI>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
                        static_cast<const uint16_t *>(kI), Q, N, q_pos, m, cand, P, scores, stats, ntiles, sumwq);

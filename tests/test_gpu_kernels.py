@@ -44,6 +44,24 @@ def test_index_score_within_reported_bound(b, B, Q, N, HI, dI, dt):
     print(f"max |s - ref| / E = {worst:.3e}, E = {host(e).max().item():.3e}")
 
 
+@pytest.mark.parametrize("HI,dI", [(64, 128), (128, 64), (16, 128)])
+def test_index_score_streaming_path_causal_ragged(b, HI, dI):
+    """Launches of at least 1024 tiles take the streaming kernel: ragged N,
+    causal queries that see none, part, or all of the entries (tails inside a
+    tile, inside a 64-slot step and at a tile edge)."""
+    rng = np.random.default_rng(HI * dI)
+    B, Q, N, m = 2, 3, 175_001, 4
+    kI = synth.normal_bf16(rng, (B, N, dI))
+    qI = synth.normal_bf16(rng, (B, Q, HI, dI))
+    w = synth.uniform_f32(rng, (B, Q, HI))
+    pos = torch.tensor([[-1, 4 * 1000 + 2, 10**7], [4 * 256 - 1, 4 * 64 * 1001 + 3, 4 * 175_000 + 1]],
+                       dtype=torch.int64)
+    ref = oracle.index_score(qI, w, kI, q_pos=pos, m=m)
+    s, e = b.index_score(dev(qI), dev(w), dev(kI), q_pos=dev(pos), m=m)
+    torch.cuda.synchronize()
+    assert_scores_within_bound(s, e, ref)
+
+
 def test_index_score_causal_and_candidates(b):
     rng = np.random.default_rng(7)
     N, m = 600, 4
