@@ -120,8 +120,9 @@ void check_layer(const csa2_layer_args *a) {
     opt_ptr(a->scores, "scores");
     opt_ptr(a->q_pos, "q_pos");
     if (a->q_pos && a->m < 1) throw Error(CSA2_EINVAL, "m must be >= 1 with q_pos");
-    if (csa2::rescore_lds_bytes(a->HI, a->dI) > 65536)
-        throw Error(CSA2_EUNSUPPORTED, "indexer heads x dim too large for the binary64 rescoring kernel");
+    if (!csa2::rescore_supported(a->idx_dt, a->dI))
+        throw Error(CSA2_EUNSUPPORTED, "certified selection needs indexer rows of whole 16-byte vectors "
+                                       "(dI % 4 == 0 for fp32, dI % 8 == 0 for bf16)");
     if (a->mode == CSA2_FULL) {
         if (a->P < 0) throw Error(CSA2_EINVAL, "P must be >= 0");
         if (a->P > 0) need_ptr(a->pool, "pool");

@@ -220,6 +220,32 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
 #pragma unroll
         for (int ht = 0; ht < HT; ht++)
             wv[ht] = *reinterpret_cast<const f32x4 *>(w + (size_t)bq * HI + ht * 16 + 4 * kg);
+        if (sumwq && tile == 0) {
+            // sum_h |w_h| ||q_h|| in binary64 from the query fragments in
+            // registers (lane (col, kg) holds 8 KS elements of head 16 ht + col),
+            // while the first key rows are in flight.  Fixed order: lane
+            // partials, then kg pairs, then a butterfly over col, then ht.
+            double acc = 0.0;
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++) {
+                double q2 = 0.0;
+#pragma unroll
+                for (int s2 = 0; s2 < KS; s2++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const double x0 = (double)bf16_to_f32((uint16_t)(qa[ht][s2][e] & 0xffffu));
+                        const double x1 = (double)bf16_to_f32((uint16_t)(qa[ht][s2][e] >> 16));
+                        q2 = fma(x0, x0, q2);
+                        q2 = fma(x1, x1, q2);
+                    }
+                q2 += __shfl_xor(q2, 16);
+                q2 += __shfl_xor(q2, 32);
+                double t = fabs((double)w[(size_t)bq * HI + ht * 16 + col]) * sqrt(q2);
+                for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o);
+                acc += t;
+            }
+            if (lane == 0) sumwq[bq] = acc;
+        }
 
         float smin = POS_INF, smax = NEG_INF, kmax2 = 0.f;
         uint32_t nval = 0;
@@ -293,11 +319,6 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
             t.nvalid = nval;
             stats[(size_t)bq * ntiles + tile] = t;
         }
-    }
-    if (sumwq && blockIdx.x == 0) {
-        __shared__ double dred[256 / 16];
-        const double v = block_sumwq<256>(qI, CSA2_BF16, w, HI, DI, bq, dred);
-        if (threadIdx.x == 0) sumwq[bq] = v;
     }
 }
 

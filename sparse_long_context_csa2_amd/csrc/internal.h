@@ -34,7 +34,7 @@ struct RescoreArgs {
     int64_t N;
     const double *sumwq;  // [BQ] sum_h |w_h| ||q_h|| written by the indexer
 };
-size_t rescore_lds_bytes(int HI, int dI);  // must stay <= 64 KiB
+bool rescore_supported(int dt, int dI);  // rows of whole 16-byte vectors
 SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified);
 size_t sel_workspace(const SelPlan &p, bool own_stats);
 void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats,

@@ -374,15 +374,17 @@ template <int NT>
 __device__ void finish_target(uint32_t *bm, int64_t nwords, int64_t n, int32_t K, int32_t in_cnt, int32_t nb,
                               const int32_t *list, const double *bs, const float *scores_q,
                               const int32_t *cand_q, int32_t *dst, int32_t *count_dst, uint64_t *key_lds,
-                              int32_t *slot_lds, int32_t *out_lds, int out_cap, uint32_t *red) {
+                              int32_t *slot_lds, int32_t *out_lds, int out_cap, uint32_t *red,
+                              bool preloaded = false) {
     const int32_t r = K - in_cnt;
     auto exact_key = [&](int32_t i) -> uint64_t { return dkey(bs ? bs[i] : (double)scores_q[list[i]]); };
     if (r > 0 && nb > 0) {
         if (nb <= BANDFAST) {
-            for (int32_t i = threadIdx.x; i < nb; i += NT) {
-                key_lds[i] = exact_key(i);
-                slot_lds[i] = list[i];
-            }
+            if (!preloaded)
+                for (int32_t i = threadIdx.x; i < nb; i += NT) {
+                    key_lds[i] = exact_key(i);
+                    slot_lds[i] = list[i];
+                }
             __syncthreads();
             for (int32_t i = threadIdx.x; i < nb; i += NT) {
                 const uint64_t ki = key_lds[i];
@@ -398,11 +400,11 @@ __device__ void finish_target(uint32_t *bm, int64_t nwords, int64_t n, int32_t K
                         ss[u] = slot_lds[j0 + u];
                     }
 #pragma unroll
-                    for (int u = 0; u < 16; u++) rank += (kk[u] > ki) || (kk[u] == ki && ss[u] < si);
+                    for (int u = 0; u < 16; u++) rank += (int)((kk[u] > ki) | ((kk[u] == ki) & (ss[u] < si)));
                 }
                 for (; j0 < nb; j0++) {
                     const uint64_t kj = key_lds[j0];
-                    rank += (kj > ki) || (kj == ki && slot_lds[j0] < si);
+                    rank += (int)((kj > ki) | ((kj == ki) & (slot_lds[j0] < si)));
                 }
                 if (rank < r) atomicOr(&bm[si >> 5], 1u << (si & 31));
             }
@@ -471,20 +473,22 @@ __device__ void finish_target(uint32_t *bm, int64_t nwords, int64_t n, int32_t K
     __syncthreads();
 }
 
-// ------------------------------------------------------ fused small path
-// One 512-thread block per query keeps its n <= 32768 scores in LDS.  With
-// the score range known from the indexer's tile statistics, the histogram is
-// built while loading; the bin edges of the K-th largest come from a 64-way
-// search on the float key space; classification compares in fp32 against
-// thresholds rounded outward.  Exact mode also picks the band and compacts
-// (one launch); certified mode hands the bitmap and band list on.  Slot s is
-// read by thread s % 512, so a wave's 64 consecutive slots give two bitmap
-// words straight from one ballot.
-constexpr int SMALL_NT = 512;
-constexpr int64_t SMALL_N = 32768;
-constexpr int SPT = (int)(SMALL_N / SMALL_NT);
+// ------------------------------------------------------ one-block path
+// One 1024-thread block per query keeps its n <= 32768 scores in registers
+// (slot s in thread s % 1024, so a wave's 64 consecutive slots give two
+// bitmap words straight from one ballot).  With the score range known from
+// the indexer's tile statistics (else from the scores), the 2048-bin
+// histogram is built from registers, the bin edges of the K-th largest come
+// from a 64-way search in a narrow window around their estimate, and the
+// classification compares in fp32 against thresholds rounded outward.  Exact
+// mode also picks the band and compacts (one launch); certified mode hands
+// the IN bitmap and the band list on.
+constexpr int ONE_NT = 1024;
+constexpr int64_t ONE_N = 32768;
+constexpr int ONE_SPT = (int)(ONE_N / ONE_NT);
+constexpr int ONE_OUT = 8192;  // output entries staged in LDS
 
-struct SmallArgs {
+struct OneArgs {
     const float *scores;
     const int32_t *cand;
     int64_t n;
@@ -505,138 +509,131 @@ struct SmallArgs {
     int64_t band_cap;
 };
 
+// Smallest key in [lk, hk] whose bin is >= target (hk + 1 if none): a 64-way
+// search in a window of +-2048 keys around the estimate lo + target / inv,
+// checked to bracket the answer, else over the whole range.
+__device__ uint32_t edge_key(uint32_t lk, uint32_t hk, int target, float lo, float inv) {
+    if (inv > 0.f) {
+        const uint32_t ke0 = fkey(lo + (float)target / inv);
+        const uint32_t ke = ke0 < lk ? lk : (ke0 > hk ? hk : ke0);
+        const uint32_t L = ke - lk > 2048u ? ke - 2048u : lk;
+        const uint32_t R = hk - ke > 2048u ? ke + 2048u : hk;
+        const bool okL = L == lk || sel_bin(fkey_inv(L), lo, inv) < target;
+        const bool okR = R == hk || sel_bin(fkey_inv(R), lo, inv) >= target;
+        if (okL && okR) return wave_search_bin(L, R, target, lo, inv);
+    }
+    return wave_search_bin(lk, hk, target, lo, inv);
+}
+
 template <bool CERT>
-__global__ __launch_bounds__(SMALL_NT) void k_sel_small(SmallArgs a) {
-    __shared__ __attribute__((aligned(16))) float sc[SMALL_N];  // reused by exact mode's finishing step
+__global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     __shared__ uint32_t hist[NB];
     __shared__ uint32_t cum[NB + 1];
-    __shared__ uint32_t bm[SMALL_N / 32];
-    __shared__ uint32_t red[SMALL_NT / 64];
-    __shared__ float fred[3][SMALL_NT / 64];
-    __shared__ uint32_t grp_sum[SMALL_NT];
+    __shared__ uint32_t bm[ONE_N / 32];
+    __shared__ uint32_t red[ONE_NT / 64];
+    __shared__ f32x4 rred[ONE_NT / 64];
+    __shared__ uint32_t grp_sum[ONE_NT];
     __shared__ int bstar_sh;
     __shared__ uint32_t edge_sh[2];
-    __shared__ int32_t band_cnt_sh;
+    __shared__ int32_t band_cnt_sh, in_cnt_sh;
+    // exact mode's finishing scratch
+    __shared__ uint64_t key_lds[CERT ? 1 : BANDFAST];
+    __shared__ int32_t slot_lds[CERT ? 1 : BANDFAST];
+    __shared__ int32_t out_lds[CERT ? 1 : ONE_OUT];
     const int bq = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = (int)a.n;
     const int64_t base = (int64_t)bq * a.n;
+    const double sumwq = CERT ? a.sumwq[bq] : 0.0;  // in flight with the scores
 
-    for (int i = tid; i < NB; i += SMALL_NT) hist[i] = 0;
-    // range (and key norm) from the tile statistics, when given
+    // scores (all loads in flight, slots past n read the last slot and are
+    // dropped), candidate filter, tile statistics
+    float v[ONE_SPT];
+    const float *sp = a.scores + base;
+#pragma unroll
+    for (int i = 0; i < ONE_SPT; i++) {
+        const uint32_t sl = (uint32_t)(tid + ONE_NT * i);
+        v[i] = sp[sl < (uint32_t)n ? sl : (uint32_t)(n - 1)];
+    }
+    if (a.cand) {
+        const int32_t *cp = a.cand + base;
+        int32_t cv[ONE_SPT];
+#pragma unroll
+        for (int i = 0; i < ONE_SPT; i++) {
+            const uint32_t sl = (uint32_t)(tid + ONE_NT * i);
+            cv[i] = cp[sl < (uint32_t)n ? sl : (uint32_t)(n - 1)];
+        }
+#pragma unroll
+        for (int i = 0; i < ONE_SPT; i++)
+            if (cv[i] < 0) v[i] = NEG_INF;
+    }
+#pragma unroll
+    for (int i = 0; i < ONE_SPT; i++)
+        if (tid + ONE_NT * i >= n) v[i] = NEG_INF;
+    for (int i = tid; i < NB; i += ONE_NT) hist[i] = 0;
     float lo = POS_INF, hi = NEG_INF, km = 0.f;
-    uint32_t nvalid = 0;
-    if (a.stats) {
-        uint32_t c = 0;
-        for (int t = tid; t < a.ntiles; t += SMALL_NT) {
+    uint32_t c = 0;
+    const bool have_range = a.stats != nullptr;
+    if (have_range) {
+        for (int t = tid; t < a.ntiles; t += ONE_NT) {
             const TileStat st = a.stats[(size_t)bq * a.ntiles + t];
             lo = fminf(lo, st.smin);
             hi = fmaxf(hi, st.smax);
             km = fmaxf(km, st.kmax2);
             c += st.nvalid;
         }
-        lo = wave_min(lo);
-        hi = wave_max(hi);
-        km = wave_max(km);
-        if (lane == 0) {
-            fred[0][wave] = lo;
-            fred[1][wave] = hi;
-            fred[2][wave] = km;
-        }
-        nvalid = block_sum_u32<SMALL_NT>(c, red);  // barriers inside
-        for (int i = 0; i < SMALL_NT / 64; i++) {
-            lo = fminf(lo, fred[0][i]);
-            hi = fmaxf(hi, fred[1][i]);
-            km = fmaxf(km, fred[2][i]);
-        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < ONE_SPT; i++)
+            if (v[i] != NEG_INF) {
+                lo = fminf(lo, v[i]);
+                hi = fmaxf(hi, v[i]);
+                c++;
+            }
     }
-    const bool have_range = a.stats != nullptr;
-    float inv = (have_range && nvalid > 0 && hi - lo > 0.f) ? (float)NB / (hi - lo) : 0.f;
-
-    // load (8 x 16-byte vectors per thread, all in flight), histogram if the range is known
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    km = wave_max(km);
+    c = wave_sum_u32(c);
+    if (lane == 0) rred[wave] = f32x4{lo, hi, km, __uint_as_float(c)};
+    __syncthreads();
+    uint32_t nvalid = 0;
     {
-        constexpr int VPT = SPT / 4;
-        f32x4 xv[VPT];
-        const f32x4 ninf = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-        const bool vec_ok = (a.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
+        f32x4 rv[ONE_NT / 64];
 #pragma unroll
-        for (int i = 0; i < VPT; i++) {
-            const int s0 = 4 * (tid + SMALL_NT * i);
-            if (vec_ok && s0 < n) {
-                xv[i] = *reinterpret_cast<const f32x4 *>(a.scores + base + s0);
-            } else {
-                xv[i] = ninf;
-                for (int j = 0; j < 4; j++)
-                    if (s0 + j < n) xv[i][j] = a.scores[base + s0 + j];
-            }
-        }
-        if (a.cand) {
-            const int32_t *cp = a.cand + base;
+        for (int i = 0; i < ONE_NT / 64; i++) rv[i] = rred[i];
 #pragma unroll
-            for (int i = 0; i < VPT; i++) {
-                const int s0 = 4 * (tid + SMALL_NT * i);
-                for (int j = 0; j < 4; j++)
-                    if (s0 + j < n && cp[s0 + j] < 0) xv[i][j] = NEG_INF;
-            }
-        }
-        float mn = POS_INF, mx = NEG_INF;
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int i = 0; i < VPT; i++) {
-            const int s0 = 4 * (tid + SMALL_NT * i);
-            *reinterpret_cast<f32x4 *>(sc + s0) = xv[i];
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float x = xv[i][j];
-                if (x != NEG_INF) {
-                    if (have_range) {
-                        atomicAdd(&hist[sel_bin(x, lo, inv)], 1u);
-                    } else {
-                        mn = fminf(mn, x);
-                        mx = fmaxf(mx, x);
-                        cnt++;
-                    }
-                }
-            }
-        }
-        if (!have_range) {
-            mn = wave_min(mn);
-            mx = wave_max(mx);
-            if (lane == 0) {
-                fred[0][wave] = mn;
-                fred[1][wave] = mx;
-            }
-            nvalid = block_sum_u32<SMALL_NT>(cnt, red);
-            for (int i = 0; i < SMALL_NT / 64; i++) {
-                lo = fminf(lo, fred[0][i]);
-                hi = fmaxf(hi, fred[1][i]);
-            }
-            inv = (nvalid > 0 && hi - lo > 0.f) ? (float)NB / (hi - lo) : 0.f;
-#pragma unroll 8
-            for (int i = 0; i < SPT; i++) {
-                const float x = sc[tid + SMALL_NT * i];
-                if (x != NEG_INF) atomicAdd(&hist[sel_bin(x, lo, inv)], 1u);
-            }
+        for (int i = 0; i < ONE_NT / 64; i++) {
+            lo = fminf(lo, rv[i][0]);
+            hi = fmaxf(hi, rv[i][1]);
+            km = fmaxf(km, rv[i][2]);
+            nvalid += __float_as_uint(rv[i][3]);
         }
     }
+    const float inv = (nvalid > 0 && hi - lo > 0.f) ? (float)NB / (hi - lo) : 0.f;
+
+    // histogram from registers
+#pragma unroll
+    for (int i = 0; i < ONE_SPT; i++)
+        if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
     __syncthreads();
     // suffix counts: cum[b] = number of scores in bins >= b
     {
-        constexpr int BPT = NB / SMALL_NT;
+        constexpr int BPT = NB / ONE_NT;
         uint32_t hb[BPT], local = 0;
 #pragma unroll
         for (int j = 0; j < BPT; j++) {
             hb[j] = hist[BPT * tid + j];
             local += hb[j];
         }
-        grp_sum[SMALL_NT - 1 - tid] = local;
+        grp_sum[ONE_NT - 1 - tid] = local;
         __syncthreads();
         uint32_t tot;
-        const uint32_t ex = block_excl_scan<SMALL_NT>(grp_sum[tid], red, tot);
+        const uint32_t ex = block_excl_scan<ONE_NT>(grp_sum[tid], red, tot);
         __syncthreads();
         grp_sum[tid] = ex;
         __syncthreads();
-        uint32_t run = grp_sum[SMALL_NT - 1 - tid];
+        uint32_t run = grp_sum[ONE_NT - 1 - tid];
 #pragma unroll
         for (int j = BPT - 1; j >= 0; j--) {
             run += hb[j];
@@ -644,11 +641,9 @@ __global__ __launch_bounds__(SMALL_NT) void k_sel_small(SmallArgs a) {
         }
         if (tid == 0) cum[NB] = 0;
     }
-    // error bound of the fp32 scores (certified mode)
     double E = 0.0;
     if constexpr (CERT)
-        E = score_bound(sqrt((double)km * (1.0 + ldexp(1.0, -10))), a.sumwq[bq] * (1.0 + ldexp(1.0, -30)), a.HI,
-                        a.dI);
+        E = score_bound(sqrt((double)km * (1.0 + ldexp(1.0, -10))), sumwq * (1.0 + ldexp(1.0, -30)), a.HI, a.dI);
     __syncthreads();
 
     const int64_t nwords = (a.n + 31) / 32;
@@ -657,10 +652,11 @@ __global__ __launch_bounds__(SMALL_NT) void k_sel_small(SmallArgs a) {
         if (tid == 0) {
             bstar_sh = -1;
             band_cnt_sh = 0;
+            in_cnt_sh = 0;
         }
         __syncthreads();
         if (nvalid > (uint32_t)K)
-            for (int b2 = (NB / SMALL_NT) * tid; b2 < (NB / SMALL_NT) * (tid + 1); b2++)
+            for (int b2 = (NB / ONE_NT) * tid; b2 < (NB / ONE_NT) * (tid + 1); b2++)
                 if (cum[b2] >= (uint32_t)K && cum[b2 + 1] < (uint32_t)K) bstar_sh = b2;
         __syncthreads();
         const int bstar = bstar_sh;
@@ -669,8 +665,8 @@ __global__ __launch_bounds__(SMALL_NT) void k_sel_small(SmallArgs a) {
             // [a, z] = float values >= lo whose bin is b* (bin() is monotone)
             if (wave == 0) {
                 const uint32_t lk = fkey(lo), hk = 0xff7fffffu;
-                const uint32_t ka = wave_search_bin(lk, hk, bstar, lo, inv);
-                const uint32_t kz = bstar + 1 < NB ? wave_search_bin(lk, hk, bstar + 1, lo, inv) - 1 : hk;
+                const uint32_t ka = edge_key(lk, hk, bstar, lo, inv);
+                const uint32_t kz = bstar + 1 < NB ? edge_key(lk, hk, bstar + 1, lo, inv) - 1 : hk;
                 if (lane == 0) {
                     edge_sh[0] = ka;
                     edge_sh[1] = kz;
@@ -684,15 +680,20 @@ __global__ __launch_bounds__(SMALL_NT) void k_sel_small(SmallArgs a) {
         const float f_hi = f32_down(thi), f_lo = f32_up(tlo);
         uint32_t nin = 0;
         int32_t *band = a.band + ((size_t)tg * gridDim.x + bq) * a.band_cap;
-#pragma unroll 4
-        for (int i = 0; i < SPT; i++) {
-            const float x = sc[tid + SMALL_NT * i];
+        // a fresh copy of the thread index: slot numbers are recomputed here
+        // rather than kept live (and spilled) from the loads
+        int tidc = tid;
+        asm volatile("" : "+v"(tidc));
+        const int wword = __builtin_amdgcn_readfirstlane(2 * wave);  // this wave's first bitmap word
+#pragma unroll
+        for (int i = 0; i < ONE_SPT; i++) {
+            const float x = v[i];
             const bool valid = x != NEG_INF;
             const bool in = valid && x > f_hi;
             const bool bnd = valid && !in && x >= f_lo;
             const uint64_t bal = __ballot(in);
             const uint64_t bb = __ballot(bnd);
-            const int word0 = (wave * 64 + SMALL_NT * i) >> 5;
+            const int word0 = (ONE_NT / 32) * i + wword;
             if (lane == 0) {
                 bm[word0] = (uint32_t)bal;
                 bm[word0 + 1] = (uint32_t)(bal >> 32);
@@ -705,15 +706,17 @@ __global__ __launch_bounds__(SMALL_NT) void k_sel_small(SmallArgs a) {
                 if (bnd) {
                     const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32),
                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u));
-                    band[basepos + (int32_t)below] = tid + SMALL_NT * i;
+                    band[basepos + (int32_t)below] = tidc + ONE_NT * i;
                 }
             }
         }
-        const int32_t in_cnt = (int32_t)block_sum_u32<SMALL_NT>(nin, red);  // barriers inside
+        if (lane == 0 && nin) atomicAdd(&in_cnt_sh, (int32_t)nin);
+        __syncthreads();
+        const int32_t in_cnt = in_cnt_sh;
         const int32_t nb = band_cnt_sh;
         if constexpr (CERT) {
             uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
-            for (int64_t wd = tid; wd < nwords; wd += SMALL_NT) gbm[wd] = bm[wd];
+            for (int64_t wd = tid; wd < nwords; wd += ONE_NT) gbm[wd] = bm[wd];
             if (tid == 0) {
                 SelTarget t;
                 t.lo = tlo;
@@ -728,29 +731,25 @@ __global__ __launch_bounds__(SMALL_NT) void k_sel_small(SmallArgs a) {
         } else {
             __threadfence_block();
             __syncthreads();
-            uint64_t *key_lds = reinterpret_cast<uint64_t *>(sc);
-            int32_t *slot_lds = reinterpret_cast<int32_t *>(key_lds + BANDFAST);
-            int32_t *out_lds = slot_lds + BANDFAST;
-            const int32_t *list = band;
             int32_t *dst = (tg == 0 ? a.out0 : a.out1) + (size_t)bq * K;
-            finish_target<SMALL_NT>(bm, nwords, a.n, K, in_cnt, nb, list, nullptr, a.scores + base,
-                                    a.cand ? a.cand + base : nullptr, dst, tg == 0 && a.count0 ? a.count0 + bq : nullptr,
-                                    key_lds, slot_lds, out_lds, (int)(SMALL_N - 3 * BANDFAST), red);
+            finish_target<ONE_NT>(bm, nwords, a.n, K, in_cnt, nb, band, nullptr, a.scores + base,
+                                  a.cand ? a.cand + base : nullptr, dst, tg == 0 && a.count0 ? a.count0 + bq : nullptr,
+                                  key_lds, slot_lds, out_lds, ONE_OUT, red);
         }
         __syncthreads();
     }
 }
 
 // ----------------------------------------------------------------- rescore
-// One wave per BAND entry (both targets' lists back to back).  The block
-// stages its query's indexer heads in LDS as fp32 rows; lane h computes head
-// h's dot product with the staged key row in the definition's order d = 0, 1,
-// ... (products of bf16/fp32 inputs are exact in binary64, so fma = rounded
-// product + add); t_h = w_h * ReLU(d_h) is rounded on its own and the head
-// sum runs h = 0, 1, ... from +0.0 through lane broadcasts.  Idle blocks exit
-// at once.
+// One wave per BAND entry (both targets' lists back to back), no staging:
+// lane h loads query head h's row and the key row (the same address in every
+// lane) with 16-byte loads into registers, and computes head h's dot product
+// in the definition's order d = 0, 1, ... (products of bf16/fp32 inputs are
+// exact in binary64, so fma = rounded product + add); t_h = w_h * ReLU(d_h)
+// is rounded on its own, and lane 0 sums t_0, t_1, ... from +0.0 out of LDS.
+// Idle blocks exit at once.
 constexpr int RS_NT = 256;
-constexpr int RS_DMAX = 1024;  // longest key row
+constexpr int RS_VB = 16;      // 16-byte vectors per row batch
 
 struct RescoreKArgs {
     const void *qI;
@@ -768,120 +767,304 @@ struct RescoreKArgs {
     int64_t band_cap;
 };
 
-__device__ __forceinline__ double readlane_f64(double x, int l) {
-    const uint64_t u = __double_as_longlong(x);
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
-    return __longlong_as_double(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ float ld_elem(const void *p, int dt, size_t i) {
-    return dt == CSA2_F32 ? static_cast<const float *>(p)[i] : bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
-}
-
-// rows x cols elements (fp32 or bf16, from element `off`) -> fp32 LDS rows of
-// `stride` floats; 16-byte loads, four in flight per thread.
-template <int NT>
-__device__ void stage_rows(float *dst, int stride, const void *src, int dt, size_t off, int rows, int cols) {
-    const int total = rows * cols;
-    const int esz = dt == CSA2_F32 ? 4 : 2;
-    const int per = 16 / esz;  // elements per 16-byte vector
-    const char *p = static_cast<const char *>(src) + off * esz;
-    const bool vec = ((reinterpret_cast<uintptr_t>(p) & 15) == 0) && (cols % per == 0);
-    if (!vec) {
-        for (int i = threadIdx.x; i < total; i += NT) {
-            const int r = i / cols;
-            dst[r * stride + (i - r * cols)] = dt == CSA2_F32 ? reinterpret_cast<const float *>(p)[i]
-                                                              : bf16_to_f32(reinterpret_cast<const uint16_t *>(p)[i]);
-        }
-        return;
-    }
-    const int nvec = total / per, vpr = cols / per;  // vectors per row
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += 4 * NT) {
-        u32x4 buf[4];
+// Running binary64 dot over one 16-byte vector of each row.
+template <bool F32>
+__device__ __forceinline__ double dot_vec(double acc, u32x4 q, u32x4 k) {
+#pragma clang fp contract(off)
+    if constexpr (F32) {
 #pragma unroll
-        for (int u = 0; u < 4; u++)
-            if (v0 + u * NT < nvec) buf[u] = reinterpret_cast<const u32x4 *>(p)[v0 + u * NT];
+        for (int e = 0; e < 4; e++) acc = __builtin_fma((double)__uint_as_float(q[e]), (double)__uint_as_float(k[e]), acc);
+    } else {
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int vi = v0 + u * NT;
-            if (vi >= nvec) continue;
-            const int r = vi / vpr;
-            float *d = dst + r * stride + (vi - r * vpr) * per;
-            if (dt == CSA2_F32) {
-#pragma unroll
-                for (int x = 0; x < 4; x++) d[x] = __uint_as_float(buf[u][x]);
-            } else {
-#pragma unroll
-                for (int x = 0; x < 8; x++) d[x] = bf16_to_f32((uint16_t)(buf[u][x >> 1] >> (16 * (x & 1))));
-            }
+        for (int e = 0; e < 4; e++) {
+            acc = __builtin_fma((double)__uint_as_float(q[e] << 16), (double)__uint_as_float(k[e] << 16), acc);
+            acc = __builtin_fma((double)__uint_as_float(q[e] & 0xffff0000u), (double)__uint_as_float(k[e] & 0xffff0000u),
+                                acc);
         }
     }
+    return acc;
 }
 
+// Rows of at most RS_ROWB bytes: a block takes RS_EPB consecutive band
+// entries of one query.  Their slots are read speculatively with the target
+// record, their key rows staged once in LDS (one 16-byte load per thread),
+// and each wave runs RS_EPW entries as independent binary64 chains: lane h
+// holds query head h's row in registers and reads the key rows from LDS (the
+// same address in every lane).  Lane e then sums entry e's head terms in
+// order.  Blocks loop over the list when it is longer than the grid.
+constexpr int RS_EPW = 4;                       // entries per wave
+constexpr int RS_EPB = RS_EPW * (RS_NT / 64);  // entries per block
+constexpr int RS_ROWB = 512;                    // longest key row staged (bytes)
+constexpr int RS_QCH = 16;                      // query-row vectors per chunk
+
+template <bool F32>
 __global__ __launch_bounds__(RS_NT) void k_sel_rescore(RescoreKArgs a) {
 #pragma clang fp contract(off)
-    extern __shared__ __attribute__((aligned(16))) float lds[];
+    __shared__ __attribute__((aligned(16))) u32x4 krow_lds[RS_EPB][RS_ROWB / 16];
+    __shared__ double tl[RS_NT / 64][RS_EPW][64];
+    constexpr int ESZ = F32 ? 4 : 2;
+    constexpr int NW = RS_NT / 64;
+    const int bq = blockIdx.y;
+    const int b = bq / a.Q;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nvec = a.dI * ESZ / 16;  // 16-byte vectors per row
+    const size_t row0 = (size_t)bq * a.band_cap, row1 = ((size_t)gridDim.y + bq) * a.band_cap;
+    // speculative: this block's first entries as target-0 slots
+    const int32_t eb0 = blockIdx.x * RS_EPB;
+    const int32_t my_e = eb0 + tid / nvec;  // entry whose row chunk this thread stages
+    const int32_t spec = (tid < RS_EPB * nvec && my_e < a.band_cap) ? a.band[row0 + my_e] : 0;
+    const SelQuery sqv = a.sq[bq];
+    const int32_t nb0 = sqv.t[0].band_cnt, nb1 = a.ntgt > 1 ? sqv.t[1].band_cnt : 0;
+    const int32_t total = nb0 + nb1;
+    if (eb0 >= total) return;
+    for (int32_t e0 = eb0; e0 < total; e0 += gridDim.x * RS_EPB) {
+        // stage the key rows of entries e0 .. e0 + RS_EPB - 1 (16-byte chunk q of the block's rows)
+        for (int q = tid; q < RS_EPB * nvec; q += RS_NT) {
+            const int i = q / nvec, c = q - i * nvec;
+            const int32_t e = e0 + i;
+            if (e < total) {
+                const int32_t slot = (e0 == eb0 && q == tid && e < nb0)
+                                         ? spec
+                                         : (e < nb0 ? a.band[row0 + e] : a.band[row1 + (e - nb0)]);
+                const int64_t j = a.cand ? (int64_t)a.cand[(int64_t)bq * a.n + slot] : (int64_t)slot;
+                krow_lds[i][c] = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.kI) +
+                                                                ((size_t)b * a.N + j) * a.dI * ESZ)[c];
+            }
+        }
+        __syncthreads();
+        const int ew = wave * RS_EPW;  // this wave's first entry in the block
+        double sc = 0.0;               // lane e < RS_EPW: running score of entry e0 + ew + e
+        for (int h0 = 0; h0 < a.HI; h0 += 64) {
+            const int h = h0 + lane;
+            const int hc = h < a.HI ? h : a.HI - 1;  // idle lanes recompute the last head, unused
+            const u32x4 *qrow = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.qI) +
+                                                                ((size_t)bq * a.HI + hc) * a.dI * ESZ);
+            const double wh = (double)a.w[(size_t)bq * a.HI + hc];
+            double dot[RS_EPW];
+#pragma unroll
+            for (int e = 0; e < RS_EPW; e++) dot[e] = 0.0;
+            for (int v0 = 0; v0 < nvec; v0 += RS_QCH) {
+                u32x4 qv[RS_QCH];
+#pragma unroll
+                for (int u = 0; u < RS_QCH; u++)
+                    if (v0 + u < nvec) qv[u] = qrow[v0 + u];
+#pragma unroll
+                for (int u = 0; u < RS_QCH; u++) {
+                    if (v0 + u >= nvec) break;
+                    u32x4 kv[RS_EPW];
+#pragma unroll
+                    for (int e = 0; e < RS_EPW; e++) kv[e] = krow_lds[ew + e][v0 + u];
+#pragma unroll
+                    for (int x = 0; x < (F32 ? 4 : 8); x++) {
+                        const uint32_t qw = qv[u][F32 ? x : x >> 1];
+                        const double qd = (double)__uint_as_float(F32 ? qw : ((x & 1) ? (qw & 0xffff0000u) : (qw << 16)));
+#pragma unroll
+                        for (int e = 0; e < RS_EPW; e++) {
+                            const uint32_t kw = kv[e][F32 ? x : x >> 1];
+                            const double kd =
+                                (double)__uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
+                            dot[e] = __builtin_fma(qd, kd, dot[e]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < RS_EPW; e++) tl[wave][e][lane] = wh * (dot[e] > 0.0 ? dot[e] : 0.0);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < RS_EPW) {
+                // head terms t_h0, t_h0+1, ... added in order (read 16 at a time)
+                const int hn = a.HI - h0 < 64 ? a.HI - h0 : 64;
+                for (int c0 = 0; c0 < hn; c0 += 16) {
+                    double tv[16];
+#pragma unroll
+                    for (int i = 0; i < 16; i++) tv[i] = tl[wave][lane][c0 + i];
+#pragma unroll
+                    for (int i = 0; i < 16; i++)
+                        if (c0 + i < hn) sc = sc + tv[i];
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        const int32_t e = e0 + ew + lane;
+        if (lane < RS_EPW && e < total) {
+            if (e < nb0) a.band_score[row0 + e] = sc;
+            else a.band_score[row1 + (e - nb0)] = sc;
+        }
+        __syncthreads();  // the staged rows are replaced next round
+    }
+}
+
+// Rows longer than RS_ROWB: one wave per band entry.  The entry's slot is read
+// speculatively with the target record, and the wave's query rows and head
+// weights before the first entry.
+template <bool F32>
+__global__ __launch_bounds__(RS_NT) void k_sel_rescore_wide(RescoreKArgs a) {
+#pragma clang fp contract(off)
+    __shared__ double tl[RS_NT / 64][64];
+    constexpr int ESZ = F32 ? 4 : 2;
     const int bq = blockIdx.y;
     const int b = bq / a.Q;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int NW = RS_NT / 64;
+    const int nvec = a.dI * ESZ / 16;  // 16-byte vectors per row (a whole number, checked on the host)
+    const int32_t e0 = blockIdx.x * NW + wave;
+    // speculative: the first entry's slot in each target list
+    const size_t row0 = (size_t)bq * a.band_cap, row1 = ((size_t)gridDim.y + bq) * a.band_cap;
+    const int32_t spec0 = e0 < a.band_cap ? a.band[row0 + e0] : 0;
     const SelQuery sqv = a.sq[bq];
     const int32_t nb0 = sqv.t[0].band_cnt, nb1 = a.ntgt > 1 ? sqv.t[1].band_cnt : 0;
     const int32_t total = nb0 + nb1;
-    if ((int32_t)blockIdx.x * NW >= total) return;
-    const int qstride = a.dI + 1;  // padded rows: lane h reads bank (h + d) % 64
-    float *qs = lds;
-    float *ks = lds + ((a.HI * qstride + 3) & ~3) + wave * a.dI;
-    stage_rows<RS_NT>(qs, qstride, a.qI, a.dt, (size_t)bq * a.HI * a.dI, a.HI, a.dI);
-    __syncthreads();
-    for (int32_t e = blockIdx.x * NW + wave; e < total; e += gridDim.x * NW) {
-        const int tg = e < nb0 ? 0 : 1;
-        const int32_t pos = tg == 0 ? e : e - nb0;
-        const int32_t slot = a.band[((size_t)tg * gridDim.y + bq) * a.band_cap + pos];
-        const int64_t j = a.cand ? (int64_t)a.cand[(int64_t)bq * a.n + slot] : (int64_t)slot;
-        {
-            float kv[RS_DMAX / 64];
-            const size_t kb = ((size_t)b * a.N + j) * a.dI;
+    if (e0 >= total) return;
+    for (int h0 = 0; h0 < a.HI; h0 += 64) {
+        const int h = h0 + lane;
+        const int hc = h < a.HI ? h : a.HI - 1;  // idle lanes recompute the last head, unused
+        const u32x4 *qrow = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.qI) +
+                                                            ((size_t)bq * a.HI + hc) * a.dI * ESZ);
+        const double wh = (double)a.w[(size_t)bq * a.HI + hc];
+        u32x4 qv[RS_VB];
+        const bool qcached = nvec <= RS_VB;  // the query row stays in registers across entries
+        if (qcached) {
 #pragma unroll
-            for (int u = 0; u < RS_DMAX / 64; u++)
-                if (lane + 64 * u < a.dI) kv[u] = ld_elem(a.kI, a.dt, kb + lane + 64 * u);
-#pragma unroll
-            for (int u = 0; u < RS_DMAX / 64; u++)
-                if (lane + 64 * u < a.dI) ks[lane + 64 * u] = kv[u];
+            for (int u = 0; u < RS_VB; u++)
+                if (u < nvec) qv[u] = qrow[u];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        double s = 0.0;
-        for (int h0 = 0; h0 < a.HI; h0 += 64) {
-            const int h = h0 + lane;
-            double t = 0.0;
-            if (h < a.HI) {
-                const float *qh = qs + h * qstride;
-                double dot = 0.0;
-                int d0 = 0;
-                for (; d0 + 8 <= a.dI; d0 += 8) {
-                    float qv[8], kk[8];
+        for (int32_t e = e0; e < total; e += gridDim.x * NW) {
+            const int tg = e < nb0 ? 0 : 1;
+            const int32_t pos = tg == 0 ? e : e - nb0;
+            const int32_t slot = (e == e0 && tg == 0) ? spec0 : a.band[(tg == 0 ? row0 : row1) + pos];
+            const int64_t j = a.cand ? (int64_t)a.cand[(int64_t)bq * a.n + slot] : (int64_t)slot;
+            const u32x4 *krow = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.kI) +
+                                                                ((size_t)b * a.N + j) * a.dI * ESZ);
+            double dot = 0.0;
+            for (int v0 = 0; v0 < nvec; v0 += RS_VB) {
+                u32x4 kv[RS_VB];
 #pragma unroll
-                    for (int u = 0; u < 8; u++) {
-                        qv[u] = qh[d0 + u];
-                        kk[u] = ks[d0 + u];
+                for (int u = 0; u < RS_VB; u++)
+                    if (v0 + u < nvec) {
+                        if (!qcached) qv[u] = qrow[v0 + u];
+                        kv[u] = krow[v0 + u];
                     }
 #pragma unroll
-                    for (int u = 0; u < 8; u++) dot = __builtin_fma((double)qv[u], (double)kk[u], dot);
-                }
-                for (; d0 < a.dI; d0++) dot = __builtin_fma((double)qh[d0], (double)ks[d0], dot);
-                const double rl = dot > 0.0 ? dot : 0.0;
-                t = (double)a.w[(size_t)bq * a.HI + h] * rl;
+                for (int u = 0; u < RS_VB; u++)
+                    if (v0 + u < nvec) dot = dot_vec<F32>(dot, qv[u], kv[u]);
             }
-            const int hn = a.HI - h0 < 64 ? a.HI - h0 : 64;
-            for (int i = 0; i < hn; i++) s = s + readlane_f64(t, i);
+            const double rl = dot > 0.0 ? dot : 0.0;
+            tl[wave][lane] = wh * rl;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane == 0) {
+                // head terms t_h0, t_h0+1, ... added in order (read 16 at a time)
+                const int hn = a.HI - h0 < 64 ? a.HI - h0 : 64;
+                double sc = h0 == 0 ? 0.0 : a.band_score[(tg == 0 ? row0 : row1) + pos];
+                for (int c0 = 0; c0 < hn; c0 += 16) {
+                    double tv[16];
+#pragma unroll
+                    for (int i = 0; i < 16; i++) tv[i] = tl[wave][c0 + i];
+#pragma unroll
+                    for (int i = 0; i < 16; i++)
+                        if (c0 + i < hn) sc = sc + tv[i];
+                }
+                a.band_score[(tg == 0 ? row0 : row1) + pos] = sc;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        if (lane == 0) a.band_score[((size_t)tg * gridDim.y + bq) * a.band_cap + pos] = s;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// ------------------------------------------------------- one-block finish
+// Certified finish of the one-block path: the IN bitmap (one word per
+// thread), the target record and the first ONE_NT band entries with their
+// binary64 scores arrive in one round of loads.  Each band entry is ranked by
+// counting the entries ahead of it in (score descending, slot ascending)
+// order; the best K - |IN| join the bitmap, which is compacted in slot order
+// through LDS.  Larger bands or outputs take the general path.
+struct BandEnt {
+    uint64_t key;
+    int32_t slot, pad;
+};
+
+__global__ __launch_bounds__(ONE_NT) void k_sel_finish_one(const float *__restrict__ scores,
+                                                           const int32_t *__restrict__ cand, int64_t n, int ntgt,
+                                                           const SelQuery *__restrict__ sq, const uint32_t *bitmap,
+                                                           int64_t nwords, const int32_t *band, const double *band_score,
+                                                           int64_t band_cap, int32_t *out0, int32_t *count0,
+                                                           int32_t *out1) {
+    __shared__ uint32_t bm[ONE_N / 32];
+    __shared__ __attribute__((aligned(16))) BandEnt ent[ONE_NT];
+    __shared__ int32_t out_lds[ONE_OUT];
+    __shared__ uint32_t red[ONE_NT / 64];
+    const int bq = blockIdx.x, tid = threadIdx.x;
+    for (int tg = 0; tg < ntgt; tg++) {
+        const size_t row = (size_t)tg * gridDim.x + bq;
+        const SelTarget t = sq[bq].t[tg];
+        const uint32_t wv = tid < nwords ? bitmap[row * nwords + tid] : 0u;
+        const int32_t bsl = tid < band_cap ? band[row * band_cap + tid] : 0;
+        const double bsc = tid < band_cap ? band_score[row * band_cap + tid] : 0.0;
+        int32_t *dst = (tg == 0 ? out0 : out1) + (size_t)bq * t.K;
+        int32_t *cdst = tg == 0 && count0 ? count0 + bq : nullptr;
+        const int32_t nb = t.band_cnt, r = t.K - t.in_cnt;
+        bm[tid] = wv;
+        if (nb > ONE_NT || t.K > ONE_OUT) {  // general path
+            __syncthreads();
+            finish_target<ONE_NT>(bm, nwords, n, t.K, t.in_cnt, nb, band + row * band_cap,
+                                  band_score + row * band_cap, scores + (int64_t)bq * n,
+                                  cand ? cand + (int64_t)bq * n : nullptr, dst, cdst,
+                                  reinterpret_cast<uint64_t *>(out_lds), reinterpret_cast<int32_t *>(ent), out_lds,
+                                  0, red);
+            __syncthreads();
+            continue;
+        }
+        if (tid < nb) {
+            BandEnt be;
+            be.key = dkey(bsc);
+            be.slot = bsl;
+            be.pad = 0;
+            ent[tid] = be;
+        }
+        __syncthreads();
+        if (r > 0 && tid < nb) {
+            const uint64_t ki = ent[tid].key;
+            const int32_t si = ent[tid].slot;
+            int32_t rank = 0;
+            int32_t j0 = 0;
+            for (; j0 + 16 <= nb; j0 += 16) {
+                BandEnt bj[16];
+#pragma unroll
+                for (int u = 0; u < 16; u++) bj[u] = ent[j0 + u];
+#pragma unroll
+                for (int u = 0; u < 16; u++)
+                    rank += (int)((bj[u].key > ki) | ((bj[u].key == ki) & (bj[u].slot < si)));
+            }
+            for (; j0 < nb; j0++) {
+                const BandEnt bj = ent[j0];
+                rank += (int)((bj.key > ki) | ((bj.key == ki) & (bj.slot < si)));
+            }
+            if (rank < r) atomicOr(&bm[si >> 5], 1u << (si & 31));
+        }
+        __syncthreads();
+        // compaction: thread tid owns bitmap word tid
+        uint32_t bits = bm[tid];
+        uint32_t tot;
+        uint32_t pos = block_excl_scan<ONE_NT>((uint32_t)__builtin_popcount(bits), red, tot);
+        while (bits) {
+            const int i = __builtin_ctz(bits);
+            bits &= bits - 1;
+            if (pos < (uint32_t)t.K) out_lds[pos] = tid * 32 + i;
+            pos++;
+        }
+        const int32_t kept = (int32_t)(tot < (uint32_t)t.K ? tot : (uint32_t)t.K);
+        __syncthreads();
+        const int32_t *cq = cand ? cand + (int64_t)bq * n : nullptr;
+        for (int32_t i = tid; i < t.K; i += ONE_NT) dst[i] = i < kept ? (cq ? cq[out_lds[i]] : out_lds[i]) : -1;
+        if (cdst && tid == 0) *cdst = kept;
+        __syncthreads();
     }
 }
 
@@ -951,10 +1134,7 @@ __global__ __launch_bounds__(FIN_NT) void k_sel_finish(FinishArgs a) {
 
 // ------------------------------------------------------------------ host
 
-size_t rescore_lds_bytes(int HI, int dI) {
-    if (dI > RS_DMAX) return SIZE_MAX;
-    return sizeof(float) * ((((size_t)HI * (dI + 1)) + 3) / 4 * 4 + (size_t)(RS_NT / 64) * dI);
-}
+bool rescore_supported(int dt, int dI) { return dI >= 1 && (dI * (dt == CSA2_F32 ? 4 : 2)) % 16 == 0; }
 
 SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified) {
     SelPlan p;
@@ -971,7 +1151,7 @@ SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified) {
     return p;
 }
 
-static bool small_path(const SelPlan &p) { return p.n <= SMALL_N; }
+static bool small_path(const SelPlan &p) { return p.n <= ONE_N; }
 
 size_t sel_workspace(const SelPlan &p, bool own_stats) {
     Carve c(nullptr, 0);
@@ -1001,7 +1181,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     if (p.certified && (!rs || !rs->sumwq)) throw Error(CSA2_EINTERNAL, "certified selection needs query norms");
 
     if (small_path(p)) {
-        SmallArgs a{};
+        OneArgs a{};
         a.scores = scores;
         a.cand = cand;
         a.n = p.n;
@@ -1023,9 +1203,9 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         a.nwords = p.nwords;
         a.band = band;
         a.band_cap = p.band_cap;
-        if (p.certified) hipLaunchKernelGGL(k_sel_small<true>, dim3(p.BQ), dim3(SMALL_NT), 0, s, a);
-        else hipLaunchKernelGGL(k_sel_small<false>, dim3(p.BQ), dim3(SMALL_NT), 0, s, a);
-        check_launch("selection (fused)");
+        if (p.certified) hipLaunchKernelGGL(k_sel_one<true>, dim3(p.BQ), dim3(ONE_NT), 0, s, a);
+        else hipLaunchKernelGGL(k_sel_one<false>, dim3(p.BQ), dim3(ONE_NT), 0, s, a);
+        check_launch("selection (one block per query)");
         if (!p.certified) return;
     } else {
         if (!stats_in) {
@@ -1063,10 +1243,26 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         r.band = band;
         r.band_score = band_score;
         r.band_cap = p.band_cap;
-        int nblk = 4096 / p.BQ / (RS_NT / 64);
-        nblk = nblk < 2 ? 2 : (nblk > 64 ? 64 : nblk);
-        hipLaunchKernelGGL(k_sel_rescore, dim3(nblk, p.BQ), dim3(RS_NT), rescore_lds_bytes(rs->HI, rs->dI), s, r);
+        const int rowb = rs->dI * (rs->dt == CSA2_F32 ? 4 : 2);
+        if (rowb <= RS_ROWB) {
+            // about 256 entries per query per round; the grid stays small enough to be resident at once
+            int nblk = 256 / RS_EPB;
+            if ((int64_t)nblk * p.BQ > 2048) nblk = (int)(2048 / p.BQ) > 1 ? (int)(2048 / p.BQ) : 1;
+            if (rs->dt == CSA2_F32) hipLaunchKernelGGL(k_sel_rescore<true>, dim3(nblk, p.BQ), dim3(RS_NT), 0, s, r);
+            else hipLaunchKernelGGL(k_sel_rescore<false>, dim3(nblk, p.BQ), dim3(RS_NT), 0, s, r);
+        } else {
+            int nblk = 4096 / p.BQ / (RS_NT / 64);
+            nblk = nblk < 2 ? 2 : (nblk > 64 ? 64 : nblk);
+            if (rs->dt == CSA2_F32) hipLaunchKernelGGL(k_sel_rescore_wide<true>, dim3(nblk, p.BQ), dim3(RS_NT), 0, s, r);
+            else hipLaunchKernelGGL(k_sel_rescore_wide<false>, dim3(nblk, p.BQ), dim3(RS_NT), 0, s, r);
+        }
         check_launch("selection rescore");
+    }
+    if (small_path(p)) {
+        hipLaunchKernelGGL(k_sel_finish_one, dim3(p.BQ), dim3(ONE_NT), 0, s, scores, cand, p.n, p.ntgt, sq, bitmap,
+                           p.nwords, band, band_score, p.band_cap, out0, count0, out1);
+        check_launch("selection finish");
+        return;
     }
     FinishArgs f{};
     f.scores = scores;

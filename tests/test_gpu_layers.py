@@ -61,3 +61,15 @@ def test_rerun_is_bitwise_deterministic(b):
     torch.cuda.synchronize()
     for key in ("idx", "out", "lse"):
         assert torch.equal(g1[key], g2[key]), key
+
+
+@pytest.mark.parametrize("HI,dI,idx_dtype", [
+    (8, 256, "f32"),     # 1 KiB indexer rows: the one-wave-per-entry rescoring kernel
+    (16, 40, "bf16"),    # 5 vectors per row
+    (100, 24, "f32"),    # more heads than lanes: head sums carried across two passes
+    (128, 64, "bf16"),   # matrix-core indexer with two head passes
+])
+def test_certified_rescoring_row_shapes(b, HI, dI, idx_dtype):
+    spec = synth.Decode(B=1, Q=2, N=3000, HI=HI, dI=dI, H=16, D=128, k=256, idx_dtype=idx_dtype, seed=HI + dI,
+                        layers=["FULL"])
+    run_group(b, synth.make_decode(spec))
