@@ -21,8 +21,12 @@
 
 namespace csa2 {
 
-constexpr int ATT_SPLIT = 128;  // selected entries per block (fixed)
-constexpr int ATT_SUB = 32;     // entries per wave iteration
+constexpr int ATT_SUB = 32;  // entries per tile
+
+// Selected entries per split: fixed, so that a query's result does not depend
+// on the batch it is computed in.  (Longer splits halve the combine traffic but
+// leave each block a longer chain of gathers; measured slower at k = 2048.)
+constexpr int ATT_SPLIT = 128;
 
 namespace {
 
@@ -76,8 +80,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ------------------------------------------------------------ MFMA kernel
-// Block = one query x one split of ATT_SPLIT selected entries; wave w serves
-// heads 16 (w % HGS) .. +15 and, with DS = 2, half of the output channels (the
+// Block = one query x one split of the selected entries x HB groups of 16
+// heads; wave w serves heads 16 (HB g + w % HB) .. +15 and, with DS = 2, half of the output channels (the
 // two waves of a head group both compute that group's logits).  Per 32-entry tile: all threads gather the rows into an
 // LDS buffer (bf16 rows as is, FP4 rows decoded to fp16), the next tile's rows
 // are already in flight in registers; each wave computes S^T = C Q^T (rows as
@@ -176,34 +180,43 @@ __device__ __forceinline__ void gather_store(uint16_t *T, const u32x4 *buf, cons
     }
 }
 
-template <int D, int FMT, int HGS, int DS>
-__global__ __launch_bounds__(64 * HGS * DS, 1) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
+// Block order: the NG blocks that share one (query, split) -- one per group
+// of HB x 16 heads -- get linear ids congruent mod 8, so that the round-robin
+// dispatch puts them on one XCD and they gather the split's rows through one
+// L2.  Ids past the last (query, split) pair exit at once.
+template <int D, int FMT, int HB, int DS, int SPLIT>
+__global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                           int Q, int H, int64_t N, const int32_t *__restrict__ idx,
-                                                          int k, float scale, int nsplit, uint16_t *__restrict__ out,
-                                                          float *__restrict__ lse, float *__restrict__ part_o,
-                                                          float2 *__restrict__ part_ml) {
-    constexpr int NT = 64 * HGS * DS;
+                                                          int k, float scale, int nsplit, int npairs,
+                                                          uint16_t *__restrict__ out, float *__restrict__ lse,
+                                                          float *__restrict__ part_o, float2 *__restrict__ part_ml) {
+    constexpr int NT = 64 * HB * DS;
     constexpr int KS = D / 32;       // contraction steps of S
     constexpr int DT = D / 16 / DS;  // 16-wide d tiles of O owned by this wave
     constexpr int LS = D + 8;   // LDS row stride in 16-bit elements (16-byte pad)
     using G = TileGather<D, FMT>;
     constexpr int PER = (G::CHUNKS + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][ATT_SUB * LS];
-    __shared__ int32_t jsh[ATT_SPLIT];
+    __shared__ int32_t jsh[SPLIT];
 
-    const int split = blockIdx.x % nsplit;
-    const int bq = blockIdx.x / nsplit;
+    const int NG = H / (16 * HB);
+    const int L = blockIdx.x;
+    const int pair = (L / (8 * NG)) * 8 + (L % 8);
+    const int hgb = (L % (8 * NG)) / 8;
+    if (pair >= npairs) return;
+    const int split = pair % nsplit;
+    const int bq = pair / nsplit;
     const int b = bq / Q;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 15, kg = lane >> 4;
-    const int hg = wave % HGS;  // this wave's 16 heads
-    const int dt0 = (wave / HGS) * DT;  // first d tile of this wave (S is computed by every d part)
+    const int hg = hgb * HB + wave % HB;  // this wave's 16 heads
+    const int dt0 = (wave / HB) * DT;     // first d tile of this wave (S is computed by every d part)
 
-    const int e_begin = split * ATT_SPLIT;
-    const int e_end = min(k, e_begin + ATT_SPLIT);
+    const int e_begin = split * SPLIT;
+    const int e_end = min(k, e_begin + SPLIT);
     const int ne = e_end - e_begin;
     const int32_t *irow = idx + (size_t)bq * k + e_begin;
-    for (int e = threadIdx.x; e < ATT_SPLIT; e += NT) {
+    for (int e = threadIdx.x; e < SPLIT; e += NT) {
         int j = e < ne ? irow[e] : -1;
         jsh[e] = (j >= 0 && j < N) ? j : -1;  // out-of-range entries are skipped like -1
     }
@@ -249,8 +262,8 @@ __global__ __launch_bounds__(64 * HGS * DS, 1) void k_attn_mfma(const uint16_t *
     }
     __syncthreads();
     for (int t = 0; t < ntiles; t++) {
-        const uint16_t *T = tile[t & 1];
         if (t + 1 < ntiles) gather_issue<D, FMT, NT>(kvb, jsh + (t + 1) * ATT_SUB, buf, sbuf);
+        const uint16_t *T = tile[t & 1];
         const int32_t *jt = jsh + t * ATT_SUB;
         // ---- S^T[e][h] for the two 16-entry halves
         f32x4 st[2];
@@ -459,29 +472,42 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
     if (lse && threadIdx.x == 0) lse[(size_t)bq * H + h] = Z > 0.f ? M + logf(Z) : NEG_INF;
 }
 
-template <int D, int FMT, int HGS>
-void launch_mfma_nw(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
+// Heads per block: enough blocks to fill the chip (about 256) with as many
+// heads per block as that allows, so that fewer blocks gather the same rows.
+template <int D, int FMT, int HB, int SPLIT>
+void launch_mfma_hb(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
                     float *lse, float *part_o, float2 *part_ml, hipStream_t s) {
-    const int blocks = p.B * p.Q * p.nsplit;
-    // two waves per head group (each owns half of the channels) while that
-    // stays within 512 threads
-    constexpr int DS = (HGS <= 4 && D >= 128) ? 2 : 1;
-    hipLaunchKernelGGL((k_attn_mfma<D, FMT, HGS, DS>), dim3(blocks), dim3(64 * HGS * DS), 0, s,
-                       static_cast<const uint16_t *>(q),
-                       static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k, scale, p.nsplit,
-                       static_cast<uint16_t *>(out), lse, part_o, part_ml);
+    // two or more waves per head group (each owns a share of the channels)
+    // while that stays within 512 threads
+    constexpr int DS = HB == 1 ? (D >= 256 ? 4 : 2) : ((HB <= 4 && D >= 128) ? 2 : 1);
+    const int npairs = p.B * p.Q * p.nsplit;
+    const int NG = p.H / (16 * HB);
+    const int blocks = (npairs + 7) / 8 * 8 * NG;
+    hipLaunchKernelGGL((k_attn_mfma<D, FMT, HB, DS, SPLIT>), dim3(blocks), dim3(64 * HB * DS), 0, s,
+                       static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,
+                       scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml);
+}
+
+template <int D, int FMT, int SPLIT>
+void launch_mfma_split(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
+                       float *lse, float *part_o, float2 *part_ml, hipStream_t s) {
+    const int64_t pairs = (int64_t)p.B * p.Q * p.nsplit;
+    const int hgroups = p.H / 16;
+    int hb = hgroups;  // head groups per block
+    while (hb > 1 && pairs * (hgroups / hb) < 256) hb /= 2;
+    switch (hb) {
+        case 1: launch_mfma_hb<D, FMT, 1, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        case 2: launch_mfma_hb<D, FMT, 2, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        case 4: launch_mfma_hb<D, FMT, 4, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        case 8: launch_mfma_hb<D, FMT, 8, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        default: throw Error(CSA2_EUNSUPPORTED, "matrix-core attention needs H in {16, 32, 64, 128}");
+    }
 }
 
 template <int D, int FMT>
 void launch_mfma(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
                  float *lse, float *part_o, float2 *part_ml, hipStream_t s) {
-    switch (p.H / 16) {
-        case 1: launch_mfma_nw<D, FMT, 1>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
-        case 2: launch_mfma_nw<D, FMT, 2>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
-        case 4: launch_mfma_nw<D, FMT, 4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
-        case 8: launch_mfma_nw<D, FMT, 8>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
-        default: throw Error(CSA2_EUNSUPPORTED, "matrix-core attention needs H in {16, 32, 64, 128}");
-    }
+    launch_mfma_split<D, FMT, ATT_SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s);
 }
 
 }  // namespace
