@@ -663,14 +663,12 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
         double tlo = -__builtin_inf(), thi = -__builtin_inf();
         if (bstar >= 0) {
             // [a, z] = float values >= lo whose bin is b* (bin() is monotone)
-            if (wave == 0) {
+            if (wave < 2) {  // wave 0: lower edge, wave 1: upper edge
                 const uint32_t lk = fkey(lo), hk = 0xff7fffffu;
-                const uint32_t ka = edge_key(lk, hk, bstar, lo, inv);
-                const uint32_t kz = bstar + 1 < NB ? edge_key(lk, hk, bstar + 1, lo, inv) - 1 : hk;
-                if (lane == 0) {
-                    edge_sh[0] = ka;
-                    edge_sh[1] = kz;
-                }
+                uint32_t kk = hk;
+                if (wave == 0) kk = edge_key(lk, hk, bstar, lo, inv);
+                else if (bstar + 1 < NB) kk = edge_key(lk, hk, bstar + 1, lo, inv) - 1;
+                if (lane == 0) edge_sh[wave] = kk;
             }
             __syncthreads();
             tlo = thr_lo(fkey_inv(edge_sh[0]), E);
@@ -803,7 +801,6 @@ __global__ __launch_bounds__(RS_NT) void k_sel_rescore(RescoreKArgs a) {
     __shared__ __attribute__((aligned(16))) u32x4 krow_lds[RS_EPB][RS_ROWB / 16];
     __shared__ double tl[RS_NT / 64][RS_EPW][64];
     constexpr int ESZ = F32 ? 4 : 2;
-    constexpr int NW = RS_NT / 64;
     const int bq = blockIdx.y;
     const int b = bq / a.Q;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1029,25 +1026,24 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_finish_one(const float *__restri
             ent[tid] = be;
         }
         __syncthreads();
-        if (r > 0 && tid < nb) {
-            const uint64_t ki = ent[tid].key;
-            const int32_t si = ent[tid].slot;
-            int32_t rank = 0;
-            int32_t j0 = 0;
-            for (; j0 + 16 <= nb; j0 += 16) {
-                BandEnt bj[16];
-#pragma unroll
-                for (int u = 0; u < 16; u++) bj[u] = ent[j0 + u];
-#pragma unroll
-                for (int u = 0; u < 16; u++)
-                    rank += (int)((bj[u].key > ki) | ((bj[u].key == ki) & (bj[u].slot < si)));
-            }
-            for (; j0 < nb; j0++) {
-                const BandEnt bj = ent[j0];
+        // entry i's rank is counted by P consecutive lanes over every P-th entry
+        // (all 16 waves busy, short dependent chains), then summed by a butterfly
+        const int P = nb <= 128 ? 8 : nb <= 256 ? 4 : nb <= 512 ? 2 : 1;
+        const int ei = tid / P, ep = tid - ei * P;
+        int32_t rank = 0;
+        const bool ranks = r > 0 && ei < nb;
+        uint64_t ki = 0;
+        int32_t si = 0;
+        if (ranks) {
+            ki = ent[ei].key;
+            si = ent[ei].slot;
+            for (int32_t j = ep; j < nb; j += P) {
+                const BandEnt bj = ent[j];
                 rank += (int)((bj.key > ki) | ((bj.key == ki) & (bj.slot < si)));
             }
-            if (rank < r) atomicOr(&bm[si >> 5], 1u << (si & 31));
         }
+        for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
+        if (ranks && ep == 0 && rank < r) atomicOr(&bm[si >> 5], 1u << (si & 31));
         __syncthreads();
         // compaction: thread tid owns bitmap word tid
         uint32_t bits = bm[tid];
