@@ -288,8 +288,7 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
                 a[h2 * 4 + i] = v;
                 mt = fmaxf(mt, v);
             }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = bfly32(bfly16(mt, OpMax{}), OpMax{});
         const float m_new = fmaxf(m_run, mt);
         const float alpha = m_run == NEG_INF ? 0.f : __expf(m_run - m_new);
         float psum = 0.f;
@@ -327,8 +326,7 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
     }
 
     // ---- write this wave's 16 heads: lane holds O^T[16 dt + 4 kg + r][col]
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = bfly32(bfly16(l_run, OpAdd{}), OpAdd{});
     const int h = hg * 16 + col;
     if (nsplit == 1) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;

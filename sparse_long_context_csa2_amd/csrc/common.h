@@ -72,22 +72,64 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return uint16_t(u >> 16);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+// ------------------------------------------------------- cross-lane steps
+// Butterfly steps on 32-bit lanes without the LDS crossbar: DPP for partners
+// inside a 16-lane row, the gfx950 permlane swaps across rows.  bfly_k(v, op)
+// returns op(v, v of lane l ^ k) in every lane (op commutative), except that
+// bfly4 / bfly8 pair lane l with l ^ 7 / l ^ 15 (row half-mirror / mirror):
+// the same as l ^ 4 / l ^ 8 once the smaller steps have made groups of 4 / 8
+// lanes equal, which is how the reductions below use them.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wave_max(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+template <class T>
+__device__ __forceinline__ uint32_t as_u32(T v) { return __builtin_bit_cast(uint32_t, v); }
+template <class T>
+__device__ __forceinline__ T from_u32(uint32_t v) { return __builtin_bit_cast(T, v); }
+
+template <class T, class Op>
+__device__ __forceinline__ T bfly1(T v, Op op) { return op(v, from_u32<T>(dpp<0xB1>(as_u32(v)))); }
+template <class T, class Op>
+__device__ __forceinline__ T bfly2(T v, Op op) { return op(v, from_u32<T>(dpp<0x4E>(as_u32(v)))); }
+template <class T, class Op>
+__device__ __forceinline__ T bfly4(T v, Op op) { return op(v, from_u32<T>(dpp<0x141>(as_u32(v)))); }
+template <class T, class Op>
+__device__ __forceinline__ T bfly8(T v, Op op) { return op(v, from_u32<T>(dpp<0x140>(as_u32(v)))); }
+template <class T, class Op>
+__device__ __forceinline__ T bfly16(T v, Op op) {
+    const auto r = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
+    return op(from_u32<T>(r[0]), from_u32<T>(r[1]));
 }
-__device__ __forceinline__ float wave_min(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-    return v;
+template <class T, class Op>
+__device__ __forceinline__ T bfly32(T v, Op op) {
+    const auto r = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+    return op(from_u32<T>(r[0]), from_u32<T>(r[1]));
 }
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+    v = bfly1(v, op);
+    v = bfly2(v, op);
+    v = bfly4(v, op);
+    v = bfly8(v, op);
+    v = bfly16(v, op);
+    return bfly32(v, op);
 }
+struct OpAdd {
+    template <class T>
+    __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpMin {
+    __device__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpAdd{}); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
+__device__ __forceinline__ float wave_min(float v) { return wave_reduce(v, OpMin{}); }
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_reduce(v, OpAdd{}); }
 
 // Order-preserving key of a binary64 value (-0 is folded onto +0 so that it
 // ties with +0, as numeric comparison does).

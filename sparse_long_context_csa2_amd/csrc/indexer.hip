@@ -135,8 +135,7 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
         for (int ht = 0; ht < HT; ht++)
 #pragma unroll
             for (int r = 0; r < 4; r++) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
+        part = bfly32(bfly16(part, OpAdd{}), OpAdd{});
         // squared norm of key row (l%16), from the B fragments already in registers
         float ss = 0.f;
 #pragma unroll
@@ -146,8 +145,7 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
                 bf16x2 v = __builtin_bit_cast(bf16x2, kb[g][s][e]);
                 ss = __builtin_amdgcn_fdot2_f32_bf16(v, v, ss, false);
             }
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
+        ss = bfly32(bfly16(ss, OpAdd{}), OpAdd{});
         const int64_t slot = slot0 + g * 16 + col;
         if (kg == 0 && slot < n) scores[(int64_t)bq * n + slot] = valid[g] ? part : NEG_INF;
         if (valid[g]) {
@@ -289,10 +287,8 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
             }
 #pragma unroll
             for (int g = 0; g < G; g++) {
-                part[g] += __shfl_xor(part[g], 16);
-                part[g] += __shfl_xor(part[g], 32);
-                ss[g] += __shfl_xor(ss[g], 16);
-                ss[g] += __shfl_xor(ss[g], 32);
+                part[g] = bfly32(bfly16(part[g], OpAdd{}), OpAdd{});
+                ss[g] = bfly32(bfly16(ss[g], OpAdd{}), OpAdd{});
             }
             // lane l = 16 kg + col stores slot 64 it + l, i.e. group kg's row col
             const float mine = kg == 0 ? part[0] : kg == 1 ? part[1] : kg == 2 ? part[2] : part[3];
