@@ -269,8 +269,16 @@ int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream
             csa2::launch_index_score(a->qI, a->idx_dt, a->w, a->kI, a->B, a->Q, a->HI, a->dI, a->N, a->q_pos, a->m,
                                      cand, cand ? a->P : 0, scores, stats, sumwq, s);
             const csa2::RescoreArgs rs{a->qI, a->idx_dt, a->w, a->kI, a->Q, a->HI, a->dI, a->N, sumwq};
+            // the top-k's final pick and compaction run in the attention kernel's prologue when both sides allow
+            const bool fuse = csa2::sel_handoff_supported(z.sel) && csa2::attn_handoff_supported(z.att, z.sel.nwords);
+            csa2::SelHandoff h{};
             csa2::sel_run(z.sel, scores, cand, stats, &rs, a->idx, a->count,
-                          a->mode == CSA2_FULL && a->P > 0 ? a->pool : nullptr, selws, z.selws, s);
+                          a->mode == CSA2_FULL && a->P > 0 ? a->pool : nullptr, selws, z.selws, s, fuse ? &h : nullptr);
+            if (fuse) {
+                void *attws = c.base + c.used;
+                csa2::attn_run(z.att, a->q, a->kv, a->idx, a->scale, a->out, a->lse, attws, z.attws, s, &h);
+                return;
+            }
         }
         void *attws = c.base + c.used;
         csa2::attn_run(z.att, a->q, a->kv, a->idx, a->scale, a->out, a->lse, attws, z.attws, s);

@@ -180,16 +180,156 @@ __device__ __forceinline__ void gather_store(uint16_t *T, const u32x4 *buf, cons
     }
 }
 
+// ------------------------------------------------ selection finish (fused)
+// A block's share of the certified top-k, finished from the selection's
+// records: every block of a query ranks the band (entry i by P lanes over
+// every P-th entry: binary64 score descending, slot ascending), adds the best
+// K - |IN| to the IN bitmap, and compacts the bitmap in slot order; it keeps
+// the entries whose positions fall in its split [e_begin, e_begin + ne) in
+// jsh and writes them (and -1 padding) to the index output; split 0 writes
+// the count.  Redundant across the query's blocks, but short, and it saves a
+// dependent launch.  `scratch` (bytes available: cap) holds the bitmap and
+// the band while this runs.
+struct BandEntA {
+    uint64_t key;
+    int32_t slot, pad;
+};
+
+template <int NT, int SPLIT>
+__device__ void sel_split_entries(const SelHandoff &sel, int bq, int K, int e_begin, int ne, bool first,
+                                  uint32_t *scratch, size_t cap, int32_t *jsh) {
+    __shared__ uint32_t red[NT / 64];
+    const int tid = threadIdx.x;
+    const SelTarget t = sel.sq[bq].t[0];
+    const int64_t nwords = sel.nwords;
+    const int64_t nw4 = (nwords + 3) & ~int64_t(3);
+    uint32_t *bm = scratch;
+    BandEntA *ent = reinterpret_cast<BandEntA *>(scratch + nw4);
+    const int32_t nb = t.band_cnt, r = K - t.in_cnt;
+    const int32_t ecap = (int32_t)((cap - (size_t)nw4 * 4) / sizeof(BandEntA));
+    const bool in_lds = nb <= ecap;
+    const uint32_t *gbm = sel.bitmap + (size_t)bq * nwords;
+    const int32_t *list = sel.band + (size_t)bq * sel.band_cap;
+    const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
+    // one round of loads: the bitmap, and the first NT band entries before the count is known
+    const bool spec_ok = tid < sel.band_cap;
+    const int32_t sl0 = spec_ok ? list[tid] : 0;
+    const double sc0 = spec_ok ? bs[tid] : 0.0;
+    for (int64_t w = tid; w < nwords; w += NT) bm[w] = gbm[w];
+    if (in_lds) {
+        if (tid < nb) {
+            BandEntA e;
+            e.key = dkey(sc0);
+            e.slot = sl0;
+            e.pad = 0;
+            ent[tid] = e;
+        }
+        for (int32_t i = tid + NT; i < nb; i += NT) {
+            BandEntA e;
+            e.key = dkey(bs[i]);
+            e.slot = list[i];
+            e.pad = 0;
+            ent[i] = e;
+        }
+    }
+    __syncthreads();
+    if (r > 0 && nb > 0) {
+        const int P = nb * 8 <= NT ? 8 : nb * 4 <= NT ? 4 : nb * 2 <= NT ? 2 : 1;
+        const int per = NT / P;
+        for (int32_t i0 = 0; i0 < nb; i0 += per) {
+            const int32_t i = i0 + tid / P;
+            const int ep = tid % P;
+            const bool act = i < nb;
+            int32_t rank = 0;
+            uint64_t ki = 0;
+            int32_t si = 0;
+            if (act) {
+                ki = in_lds ? ent[i].key : dkey(bs[i]);
+                si = in_lds ? ent[i].slot : list[i];
+                if (in_lds) {
+                    // eight reads in flight per step
+                    for (int32_t j0 = ep; j0 < nb; j0 += 8 * P) {
+                        BandEntA bj[8];
+#pragma unroll
+                        for (int u = 0; u < 8; u++) {
+                            const int32_t j = j0 + u * P;
+                            bj[u] = ent[j < nb ? j : i];  // past the end: compare with itself (counts 0)
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; u++)
+                            rank += (int)((bj[u].key > ki) | ((bj[u].key == ki) & (bj[u].slot < si)));
+                    }
+                } else {
+                    for (int32_t j = ep; j < nb; j += P) {
+                        const uint64_t kj = dkey(bs[j]);
+                        const int32_t sj = list[j];
+                        rank += (int)((kj > ki) | ((kj == ki) & (sj < si)));
+                    }
+                }
+            }
+            for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
+            if (act && ep == 0 && rank < r) atomicOr(&bm[si >> 5], 1u << (si & 31));
+        }
+    }
+    __syncthreads();
+    // compaction: thread tid owns words [w0, w0 + per)
+    const int64_t per = (nwords + NT - 1) / NT;
+    const int64_t w0 = (int64_t)tid * per;
+    uint32_t mine = 0;
+    for (int64_t w = w0; w < w0 + per && w < nwords; w++) mine += __builtin_popcount(bm[w]);
+    // block exclusive scan
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t incl = mine;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+    for (int i = 0; i < NT / 64; i++) {
+        if (i < wave) before += red[i];
+        tot += red[i];
+    }
+    uint32_t pos = before + incl - mine;
+    const int32_t kept = (int32_t)(tot < (uint32_t)K ? tot : (uint32_t)K);
+    for (int e = tid; e < SPLIT; e += NT) jsh[e] = -1;
+    __syncthreads();
+    const uint32_t lo = (uint32_t)e_begin, hi = (uint32_t)(e_begin + ne);
+    if (pos < hi && pos + mine > lo) {
+        for (int64_t w = w0; w < w0 + per && w < nwords; w++) {
+            uint32_t bits = bm[w];
+            while (bits) {
+                const int b = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if (pos >= lo && pos < hi) jsh[pos - lo] = (int32_t)(w * 32 + b);
+                pos++;
+            }
+        }
+    }
+    __syncthreads();
+    int32_t *orow = sel.idx + (size_t)bq * K + e_begin;
+    for (int e = tid; e < ne; e += NT) {
+        int32_t v = jsh[e];
+        if (v >= 0 && sel.cand) v = sel.cand[(size_t)bq * sel.n + v];
+        jsh[e] = v;
+        orow[e] = v;
+    }
+    if (first && tid == 0 && sel.count) sel.count[bq] = kept;
+    __syncthreads();
+}
+
 // Block order: the NG blocks that share one (query, split) -- one per group
 // of HB x 16 heads -- get linear ids congruent mod 8, so that the round-robin
 // dispatch puts them on one XCD and they gather the split's rows through one
 // L2.  Ids past the last (query, split) pair exit at once.
-template <int D, int FMT, int HB, int DS, int SPLIT>
+template <int D, int FMT, int HB, int DS, int SPLIT, bool FROMSEL>
 __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                           int Q, int H, int64_t N, const int32_t *__restrict__ idx,
                                                           int k, float scale, int nsplit, int npairs,
                                                           uint16_t *__restrict__ out, float *__restrict__ lse,
-                                                          float *__restrict__ part_o, float2 *__restrict__ part_ml) {
+                                                          float *__restrict__ part_o, float2 *__restrict__ part_ml,
+                                                          SelHandoff sel) {
     constexpr int NT = 64 * HB * DS;
     constexpr int KS = D / 32;       // contraction steps of S
     constexpr int DT = D / 16 / DS;  // 16-wide d tiles of O owned by this wave
@@ -215,10 +355,16 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
     const int e_begin = split * SPLIT;
     const int e_end = min(k, e_begin + SPLIT);
     const int ne = e_end - e_begin;
-    const int32_t *irow = idx + (size_t)bq * k + e_begin;
-    for (int e = threadIdx.x; e < SPLIT; e += NT) {
-        int j = e < ne ? irow[e] : -1;
-        jsh[e] = (j >= 0 && j < N) ? j : -1;  // out-of-range entries are skipped like -1
+    if constexpr (FROMSEL) {
+        // the selected set from the certified selection's records (LDS scratch in the tile buffers)
+        sel_split_entries<NT, SPLIT>(sel, bq, k, e_begin, ne, split == 0, reinterpret_cast<uint32_t *>(tile[0]),
+                                     sizeof(tile), jsh);
+    } else {
+        const int32_t *irow = idx + (size_t)bq * k + e_begin;
+        for (int e = threadIdx.x; e < SPLIT; e += NT) {
+            int j = e < ne ? irow[e] : -1;
+            jsh[e] = (j >= 0 && j < N) ? j : -1;  // out-of-range entries are skipped like -1
+        }
     }
     const uint8_t *kvb = kv + (size_t)b * N * G::ROWB;
 
@@ -474,38 +620,43 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
 // heads per block as that allows, so that fewer blocks gather the same rows.
 template <int D, int FMT, int HB, int SPLIT>
 void launch_mfma_hb(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                    float *lse, float *part_o, float2 *part_ml, hipStream_t s) {
+                    float *lse, float *part_o, float2 *part_ml, hipStream_t s, const SelHandoff *sel) {
     // two or more waves per head group (each owns a share of the channels)
     // while that stays within 512 threads
     constexpr int DS = HB == 1 ? (D >= 256 ? 4 : 2) : ((HB <= 4 && D >= 128) ? 2 : 1);
     const int npairs = p.B * p.Q * p.nsplit;
     const int NG = p.H / (16 * HB);
     const int blocks = (npairs + 7) / 8 * 8 * NG;
-    hipLaunchKernelGGL((k_attn_mfma<D, FMT, HB, DS, SPLIT>), dim3(blocks), dim3(64 * HB * DS), 0, s,
-                       static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,
-                       scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml);
+    if (sel)
+        hipLaunchKernelGGL((k_attn_mfma<D, FMT, HB, DS, SPLIT, true>), dim3(blocks), dim3(64 * HB * DS), 0, s,
+                           static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,
+                           scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, *sel);
+    else
+        hipLaunchKernelGGL((k_attn_mfma<D, FMT, HB, DS, SPLIT, false>), dim3(blocks), dim3(64 * HB * DS), 0, s,
+                           static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,
+                           scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, SelHandoff{});
 }
 
 template <int D, int FMT, int SPLIT>
 void launch_mfma_split(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                       float *lse, float *part_o, float2 *part_ml, hipStream_t s) {
+                       float *lse, float *part_o, float2 *part_ml, hipStream_t s, const SelHandoff *sel) {
     const int64_t pairs = (int64_t)p.B * p.Q * p.nsplit;
     const int hgroups = p.H / 16;
     int hb = hgroups;  // head groups per block
     while (hb > 1 && pairs * (hgroups / hb) < 256) hb /= 2;
     switch (hb) {
-        case 1: launch_mfma_hb<D, FMT, 1, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
-        case 2: launch_mfma_hb<D, FMT, 2, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
-        case 4: launch_mfma_hb<D, FMT, 4, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
-        case 8: launch_mfma_hb<D, FMT, 8, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); break;
+        case 1: launch_mfma_hb<D, FMT, 1, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); break;
+        case 2: launch_mfma_hb<D, FMT, 2, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); break;
+        case 4: launch_mfma_hb<D, FMT, 4, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); break;
+        case 8: launch_mfma_hb<D, FMT, 8, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); break;
         default: throw Error(CSA2_EUNSUPPORTED, "matrix-core attention needs H in {16, 32, 64, 128}");
     }
 }
 
 template <int D, int FMT>
 void launch_mfma(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                 float *lse, float *part_o, float2 *part_ml, hipStream_t s) {
-    launch_mfma_split<D, FMT, ATT_SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s);
+                 float *lse, float *part_o, float2 *part_ml, hipStream_t s, const SelHandoff *sel) {
+    launch_mfma_split<D, FMT, ATT_SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel);
 }
 
 }  // namespace
@@ -528,8 +679,13 @@ size_t attn_workspace(const AttnPlan &p) {
     return c.used;
 }
 
+bool attn_handoff_supported(const AttnPlan &p, int64_t nwords) {
+    // the bitmap must fit the kernel's LDS tile buffers with room for a band
+    return p.mfma && (size_t)((nwords + 3) & ~int64_t(3)) * 4 + 1024 * 16 <= (size_t)2 * ATT_SUB * (p.D + 8) * 2;
+}
+
 void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-              float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
+              float *lse, void *ws, size_t ws_bytes, hipStream_t s, const SelHandoff *sel) {
     const int BQ = p.B * p.Q;
     if (!p.mfma) {
         size_t lds = sizeof(float) * ((size_t)p.D + p.k);
@@ -548,8 +704,8 @@ void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *i
     }
 #define CSA2_ATT_CASE(d)                                                                             \
     case d:                                                                                          \
-        if (p.kv_dt == CSA2_FP4) launch_mfma<d, CSA2_FP4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s); \
-        else launch_mfma<d, CSA2_BF16>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s);                   \
+        if (p.kv_dt == CSA2_FP4) launch_mfma<d, CSA2_FP4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); \
+        else launch_mfma<d, CSA2_BF16>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel);                   \
         break;
     switch (p.D) {
         CSA2_ATT_CASE(64)

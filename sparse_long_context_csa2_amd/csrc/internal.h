@@ -17,6 +17,37 @@ void launch_err_bound_from_norms(const double *sumwq, int BQ, int HI, int dI, co
                                  double *err64, hipStream_t s);
 
 // -------------------------------------------------------------- selection
+// Per-query selection records (certified mode): for each target, the value
+// interval of the band, K, |IN| and |BAND|.
+struct SelTarget {
+    double lo, hi;     // BAND = [lo, hi], IN = (hi, +inf)
+    int32_t K;         // entries to keep
+    int32_t in_cnt;    // |IN|
+    int32_t band_cnt;  // |BAND|
+    int32_t pad;
+};
+struct SelQuery {
+    float lo, inv;   // bin() parameters
+    int32_t nvalid;  // finite scores
+    int32_t pad;
+    SelTarget t[2];  // [0] = top-k, [1] = pool
+};
+// What a certified selection leaves for its top-k target when the final pick
+// and compaction are left to the consumer (the attention kernel): the IN
+// bitmap, the band list with its binary64 scores, and where the ascending
+// index list and its count go.
+struct SelHandoff {
+    const SelQuery *sq;
+    const uint32_t *bitmap;  // [BQ][nwords] IN bits of target 0
+    int64_t nwords;
+    const int32_t *band;     // [BQ][band_cap] band slots of target 0
+    const double *band_score;
+    int64_t band_cap;
+    const int32_t *cand;     // slot -> entry (nullable)
+    int64_t n;               // slots per query
+    int32_t *idx;            // [BQ][K] out
+    int32_t *count;          // [BQ] out, nullable
+};
 struct SelPlan {
     int BQ;
     int64_t n;
@@ -37,9 +68,13 @@ struct RescoreArgs {
 bool rescore_supported(int dt, int dI);  // rows of whole 16-byte vectors
 SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified);
 size_t sel_workspace(const SelPlan &p, bool own_stats);
+// With `handoff` (certified mode only) the top-k target is not finished here:
+// the records it needs are described in *handoff (out0/count0 are stored
+// there as the destinations) and the pool target, if any, is finished.
 void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats,
              const RescoreArgs *rs, int32_t *out0, int32_t *count0, int32_t *out1, void *ws, size_t ws_bytes,
-             hipStream_t s);
+             hipStream_t s, SelHandoff *handoff = nullptr);
+bool sel_handoff_supported(const SelPlan &p);
 
 // -------------------------------------------------------------- attention
 struct AttnPlan {
@@ -53,8 +88,12 @@ struct AttnPlan {
 AttnPlan attn_plan(int q_dt, int kv_dt, int B, int Q, int H, int D, int64_t N, int k);
 bool attn_supported(const AttnPlan &p);
 size_t attn_workspace(const AttnPlan &p);
+// With `sel`, the selected entries come from a certified selection's records
+// (finished in the kernel's prologue, which also writes sel->idx / sel->count)
+// instead of from idx.
 void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-              float *lse, void *ws, size_t ws_bytes, hipStream_t s);
+              float *lse, void *ws, size_t ws_bytes, hipStream_t s, const SelHandoff *sel = nullptr);
+bool attn_handoff_supported(const AttnPlan &p, int64_t nwords);
 
 // ------------------------------------------------------------ compression
 size_t compress_workspace(int dt, int64_t n_out, int D, int m, int halo);

@@ -36,20 +36,6 @@ constexpr int NB = 2048;        // histogram bins
 constexpr int CH = 8192;        // slots per chunk (256 threads x 32)
 constexpr int BANDFAST = 2048;  // largest band ranked by pairwise counting
 
-struct SelTarget {
-    double lo, hi;     // BAND = [lo, hi], IN = (hi, +inf)
-    int32_t K;         // entries to keep
-    int32_t in_cnt;    // |IN|
-    int32_t band_cnt;  // |BAND|
-    int32_t pad;
-};
-struct SelQuery {
-    float lo, inv;   // bin() parameters
-    int32_t nvalid;  // finite scores
-    int32_t pad;
-    SelTarget t[2];  // [0] = top-k, [1] = pool
-};
-
 namespace {
 
 constexpr float NEG_INF = -__builtin_inff();
@@ -992,13 +978,13 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_finish_one(const float *__restri
                                                            const SelQuery *__restrict__ sq, const uint32_t *bitmap,
                                                            int64_t nwords, const int32_t *band, const double *band_score,
                                                            int64_t band_cap, int32_t *out0, int32_t *count0,
-                                                           int32_t *out1) {
+                                                           int32_t *out1, int tg0) {
     __shared__ uint32_t bm[ONE_N / 32];
     __shared__ __attribute__((aligned(16))) BandEnt ent[ONE_NT];
     __shared__ int32_t out_lds[ONE_OUT];
     __shared__ uint32_t red[ONE_NT / 64];
     const int bq = blockIdx.x, tid = threadIdx.x;
-    for (int tg = 0; tg < ntgt; tg++) {
+    for (int tg = tg0; tg < ntgt; tg++) {
         const size_t row = (size_t)tg * gridDim.x + bq;
         const SelTarget t = sq[bq].t[tg];
         const uint32_t wv = tid < nwords ? bitmap[row * nwords + tid] : 0u;
@@ -1037,9 +1023,17 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_finish_one(const float *__restri
         if (ranks) {
             ki = ent[ei].key;
             si = ent[ei].slot;
-            for (int32_t j = ep; j < nb; j += P) {
-                const BandEnt bj = ent[j];
-                rank += (int)((bj.key > ki) | ((bj.key == ki) & (bj.slot < si)));
+            // eight reads in flight per step
+            for (int32_t j0 = ep; j0 < nb; j0 += 8 * P) {
+                BandEnt bj[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const int32_t j = j0 + u * P;
+                    bj[u] = ent[j < nb ? j : ei];  // past the end: compare with itself (counts 0)
+                }
+#pragma unroll
+                for (int u = 0; u < 8; u++)
+                    rank += (int)((bj[u].key > ki) | ((bj[u].key == ki) & (bj[u].slot < si)));
             }
         }
         for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
@@ -1083,6 +1077,7 @@ struct FinishArgs {
     const double *band_score;
     int64_t band_cap;
     int32_t *out0, *count0, *out1;
+    int tg0;  // first target to finish
 };
 
 __global__ __launch_bounds__(FIN_NT) void k_sel_finish(FinishArgs a) {
@@ -1093,7 +1088,7 @@ __global__ __launch_bounds__(FIN_NT) void k_sel_finish(FinishArgs a) {
     __shared__ uint32_t red[FIN_NT / 64];
     const int bq = blockIdx.x;
     const SelQuery sqv = a.sq[bq];
-    for (int tg = 0; tg < a.ntgt; tg++) {
+    for (int tg = a.tg0; tg < a.ntgt; tg++) {
         const SelTarget t = sqv.t[tg];
         uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
         const int32_t *list = a.band + ((size_t)tg * gridDim.x + bq) * a.band_cap;
@@ -1161,9 +1156,11 @@ size_t sel_workspace(const SelPlan &p, bool own_stats) {
     return c.used;
 }
 
+bool sel_handoff_supported(const SelPlan &p) { return p.certified && p.nwords <= 8192; }
+
 void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats_in,
              const RescoreArgs *rs, int32_t *out0, int32_t *count0, int32_t *out1, void *ws, size_t ws_bytes,
-             hipStream_t s) {
+             hipStream_t s, SelHandoff *handoff) {
     Carve c(ws, ws_bytes);
     TileStat *stats = const_cast<TileStat *>(stats_in);
     if (!stats && !small_path(p)) stats = c.take<TileStat>((size_t)p.BQ * p.ntiles);
@@ -1254,9 +1251,16 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         }
         check_launch("selection rescore");
     }
+    int tg0 = 0;
+    if (handoff) {
+        if (!sel_handoff_supported(p)) throw Error(CSA2_EINTERNAL, "selection hand-off not supported for this size");
+        *handoff = SelHandoff{sq, bitmap, p.nwords, band, band_score, p.band_cap, cand, p.n, out0, count0};
+        if (p.ntgt == 1) return;
+        tg0 = 1;  // the pool is finished here
+    }
     if (small_path(p)) {
         hipLaunchKernelGGL(k_sel_finish_one, dim3(p.BQ), dim3(ONE_NT), 0, s, scores, cand, p.n, p.ntgt, sq, bitmap,
-                           p.nwords, band, band_score, p.band_cap, out0, count0, out1);
+                           p.nwords, band, band_score, p.band_cap, out0, count0, out1, tg0);
         check_launch("selection finish");
         return;
     }
@@ -1274,6 +1278,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     f.out0 = out0;
     f.count0 = count0;
     f.out1 = out1;
+    f.tg0 = tg0;
     hipLaunchKernelGGL(k_sel_finish, dim3(p.BQ), dim3(FIN_NT), 0, s, f);
     check_launch("selection finish");
 }
