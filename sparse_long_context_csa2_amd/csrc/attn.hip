@@ -323,6 +323,14 @@ __device__ void sel_split_entries(const SelHandoff &sel, int bq, int K, int e_be
 // of HB x 16 heads -- get linear ids congruent mod 8, so that the round-robin
 // dispatch puts them on one XCD and they gather the split's rows through one
 // L2.  Ids past the last (query, split) pair exit at once.
+// Balanced pairwise sum of 1, 2 or 4 partial tiles.
+template <int NPS>
+__device__ __forceinline__ f32x4 tree_sum(const f32x4 *p) {
+    if constexpr (NPS == 1) return p[0];
+    else if constexpr (NPS == 2) return p[0] + p[1];
+    else return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
 template <int D, int FMT, int HB, int DS, int SPLIT, bool FROMSEL>
 __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                           int Q, int H, int64_t N, const int32_t *__restrict__ idx,
@@ -331,13 +339,19 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
                                                           float *__restrict__ part_o, float2 *__restrict__ part_ml,
                                                           SelHandoff sel) {
     constexpr int NT = 64 * HB * DS;
-    constexpr int KS = D / 32;       // contraction steps of S
+    constexpr int KS = D / 32 / DS;  // contraction steps of S owned by this wave (its channel part)
+    constexpr int SP = D >= 256 ? 4 : 2;  // channel parts of the S contraction, for every DS
+    static_assert(SP % DS == 0 && (D / 32) % SP == 0, "S parts must split evenly over the waves");
+    constexpr int LP = SP / DS;       // parts contracted by this wave
+    constexpr int PS = KS / LP;       // steps per part
     constexpr int DT = D / 16 / DS;  // 16-wide d tiles of O owned by this wave
     constexpr int LS = D + 8;   // LDS row stride in 16-bit elements (16-byte pad)
     using G = TileGather<D, FMT>;
     constexpr int PER = (G::CHUNKS + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][ATT_SUB * LS];
     __shared__ int32_t jsh[SPLIT];
+    // partial logits of each wave's channel part, summed over the head group's DS waves
+    __shared__ __attribute__((aligned(16))) f32x4 spart[DS > 1 ? 64 * HB * DS * 2 : 1];
 
     const int NG = H / (16 * HB);
     const int L = blockIdx.x;
@@ -350,7 +364,8 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 15, kg = lane >> 4;
     const int hg = hgb * HB + wave % HB;  // this wave's 16 heads
-    const int dt0 = (wave / HB) * DT;     // first d tile of this wave (S is computed by every d part)
+    const int dpart = wave / HB;          // this wave's channel part: S over it, O for it
+    const int dt0 = dpart * DT;           // first d tile of this wave
 
     const int e_begin = split * SPLIT;
     const int e_end = min(k, e_begin + SPLIT);
@@ -370,17 +385,22 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
 
     // Query heads as the B operand of S^T = C Q^T (fp16 for FP4 rows).
     u32x4 qf[KS];
-    const uint16_t *qrow = q + ((size_t)bq * H + hg * 16 + col) * D + 8 * kg;
+    const uint16_t *qrow = q + ((size_t)bq * H + hg * 16 + col) * D + 8 * kg + 32 * KS * dpart;
 #pragma unroll
     for (int s = 0; s < KS; s++) qf[s] = *reinterpret_cast<const u32x4 *>(qrow + 32 * s);
     float qscale = scale;
     if constexpr (FMT == CSA2_FP4) {
+        // the power-of-two scale covers the whole rows of the 16 heads, so that the
+        // DS waves sharing them contract with the same scaled q
         float amax = 0.f;
+        const uint16_t *qall = qrow - 32 * KS * dpart;
 #pragma unroll
-        for (int s = 0; s < KS; s++)
+        for (int s = 0; s < KS * DS; s++) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(qall + 32 * s);
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(qf[s][e] & 0xffffu)), fabsf(bf16_to_f32(qf[s][e] >> 16))));
+                amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(v[e] & 0xffffu)), fabsf(bf16_to_f32(v[e] >> 16))));
+        }
         amax = wave_max(amax);
         int ex = 0;
         if (amax > 32768.f) ex = (int)ceilf(log2f(amax / 32768.f));
@@ -411,16 +431,35 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
         if (t + 1 < ntiles) gather_issue<D, FMT, NT>(kvb, jsh + (t + 1) * ATT_SUB, buf, sbuf);
         const uint16_t *T = tile[t & 1];
         const int32_t *jt = jsh + t * ATT_SUB;
-        // ---- S^T[e][h] for the two 16-entry halves
+        // ---- S^T[e][h] for the two 16-entry halves. The contraction is cut into SP
+        // channel parts summed as a balanced tree, the same for every DS: this wave
+        // contracts its SP/DS parts and adds them, the DS waves' sums are then added.
         f32x4 st[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; h2++) {
-            st[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t *arow = T + (h2 * 16 + col) * LS + 8 * kg;
+            const uint16_t *arow = T + (h2 * 16 + col) * LS + 8 * kg + 32 * KS * dpart;
+            f32x4 pp[LP];
 #pragma unroll
-            for (int s = 0; s < KS; s++) {
-                const u32x4 av = *reinterpret_cast<const u32x4 *>(arow + 32 * s);
-                st[h2] = mma<FMT>(av, qf[s], st[h2]);
+            for (int lp = 0; lp < LP; lp++) {
+                pp[lp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < PS; s++) {
+                    const u32x4 av = *reinterpret_cast<const u32x4 *>(arow + 32 * (lp * PS + s));
+                    pp[lp] = mma<FMT>(av, qf[lp * PS + s], pp[lp]);
+                }
+            }
+            st[h2] = tree_sum<LP>(pp);
+        }
+        if constexpr (DS > 1) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++) spart[(wave * 64 + lane) * 2 + h2] = st[h2];
+            __syncthreads();
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++) {
+                f32x4 pp[DS];
+#pragma unroll
+                for (int p2 = 0; p2 < DS; p2++) pp[p2] = spart[(((wave % HB) + p2 * HB) * 64 + lane) * 2 + h2];
+                st[h2] = tree_sum<DS>(pp);
             }
         }
         // ---- online softmax for head col; this lane holds entries 16 h2 + 4 kg + i
