@@ -135,25 +135,24 @@ struct TileGather {
     static constexpr int ROWB = FMT == CSA2_FP4 ? D / 2 + D / 16 : 2 * D;
 };
 
+// Loads of one tile's rows into registers: every lane loads (entries of -1
+// read row 0 and are flagged in bit 31 of sbuf, then zeroed by gather_store),
+// so that no branch or copy stands between the loads and they all fly at once.
 template <int D, int FMT, int NT>
 __device__ __forceinline__ void gather_issue(const uint8_t *kvb, const int32_t *jt, u32x4 *buf, uint32_t *sbuf) {
     using G = TileGather<D, FMT>;
     constexpr int PER = (G::CHUNKS + NT - 1) / NT;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < PER; u++) {
         const int c = threadIdx.x + u * NT;
-        buf[u] = zero;
-        sbuf[u] = 0;
-        if (c < G::CHUNKS) {
-            const int r = c / G::CPR, cc = c % G::CPR;
-            const int j = jt[r];
-            if (j >= 0) {
-                const uint8_t *row = kvb + (size_t)j * G::ROWB;
-                buf[u] = *reinterpret_cast<const u32x4 *>(row + cc * 16);
-                if constexpr (FMT == CSA2_FP4) sbuf[u] = *reinterpret_cast<const uint16_t *>(row + D / 2 + cc * 2);
-            }
-        }
+        const int cs = c < G::CHUNKS ? c : 0;
+        const int r = cs / G::CPR, cc = cs % G::CPR;
+        const int j = jt[r];
+        const uint8_t *row = kvb + (size_t)(j >= 0 ? j : 0) * G::ROWB;
+        buf[u] = *reinterpret_cast<const u32x4 *>(row + cc * 16);
+        uint32_t sc = 0;
+        if constexpr (FMT == CSA2_FP4) sc = *reinterpret_cast<const uint16_t *>(row + D / 2 + cc * 2);
+        sbuf[u] = sc | (j < 0 ? 0x80000000u : 0u);
     }
 }
 
@@ -167,64 +166,122 @@ __device__ __forceinline__ void gather_store(uint16_t *T, const u32x4 *buf, cons
         const int c = threadIdx.x + u * NT;
         if (c >= G::CHUNKS) continue;
         const int r = c / G::CPR, cc = c % G::CPR;
+        const bool skip = sbuf[u] >> 31;  // no entry: the row is zero
         if constexpr (FMT == CSA2_FP4) {
             uint32_t o[16];
-            fp4_chunk_to_f16(buf[u], sbuf[u], o);
+            fp4_chunk_to_f16(skip ? u32x4{0u, 0u, 0u, 0u} : buf[u], skip ? 0u : sbuf[u] & 0xffffu, o);
             uint32_t *dst = reinterpret_cast<uint32_t *>(T + r * LS + cc * 32);
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++)
                 reinterpret_cast<u32x4 *>(dst)[q4] = u32x4{o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]};
         } else {
-            *reinterpret_cast<u32x4 *>(T + r * LS + cc * 8) = buf[u];
+            *reinterpret_cast<u32x4 *>(T + r * LS + cc * 8) = skip ? u32x4{0u, 0u, 0u, 0u} : buf[u];
         }
     }
 }
 
 // ------------------------------------------------ selection finish (fused)
 // A block's share of the certified top-k, finished from the selection's
-// records: every block of a query ranks the band (entry i by P lanes over
-// every P-th entry: binary64 score descending, slot ascending), adds the best
-// K - |IN| to the IN bitmap, and compacts the bitmap in slot order; it keeps
-// the entries whose positions fall in its split [e_begin, e_begin + ne) in
-// jsh and writes them (and -1 padding) to the index output; split 0 writes
-// the count.  Redundant across the query's blocks, but short, and it saves a
+// records in three steps.  The attention itself only needs the selected SET;
+// its blocks take the entries in this order: the IN entries in slot order
+// (positions 0 .. |IN|-1), then the best K - |IN| band entries in rank order
+// (binary64 score descending, slot ascending).  A split's first tile usually
+// holds IN entries only, so its rows are in flight while the band is ranked.
+// The index output is the selected set in slot order, written after the
+// ranking.  Redundant across the query's blocks, but short, and it saves a
 // dependent launch.  `scratch` (bytes available: cap) holds the bitmap and
-// the band while this runs.
+// the band until sel_split_idx returns.
 struct BandEntA {
     uint64_t key;
     int32_t slot, pad;
 };
 
+struct SplitSel {
+    int32_t in_cnt, nb;  // |IN| and the band size
+    bool in_lds;         // the band is staged in LDS
+};
+
+__device__ __forceinline__ int32_t sel_entry(const SelHandoff &sel, int bq, int32_t slot) {
+    return sel.cand ? sel.cand[(size_t)bq * sel.n + slot] : slot;
+}
+
+// Popcount scan of the bitmap: thread tid owns words [tid * per, ...); returns
+// its first position and the block total.
+template <int NT>
+__device__ __forceinline__ uint32_t bitmap_scan(const uint32_t *bm, int64_t nwords, uint32_t *red, uint32_t &mine,
+                                                uint32_t &tot) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t per = (nwords + NT - 1) / NT;
+    const int64_t w0 = (int64_t)tid * per;
+    mine = 0;
+    for (int64_t w = w0; w < w0 + per && w < nwords; w++) mine += __builtin_popcount(bm[w]);
+    const uint32_t incl = wave_incl_scan_u32(mine);
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; i++) {
+        const uint32_t x = red[i];
+        before += i < wave ? x : 0u;
+        tot += x;
+    }
+    return before + incl - mine;
+}
+
+// Step 1: the records into LDS (IN bitmap, band entries with their keys) and
+// the split's IN positions into jsh (-1 elsewhere).  Ends with jsh's IN part
+// visible to the block.
 template <int NT, int SPLIT>
-__device__ void sel_split_entries(const SelHandoff &sel, int bq, int K, int e_begin, int ne, bool first,
-                                  uint32_t *scratch, size_t cap, int32_t *jsh) {
-    __shared__ uint32_t red[NT / 64];
+__device__ SplitSel sel_split_in(const SelHandoff &sel, int bq, int e_begin, int ne, uint32_t *scratch, size_t cap,
+                                 int32_t *jsh, uint32_t *red) {
     const int tid = threadIdx.x;
     const SelTarget t = sel.sq[bq].t[0];
     const int64_t nwords = sel.nwords;
     const int64_t nw4 = (nwords + 3) & ~int64_t(3);
     uint32_t *bm = scratch;
     BandEntA *ent = reinterpret_cast<BandEntA *>(scratch + nw4);
-    const int32_t nb = t.band_cnt, r = K - t.in_cnt;
-    const int32_t ecap = (int32_t)((cap - (size_t)nw4 * 4) / sizeof(BandEntA));
-    const bool in_lds = nb <= ecap;
+    SplitSel st;
+    st.in_cnt = t.in_cnt;
+    st.nb = t.band_cnt;
+    st.in_lds = st.nb <= (int32_t)((cap - (size_t)nw4 * 4) / sizeof(BandEntA));
     const uint32_t *gbm = sel.bitmap + (size_t)bq * nwords;
     const int32_t *list = sel.band + (size_t)bq * sel.band_cap;
     const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
-    // one round of loads: the bitmap, and the first NT band entries before the count is known
+    // one round of loads: the first NT band entries (before the count is known)
+    // and the bitmap, four words per load where the rows are 16-byte aligned
     const bool spec_ok = tid < sel.band_cap;
     const int32_t sl0 = spec_ok ? list[tid] : 0;
     const double sc0 = spec_ok ? bs[tid] : 0.0;
-    for (int64_t w = tid; w < nwords; w += NT) bm[w] = gbm[w];
-    if (in_lds) {
-        if (tid < nb) {
+    if ((nwords & 3) == 0) {
+        constexpr int U = 4;  // NT * U * 4 words per round
+        const int64_t nq = nwords >> 2;
+        for (int64_t q0 = 0; q0 < nq; q0 += (int64_t)NT * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int64_t qi = q0 + tid + (int64_t)NT * u;
+                v[u] = reinterpret_cast<const u32x4 *>(gbm)[qi < nq ? qi : nq - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int64_t qi = q0 + tid + (int64_t)NT * u;
+                if (qi < nq) reinterpret_cast<u32x4 *>(bm)[qi] = v[u];
+            }
+        }
+    } else {
+        for (int64_t w = tid; w < nwords; w += NT) bm[w] = gbm[w];
+    }
+    for (int e = tid; e < SPLIT; e += NT) jsh[e] = -1;
+    if (st.in_lds) {
+        if (tid < st.nb) {
             BandEntA e;
             e.key = dkey(sc0);
             e.slot = sl0;
             e.pad = 0;
             ent[tid] = e;
         }
-        for (int32_t i = tid + NT; i < nb; i += NT) {
+        for (int32_t i = tid + NT; i < st.nb; i += NT) {
             BandEntA e;
             e.key = dkey(bs[i]);
             e.slot = list[i];
@@ -233,96 +290,194 @@ __device__ void sel_split_entries(const SelHandoff &sel, int bq, int K, int e_be
         }
     }
     __syncthreads();
-    if (r > 0 && nb > 0) {
+    uint32_t mine, tot;
+    uint32_t pos = bitmap_scan<NT>(bm, nwords, red, mine, tot);
+    const uint32_t lo = (uint32_t)e_begin, hi = (uint32_t)(e_begin + ne);
+    if (pos < hi && pos + mine > lo) {
+        const int64_t per = (nwords + NT - 1) / NT;
+        const int64_t w0 = (int64_t)tid * per;
+        for (int64_t w = w0; w < w0 + per && w < nwords; w++) {
+            uint32_t bits = bm[w];
+            while (bits) {
+                const int b = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if (pos >= lo && pos < hi) jsh[pos - lo] = sel_entry(sel, bq, (int32_t)(w * 32 + b));
+                pos++;
+            }
+        }
+    }
+    __syncthreads();
+    return st;
+}
+
+// Step 2: rank the band; the best r = K - |IN| entries join the bitmap, and
+// those whose positions |IN| + rank fall in the split go into jsh.  issue()
+// is called once (it starts the first tile's row loads when they are known):
+// on the common path right after the ranking's LDS reads, so that the loads
+// fly during the ranking.  Ends with jsh complete.
+template <int NT, int SPLIT, class Issue>
+__device__ void sel_split_band(const SelHandoff &sel, int bq, int K, const SplitSel &st, int e_begin, int ne,
+                               uint32_t *scratch, int32_t *jsh, Issue &&issue) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t nw4 = (sel.nwords + 3) & ~int64_t(3);
+    uint32_t *bm = scratch;
+    const u32x4 *ent4 = reinterpret_cast<const u32x4 *>(scratch + nw4);
+    const int32_t nb = st.nb, r = K - st.in_cnt;
+    const int32_t *list = sel.band + (size_t)bq * sel.band_cap;
+    const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
+    // entry with slot si and rank rk (< r) is selected
+    auto take = [&](int32_t si, int32_t rk) {
+        atomicOr(&bm[si >> 5], 1u << (si & 31));
+        const int32_t p = st.in_cnt + rk - e_begin;
+        if (p >= 0 && p < ne) jsh[p] = sel_entry(sel, bq, si);
+    };
+    if (r > 0 && nb > 0 && st.in_lds && nb <= NT) {
+        // every wave holds all nb entries in registers (lane l of chunk c: entry
+        // 64 c + l) and ranks the entries i = wave + NW t, four per step: entry
+        // i's key and slot are read out of lane t, each chunk's comparisons
+        // give lane masks, the rank is the sum of their populations
+        constexpr int NW = NT / 64;
+        constexpr int MAXC = NT / 64;
+        const int nch = (nb + 63) / 64;
+        u32x4 jc[MAXC];
+#pragma unroll
+        for (int c = 0; c < MAXC; c++) {
+            const int j = 64 * c + lane;
+            jc[c] = c < nch ? ent4[j < nb ? j : 0] : u32x4{0u, 0u, 0u, 0u};
+        }
+        uint64_t vmask[MAXC];  // lanes of chunk c that hold an entry
+#pragma unroll
+        for (int c = 0; c < MAXC; c++) vmask[c] = __ballot(64 * c + lane < nb);
+        const int ni = (nb - wave + NW - 1) / NW;  // <= 64 since nb <= NT
+        const u32x4 mine = ent4[lane < ni ? wave + NW * lane : 0];
+        const int32_t mine_e = sel_entry(sel, bq, (int32_t)mine[2]);  // before the row loads
+        issue();  // global loads go out after the LDS reads of the ranking
+        uint32_t myrank = 0;
+        for (int t0 = 0; t0 < ni; t0 += 4) {
+            uint64_t ki[4];
+            uint32_t si[4], cnt[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int tt = t0 + u < ni ? t0 + u : ni - 1;
+                ki[u] = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mine[0], tt) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mine[1], tt) << 32);
+                si[u] = (uint32_t)__builtin_amdgcn_readlane((int)mine[2], tt);
+                cnt[u] = 0;
+            }
+#pragma unroll
+            for (int c = 0; c < MAXC; c++) {
+                if (c < nch) {
+                    const uint64_t kj = (uint64_t)jc[c][0] | ((uint64_t)jc[c][1] << 32);
+#pragma unroll
+                    for (int u = 0; u < 4; u++) {
+                        // key greater, or equal with a lower slot
+                        const uint64_t gt = __builtin_amdgcn_uicmpl(kj, ki[u], 34);       // unsigned >
+                        const uint64_t eq = __builtin_amdgcn_uicmpl(kj, ki[u], 32);       // ==
+                        const uint64_t lt = __builtin_amdgcn_uicmp(jc[c][2], si[u], 36);  // unsigned <
+                        cnt[u] += (uint32_t)__builtin_popcountll((gt | (eq & lt)) & vmask[c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++) myrank = lane == t0 + u ? cnt[u] : myrank;
+        }
+        if (lane < ni && myrank < (uint32_t)r) {
+            const int32_t si = (int32_t)mine[2];
+            atomicOr(&bm[si >> 5], 1u << (si & 31));
+            const int32_t p = st.in_cnt + (int32_t)myrank - e_begin;
+            if (p >= 0 && p < ne) jsh[p] = mine_e;
+        }
+    } else if (r > 0 && nb > 0) {
+        // entry i is ranked by P consecutive lanes, each comparing a 1/P share
         const int P = nb * 8 <= NT ? 8 : nb * 4 <= NT ? 4 : nb * 2 <= NT ? 2 : 1;
         const int per = NT / P;
         for (int32_t i0 = 0; i0 < nb; i0 += per) {
             const int32_t i = i0 + tid / P;
             const int ep = tid % P;
             const bool act = i < nb;
+            const int32_t ii = act ? i : 0;
             int32_t rank = 0;
-            uint64_t ki = 0;
-            int32_t si = 0;
-            if (act) {
-                ki = in_lds ? ent[i].key : dkey(bs[i]);
-                si = in_lds ? ent[i].slot : list[i];
-                if (in_lds) {
-                    // eight reads in flight per step
-                    for (int32_t j0 = ep; j0 < nb; j0 += 8 * P) {
-                        BandEntA bj[8];
+            uint64_t ki;
+            int32_t si;
+            if (st.in_lds) {
+                const u32x4 me = ent4[ii];
+                ki = (uint64_t)me[0] | ((uint64_t)me[1] << 32);
+                si = (int32_t)me[2];
+                for (int32_t j0 = ep; j0 < nb; j0 += 8 * P) {
+                    u32x4 bj[8];
 #pragma unroll
-                        for (int u = 0; u < 8; u++) {
-                            const int32_t j = j0 + u * P;
-                            bj[u] = ent[j < nb ? j : i];  // past the end: compare with itself (counts 0)
-                        }
-#pragma unroll
-                        for (int u = 0; u < 8; u++)
-                            rank += (int)((bj[u].key > ki) | ((bj[u].key == ki) & (bj[u].slot < si)));
+                    for (int u = 0; u < 8; u++) {
+                        const int32_t j = j0 + u * P;
+                        bj[u] = ent4[j < nb ? j : ii];  // past the end: compare with itself (counts 0)
                     }
-                } else {
-                    for (int32_t j = ep; j < nb; j += P) {
-                        const uint64_t kj = dkey(bs[j]);
-                        const int32_t sj = list[j];
-                        rank += (int)((kj > ki) | ((kj == ki) & (sj < si)));
+#pragma unroll
+                    for (int u = 0; u < 8; u++) {
+                        const uint64_t kj = (uint64_t)bj[u][0] | ((uint64_t)bj[u][1] << 32);
+                        rank += (int)((kj > ki) | ((kj == ki) & ((int32_t)bj[u][2] < si)));
                     }
                 }
+            } else {
+                ki = dkey(bs[ii]);
+                si = list[ii];
+                for (int32_t j = ep; j < nb; j += P) {
+                    const uint64_t kj = dkey(bs[j]);
+                    const int32_t sj = list[j];
+                    rank += (int)((kj > ki) | ((kj == ki) & (sj < si)));
+                }
             }
-            for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
-            if (act && ep == 0 && rank < r) atomicOr(&bm[si >> 5], 1u << (si & 31));
+            if (P >= 2) rank = bfly1(rank, OpAdd{});
+            if (P >= 4) rank = bfly2(rank, OpAdd{});
+            if (P >= 8) rank = bfly4(rank, OpAdd{});
+            if (act && ep == 0 && rank < r) take(si, rank);
         }
+        __builtin_amdgcn_s_waitcnt(0);  // this path's own loads are done before the rows go out
+        issue();
+    } else {
+        issue();
     }
     __syncthreads();
-    // compaction: thread tid owns words [w0, w0 + per)
-    const int64_t per = (nwords + NT - 1) / NT;
-    const int64_t w0 = (int64_t)tid * per;
-    uint32_t mine = 0;
-    for (int64_t w = w0; w < w0 + per && w < nwords; w++) mine += __builtin_popcount(bm[w]);
-    // block exclusive scan
-    const int lane = tid & 63, wave = tid >> 6;
-    uint32_t incl = mine;
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
-    if (lane == 63) red[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-    for (int i = 0; i < NT / 64; i++) {
-        if (i < wave) before += red[i];
-        tot += red[i];
-    }
-    uint32_t pos = before + incl - mine;
+}
+
+// Step 3: the index output, the selected set in slot order (its split's share,
+// -1 past the count), and the count (split 0).  Ends with the scratch free.
+template <int NT>
+__device__ void sel_split_idx(const SelHandoff &sel, int bq, int K, int e_begin, int ne, bool first,
+                              const uint32_t *scratch, uint32_t *red) {
+    const int tid = threadIdx.x;
+    const int64_t nwords = sel.nwords;
+    const uint32_t *bm = scratch;
+    uint32_t mine, tot;
+    uint32_t pos = bitmap_scan<NT>(bm, nwords, red, mine, tot);
     const int32_t kept = (int32_t)(tot < (uint32_t)K ? tot : (uint32_t)K);
-    for (int e = tid; e < SPLIT; e += NT) jsh[e] = -1;
-    __syncthreads();
     const uint32_t lo = (uint32_t)e_begin, hi = (uint32_t)(e_begin + ne);
-    if (pos < hi && pos + mine > lo) {
+    int32_t *orow = sel.idx + (size_t)bq * K + e_begin;
+    // one loop per mapping, so that the identity mapping waits for no load
+    auto scatter = [&](auto map) {
+        const int64_t per = (nwords + NT - 1) / NT;
+        const int64_t w0 = (int64_t)tid * per;
         for (int64_t w = w0; w < w0 + per && w < nwords; w++) {
             uint32_t bits = bm[w];
             while (bits) {
                 const int b = __builtin_ctz(bits);
                 bits &= bits - 1;
-                if (pos >= lo && pos < hi) jsh[pos - lo] = (int32_t)(w * 32 + b);
+                if (pos >= lo && pos < hi) orow[pos - lo] = map((int32_t)(w * 32 + b));
                 pos++;
             }
         }
+    };
+    if (pos < hi && pos + mine > lo) {
+        if (sel.cand) {
+            const int32_t *cq = sel.cand + (size_t)bq * sel.n;
+            scatter([&](int32_t sl) { return cq[sl]; });
+        } else {
+            scatter([](int32_t sl) { return sl; });
+        }
     }
-    __syncthreads();
-    int32_t *orow = sel.idx + (size_t)bq * K + e_begin;
-    for (int e = tid; e < ne; e += NT) {
-        int32_t v = jsh[e];
-        if (v >= 0 && sel.cand) v = sel.cand[(size_t)bq * sel.n + v];
-        jsh[e] = v;
-        orow[e] = v;
-    }
+    for (int e = (kept > e_begin ? kept - e_begin : 0) + tid; e < ne; e += NT) orow[e] = -1;
     if (first && tid == 0 && sel.count) sel.count[bq] = kept;
     __syncthreads();
 }
 
-// Block order: the NG blocks that share one (query, split) -- one per group
-// of HB x 16 heads -- get linear ids congruent mod 8, so that the round-robin
-// dispatch puts them on one XCD and they gather the split's rows through one
-// L2.  Ids past the last (query, split) pair exit at once.
 // Balanced pairwise sum of 1, 2 or 4 partial tiles.
 template <int NPS>
 __device__ __forceinline__ f32x4 tree_sum(const f32x4 *p) {
@@ -331,6 +486,11 @@ __device__ __forceinline__ f32x4 tree_sum(const f32x4 *p) {
     else return (p[0] + p[1]) + (p[2] + p[3]);
 }
 
+
+// Block order: the NG blocks that share one (query, split) -- one per group
+// of HB x 16 heads -- get linear ids congruent mod 8, so that the round-robin
+// dispatch puts them on one XCD and they gather the split's rows through one
+// L2.  Ids past the last (query, split) pair exit at once.
 template <int D, int FMT, int HB, int DS, int SPLIT, bool FROMSEL>
 __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                           int Q, int H, int64_t N, const int32_t *__restrict__ idx,
@@ -370,24 +530,38 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
     const int e_begin = split * SPLIT;
     const int e_end = min(k, e_begin + SPLIT);
     const int ne = e_end - e_begin;
+    const uint8_t *kvb = kv + (size_t)b * N * G::ROWB;
+    // Query heads as the B operand of S^T = C Q^T (fp16 for FP4 rows), in flight from the start.
+    u32x4 qf[KS];
+    const uint16_t *qrow = q + ((size_t)bq * H + hg * 16 + col) * D + 8 * kg + 32 * KS * dpart;
+#pragma unroll
+    for (int s = 0; s < KS; s++) qf[s] = *reinterpret_cast<const u32x4 *>(qrow + 32 * s);
+
+    const int ntiles = (ne + ATT_SUB - 1) / ATT_SUB;
+    u32x4 buf[PER];
+    uint32_t sbuf[PER];
     if constexpr (FROMSEL) {
         // the selected set from the certified selection's records (LDS scratch in the tile buffers)
-        sel_split_entries<NT, SPLIT>(sel, bq, k, e_begin, ne, split == 0, reinterpret_cast<uint32_t *>(tile[0]),
-                                     sizeof(tile), jsh);
+        __shared__ uint32_t sred[NT / 64];
+        uint32_t *scr = reinterpret_cast<uint32_t *>(tile[0]);
+        const SplitSel st = sel_split_in<NT, SPLIT>(sel, bq, e_begin, ne, scr, sizeof(tile), jsh, sred);
+        // the first tile's rows go out now if its entries are all IN entries
+        const bool early = e_begin + min(ATT_SUB, ne) <= st.in_cnt;
+        // (issued unconditionally: a branch around the loads would make later
+        // waits for other loads wait for these too; reissued below if not early)
+        sel_split_band<NT, SPLIT>(sel, bq, k, st, e_begin, ne, scr, jsh,
+                                  [&]() { gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf); });
+        sel_split_idx<NT>(sel, bq, k, e_begin, ne, split == 0, scr, sred);
+        if (!early) gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf);
     } else {
         const int32_t *irow = idx + (size_t)bq * k + e_begin;
         for (int e = threadIdx.x; e < SPLIT; e += NT) {
             int j = e < ne ? irow[e] : -1;
             jsh[e] = (j >= 0 && j < N) ? j : -1;  // out-of-range entries are skipped like -1
         }
+        __syncthreads();  // jsh ready
+        if (ntiles > 0) gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf);
     }
-    const uint8_t *kvb = kv + (size_t)b * N * G::ROWB;
-
-    // Query heads as the B operand of S^T = C Q^T (fp16 for FP4 rows).
-    u32x4 qf[KS];
-    const uint16_t *qrow = q + ((size_t)bq * H + hg * 16 + col) * D + 8 * kg + 32 * KS * dpart;
-#pragma unroll
-    for (int s = 0; s < KS; s++) qf[s] = *reinterpret_cast<const u32x4 *>(qrow + 32 * s);
     float qscale = scale;
     if constexpr (FMT == CSA2_FP4) {
         // the power-of-two scale covers the whole rows of the 16 heads, so that the
@@ -418,14 +592,7 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
     for (int t = 0; t < DT; t++) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = NEG_INF, l_run = 0.f;
 
-    const int ntiles = (ne + ATT_SUB - 1) / ATT_SUB;
-    u32x4 buf[PER];
-    uint32_t sbuf[PER];
-    __syncthreads();  // jsh ready
-    if (ntiles > 0) {
-        gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf);
-        gather_store<D, FMT, NT>(tile[0], buf, sbuf);
-    }
+    if (ntiles > 0) gather_store<D, FMT, NT>(tile[0], buf, sbuf);
     __syncthreads();
     for (int t = 0; t < ntiles; t++) {
         if (t + 1 < ntiles) gather_issue<D, FMT, NT>(kvb, jsh + (t + 1) * ATT_SUB, buf, sbuf);

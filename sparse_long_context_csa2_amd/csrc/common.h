@@ -126,6 +126,20 @@ struct OpMin {
     __device__ float operator()(float a, float b) const { return fminf(a, b); }
 };
 
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then the row totals are carried forward with the row
+// broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
+// Lanes that a shift or broadcast does not reach add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpAdd{}); }
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
 __device__ __forceinline__ float wave_min(float v) { return wave_reduce(v, OpMin{}); }

@@ -73,3 +73,17 @@ def test_certified_rescoring_row_shapes(b, HI, dI, idx_dtype):
     spec = synth.Decode(B=1, Q=2, N=3000, HI=HI, dI=dI, H=16, D=128, k=256, idx_dtype=idx_dtype, seed=HI + dI,
                         layers=["FULL"])
     run_group(b, synth.make_decode(spec))
+
+
+@pytest.mark.parametrize("N,distinct,k", [
+    (6000, 3, 512),    # tie groups of 2,000 entries: a band of thousands, ranked from LDS
+    (9000, 2, 1024),   # a band of 4,500 entries: more than the attention prologue stages in LDS
+    (5000, 40, 700),   # bands of a few hundred entries
+])
+def test_full_layer_tied_index_keys(b, N, distinct, k):
+    """Repeated indexer keys make runs of equal scores; the lower slot wins each tie."""
+    spec = synth.Decode(B=2, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=k, seed=N + distinct, layers=["FULL"])
+    d = synth.make_decode(spec)
+    reps = torch.arange(N) % distinct
+    d["kI"] = d["kI"][:, reps].contiguous()
+    run_group(b, d)
