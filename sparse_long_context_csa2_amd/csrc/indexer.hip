@@ -165,13 +165,17 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
 
 // ----------------------------------------------------------- streaming path
 // Same contraction and operand layouts as k_index_mfma, for full scans with
-// many tiles: each wave owns one 256-slot tile and walks it in 4 steps of 64
-// slots.  The key fragments of a 16-slot group are reloaded with the next
-// step's rows as soon as the group's matrix-core products are issued, so a
-// wave keeps about 16 KiB of keys in flight from start to end with a single
-// register buffer.  The query fragments and head weights are loaded once per
-// wave.  A step's 64 scores leave in one coalesced store (lane l writes slot
-// 64 * step + l), and the tile statistics are a wave reduction.
+// many tiles.  A block's 4 waves take one 256-slot tile per pass, wave w its
+// 64-slot step w, and the blocks of a query sweep the tiles together: in pass
+// i block x takes tile x + nbx i (nbx = blocks per query), so at any moment
+// the waves of a query read one compact region of the key cache (adjacent
+// 64 KiB tiles) rather than 2048 scattered streams.  The key fragments of a
+// 16-slot group are reloaded with the next pass's rows as soon as the
+// group's matrix-core products are issued, so a wave keeps about 16 KiB of
+// keys in flight with a single register buffer.  The query fragments and
+// head weights are loaded once per wave.  A step's 64 scores leave in one
+// coalesced store (lane l writes slot 64 w + l of the tile); each tile's
+// statistics are the min / max / count of its 4 waves' reductions.
 template <int HI, int DI>
 __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restrict__ qI, const float *__restrict__ w,
                                                          const uint16_t *__restrict__ kI, int Q, int64_t N,
@@ -180,139 +184,152 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
                                                          int ntiles, double *__restrict__ sumwq) {
     constexpr int HT = HI / 16;
     constexpr int KS = DI / 32;
-    constexpr int G = 4;           // 16-slot groups per step
-    constexpr int IT = TILE / 64;  // steps per tile
+    constexpr int G = 4;             // 16-slot groups per step
+    constexpr int IT = 4;            // passes (tiles per block)
+    static_assert(TILE == 4 * 64, "a tile is one 64-slot step per wave");
+    __shared__ TileStat tst[IT][4];
     const int bq = blockIdx.y;
     const int b = bq / Q;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 15, kg = lane >> 4;
     const int64_t nvis = visible_entries(q_pos, bq, m, N);  // slots >= nvis are not scored
-    const int tile = blockIdx.x * 4 + wave;
+    const int nbx = gridDim.x;
+    const int span = nbx * IT;
+    // each query starts its sweep at its own offset, so that the queries'
+    // regions (which sit a power of two apart) do not load the same memory
+    // channels at the same time
+    const int rot = (int)(((int64_t)bq * 8) % span);
+    auto tile_of = [&](int it) {
+        const int t = blockIdx.x + nbx * it + rot;
+        return t < span ? t : t - span;
+    };
+    // this wave's first slot in pass it (tiles past the end read clamped rows and are dropped)
+    auto step0 = [&](int it) { return (int64_t)tile_of(it) * TILE + wave * 64; };
 
-    if (tile < ntiles) {
-        const int64_t slot0 = (int64_t)tile * TILE;
-        // Rows past the visible range are clamped to the last row of the key
-        // cache and loaded anyway (no branch around the loads); their scores
-        // are replaced by -inf and they take no part in the statistics.
-        const uint16_t *kb0 = kI + (size_t)b * N * DI + 8 * kg;
-        const int64_t last = N - 1;
-        auto krow = [&](int64_t r) {
-            const int64_t j = slot0 + r + col;
-            return kb0 + (size_t)(j < last ? j : last) * DI;
-        };
-        u32x4 kb[G][KS];
+    // Rows past the visible range are clamped to the last row of the key
+    // cache and loaded anyway (no branch around the loads); their scores are
+    // replaced by -inf and they take no part in the statistics.
+    const uint16_t *kb0 = kI + (size_t)b * N * DI + 8 * kg;
+    const int64_t last = N - 1;
+    auto krow = [&](int it, int g) {
+        const int64_t j = step0(it) + g * 16 + col;
+        return kb0 + (size_t)(j < last ? j : last) * DI;
+    };
+    // query fragments first: the waits for key rows then never wait for them
+    u32x4 qa[HT][KS];
+    const uint16_t *qrow = qI + (size_t)bq * HI * DI;
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+            qa[ht][s] = *reinterpret_cast<const u32x4 *>(qrow + (ht * 16 + col) * DI + 32 * s + 8 * kg);
+    f32x4 wv[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) wv[ht] = *reinterpret_cast<const f32x4 *>(w + (size_t)bq * HI + ht * 16 + 4 * kg);
+    u32x4 kb[G][KS];
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const uint16_t *kr = krow(0, g);
+#pragma unroll
+        for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
+    }
+    if (sumwq && blockIdx.x == 0 && wave == 0) {
+        // sum_h |w_h| ||q_h|| in binary64 from the query fragments in
+        // registers (lane (col, kg) holds 8 KS elements of head 16 ht + col),
+        // while the first key rows are in flight.  Fixed order: lane
+        // partials, then kg pairs, then a butterfly over col, then ht.
+        double acc = 0.0;
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) {
+            double q2 = 0.0;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; s2++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const double x0 = (double)bf16_to_f32((uint16_t)(qa[ht][s2][e] & 0xffffu));
+                    const double x1 = (double)bf16_to_f32((uint16_t)(qa[ht][s2][e] >> 16));
+                    q2 = fma(x0, x0, q2);
+                    q2 = fma(x1, x1, q2);
+                }
+            q2 += __shfl_xor(q2, 16);
+            q2 += __shfl_xor(q2, 32);
+            double t = fabs((double)w[(size_t)bq * HI + ht * 16 + col]) * sqrt(q2);
+            for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o);
+            acc += t;
+        }
+        if (lane == 0) sumwq[bq] = acc;
+    }
+
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        float part[G], ss[G];
 #pragma unroll
         for (int g = 0; g < G; g++) {
-            const uint16_t *kr = krow(g * 16);
+            f32x4 acc[HT];
 #pragma unroll
-            for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
-        }
-        u32x4 qa[HT][KS];
-        const uint16_t *qrow = qI + (size_t)bq * HI * DI;
-#pragma unroll
-        for (int ht = 0; ht < HT; ht++)
+            for (int ht = 0; ht < HT; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; s++)
-                qa[ht][s] = *reinterpret_cast<const u32x4 *>(qrow + (ht * 16 + col) * DI + 32 * s + 8 * kg);
-        f32x4 wv[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ht++)
-            wv[ht] = *reinterpret_cast<const f32x4 *>(w + (size_t)bq * HI + ht * 16 + 4 * kg);
-        if (sumwq && tile == 0) {
-            // sum_h |w_h| ||q_h|| in binary64 from the query fragments in
-            // registers (lane (col, kg) holds 8 KS elements of head 16 ht + col),
-            // while the first key rows are in flight.  Fixed order: lane
-            // partials, then kg pairs, then a butterfly over col, then ht.
-            double acc = 0.0;
-#pragma unroll
-            for (int ht = 0; ht < HT; ht++) {
-                double q2 = 0.0;
-#pragma unroll
-                for (int s2 = 0; s2 < KS; s2++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const double x0 = (double)bf16_to_f32((uint16_t)(qa[ht][s2][e] & 0xffffu));
-                        const double x1 = (double)bf16_to_f32((uint16_t)(qa[ht][s2][e] >> 16));
-                        q2 = fma(x0, x0, q2);
-                        q2 = fma(x1, x1, q2);
-                    }
-                q2 += __shfl_xor(q2, 16);
-                q2 += __shfl_xor(q2, 32);
-                double t = fabs((double)w[(size_t)bq * HI + ht * 16 + col]) * sqrt(q2);
-                for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o);
-                acc += t;
-            }
-            if (lane == 0) sumwq[bq] = acc;
-        }
-
-        float smin = POS_INF, smax = NEG_INF, kmax2 = 0.f;
-        uint32_t nval = 0;
-#pragma unroll
-        for (int it = 0; it < IT; it++) {
-            float part[G], ss[G];
-#pragma unroll
-            for (int g = 0; g < G; g++) {
-                f32x4 acc[HT];
-#pragma unroll
-                for (int ht = 0; ht < HT; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < KS; s++)
-#pragma unroll
-                    for (int ht = 0; ht < HT; ht++)
-                        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ht][s]),
-                                                                          __builtin_bit_cast(bf16x8, kb[g][s]),
-                                                                          acc[ht], 0, 0, 0);
-                float q2 = 0.f;
-#pragma unroll
-                for (int s = 0; s < KS; s++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        bf16x2 v = __builtin_bit_cast(bf16x2, kb[g][s][e]);
-                        q2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, q2, false);
-                    }
-                ss[g] = q2;
-                if (it + 1 < IT) {  // this group's rows of the next step
-                    const uint16_t *kr = krow((it + 1) * 64 + g * 16);
-#pragma unroll
-                    for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
-                }
-                float p = 0.f;
 #pragma unroll
                 for (int ht = 0; ht < HT; ht++)
+                    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ht][s]),
+                                                                      __builtin_bit_cast(bf16x8, kb[g][s]),
+                                                                      acc[ht], 0, 0, 0);
+            float q2 = 0.f;
 #pragma unroll
-                    for (int r = 0; r < 4; r++) p = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), p);
-                part[g] = p;
-                // keep each group's reload where it is: hoisting them all would need a second buffer
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int s = 0; s < KS; s++)
 #pragma unroll
-            for (int g = 0; g < G; g++) {
-                part[g] = bfly32(bfly16(part[g], OpAdd{}), OpAdd{});
-                ss[g] = bfly32(bfly16(ss[g], OpAdd{}), OpAdd{});
+                for (int e = 0; e < 4; e++) {
+                    bf16x2 v = __builtin_bit_cast(bf16x2, kb[g][s][e]);
+                    q2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, q2, false);
+                }
+            ss[g] = q2;
+            if (it + 1 < IT) {  // this group's rows of the next pass
+                const uint16_t *kr = krow(it + 1, g);
+#pragma unroll
+                for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
             }
-            // lane l = 16 kg + col stores slot 64 it + l, i.e. group kg's row col
-            const float mine = kg == 0 ? part[0] : kg == 1 ? part[1] : kg == 2 ? part[2] : part[3];
-            const float mss = kg == 0 ? ss[0] : kg == 1 ? ss[1] : kg == 2 ? ss[2] : ss[3];
-            const int64_t slot = slot0 + it * 64 + lane;
-            const bool ok = slot < nvis;
-            if (slot < N) scores[(int64_t)bq * N + slot] = ok ? mine : NEG_INF;
-            if (ok) {
-                smin = fminf(smin, mine);
-                smax = fmaxf(smax, mine);
-                kmax2 = fmaxf(kmax2, mss);
-                nval++;
-            }
+            float p = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) p = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), p);
+            part[g] = p;
+            // keep each group's reload where it is: hoisting them all would need a second buffer
+            __builtin_amdgcn_sched_barrier(0);
         }
-        smin = wave_min(smin);
-        smax = wave_max(smax);
-        kmax2 = wave_max(kmax2);
-        nval = wave_sum_u32(nval);
-        if (lane == 0) {
-            TileStat t;
-            t.smin = smin;
-            t.smax = smax;
-            t.kmax2 = kmax2;
-            t.nvalid = nval;
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            part[g] = bfly32(bfly16(part[g], OpAdd{}), OpAdd{});
+            ss[g] = bfly32(bfly16(ss[g], OpAdd{}), OpAdd{});
+        }
+        // lane l = 16 kg + col stores slot 64 w + l of the tile, i.e. group kg's row col
+        const float mine = kg == 0 ? part[0] : kg == 1 ? part[1] : kg == 2 ? part[2] : part[3];
+        const float mss = kg == 0 ? ss[0] : kg == 1 ? ss[1] : kg == 2 ? ss[2] : ss[3];
+        const int64_t slot = step0(it) + lane;
+        const bool ok = slot < nvis;
+        if (slot < N) scores[(int64_t)bq * N + slot] = ok ? mine : NEG_INF;
+        TileStat t;
+        t.smin = wave_min(ok ? mine : POS_INF);
+        t.smax = wave_max(ok ? mine : NEG_INF);
+        t.kmax2 = wave_max(ok ? mss : 0.f);
+        t.nvalid = (uint32_t)__builtin_popcountll(__ballot(ok));
+        if (lane == 0) tst[it][wave] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < IT) {
+        const int it = threadIdx.x;
+        const int tile = tile_of(it);
+        if (tile < ntiles) {
+            TileStat t = tst[it][0];
+#pragma unroll
+            for (int x = 1; x < 4; x++) {
+                const TileStat u = tst[it][x];
+                t.smin = fminf(t.smin, u.smin);
+                t.smax = fmaxf(t.smax, u.smax);
+                t.kmax2 = fmaxf(t.kmax2, u.kmax2);
+                t.nvalid += u.nvalid;
+            }
             stats[(size_t)bq * ntiles + tile] = t;
         }
     }
