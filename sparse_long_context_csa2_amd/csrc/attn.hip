@@ -691,7 +691,7 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
         }
         if (lse && kg == 0 && dt0 == 0) lse[(size_t)bq * H + h] = l_run > 0.f ? m_run + logf(l_run) : NEG_INF;
     } else {
-        const size_t pi = ((size_t)bq * nsplit + split) * H + h;
+        const size_t pi = ((size_t)bq * H + h) * nsplit + split;  // a head's splits are adjacent
         float *prow = part_o + pi * D + 16 * dt0 + 4 * kg;
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4 *>(prow + 16 * dt) = o[dt];
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ 
         float2 ml[COMB_UNROLL];
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; u++)
-            if (s0 + u < nsplit) ml[u] = part_ml[((size_t)bq * nsplit + s0 + u) * H + h];
+            if (s0 + u < nsplit) ml[u] = part_ml[((size_t)bq * H + h) * nsplit + s0 + u];
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; u++)
             if (s0 + u < nsplit) M = fmaxf(M, ml[u].x);
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ 
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; u++)
             if (s0 + u < nsplit) {
-                const size_t pi = ((size_t)bq * nsplit + s0 + u) * H + h;
+                const size_t pi = ((size_t)bq * H + h) * nsplit + s0 + u;
                 ml[u] = part_ml[pi];
                 po[u] = reinterpret_cast<const f32x4 *>(part_o + pi * D)[c4];
             }
