@@ -172,10 +172,14 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
 // 64 KiB tiles) rather than 2048 scattered streams.  The key fragments of a
 // 16-slot group are reloaded with the next pass's rows as soon as the
 // group's matrix-core products are issued, so a wave keeps about 16 KiB of
-// keys in flight with a single register buffer.  The query fragments and
-// head weights are loaded once per wave.  A step's 64 scores leave in one
-// coalesced store (lane l writes slot 64 w + l of the tile); each tile's
-// statistics are the min / max / count of its 4 waves' reductions.
+// keys in flight with a single register buffer.  The query heads are read
+// from HBM once per block (16 B per thread, issued ahead of the first key
+// rows) and handed to the waves' fragments through LDS: loading them per
+// wave straight from memory moved four times the bytes through the CU's
+// load path before the first key rows went out.  The block's 1024 scores
+// are kept in LDS and written after the last pass, in coalesced stores;
+// each tile's statistics are the min / max / count of its 4 waves'
+// reductions.
 template <int HI, int DI>
 __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restrict__ qI, const float *__restrict__ w,
                                                          const uint16_t *__restrict__ kI, int Q, int64_t N,
@@ -187,7 +191,10 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
     constexpr int G = 4;             // 16-slot groups per step
     constexpr int IT = 4;            // passes (tiles per block)
     static_assert(TILE == 4 * 64, "a tile is one 64-slot step per wave");
+    constexpr int QN = HI * DI / 8, QPT = (QN + 255) / 256;  // 16-byte pieces of q, per thread
     __shared__ TileStat tst[IT][4];
+    __shared__ float ssh[IT][TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t qsh[HI * DI];
     const int bq = blockIdx.y;
     const int b = bq / Q;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -215,14 +222,17 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
         const int64_t j = step0(it) + g * 16 + col;
         return kb0 + (size_t)(j < last ? j : last) * DI;
     };
-    // query fragments first: the waits for key rows then never wait for them
-    u32x4 qa[HT][KS];
-    const uint16_t *qrow = qI + (size_t)bq * HI * DI;
+    // the query heads first, so that waiting for them never waits for key rows
+    // (the guard is compiled out when the pieces split evenly over the block:
+    // a conditional load would be sunk below the key loads)
+    u32x4 qst[QPT];
+    {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(qI + (size_t)bq * HI * DI);
 #pragma unroll
-    for (int ht = 0; ht < HT; ht++)
-#pragma unroll
-        for (int s = 0; s < KS; s++)
-            qa[ht][s] = *reinterpret_cast<const u32x4 *>(qrow + (ht * 16 + col) * DI + 32 * s + 8 * kg);
+        for (int i = 0; i < QPT; i++)
+            qst[i] = src[QN % 256 == 0 ? (int)threadIdx.x + 256 * i : min((int)threadIdx.x + 256 * i, QN - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 wv[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ht++) wv[ht] = *reinterpret_cast<const f32x4 *>(w + (size_t)bq * HI + ht * 16 + 4 * kg);
@@ -233,6 +243,16 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
 #pragma unroll
         for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
     }
+#pragma unroll
+    for (int i = 0; i < QPT; i++)
+        if (QN % 256 == 0 || (int)threadIdx.x + 256 * i < QN) reinterpret_cast<u32x4 *>(qsh)[threadIdx.x + 256 * i] = qst[i];
+    __syncthreads();
+    u32x4 qa[HT][KS];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+            qa[ht][s] = *reinterpret_cast<const u32x4 *>(qsh + (ht * 16 + col) * DI + 32 * s + 8 * kg);
     if (sumwq && blockIdx.x == 0 && wave == 0) {
         // sum_h |w_h| ||q_h|| in binary64 from the query fragments in
         // registers (lane (col, kg) holds 8 KS elements of head 16 ht + col),
@@ -303,12 +323,12 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
             part[g] = bfly32(bfly16(part[g], OpAdd{}), OpAdd{});
             ss[g] = bfly32(bfly16(ss[g], OpAdd{}), OpAdd{});
         }
-        // lane l = 16 kg + col stores slot 64 w + l of the tile, i.e. group kg's row col
+        // lane l = 16 kg + col holds slot 64 w + l of the tile, i.e. group kg's row col
         const float mine = kg == 0 ? part[0] : kg == 1 ? part[1] : kg == 2 ? part[2] : part[3];
         const float mss = kg == 0 ? ss[0] : kg == 1 ? ss[1] : kg == 2 ? ss[2] : ss[3];
         const int64_t slot = step0(it) + lane;
         const bool ok = slot < nvis;
-        if (slot < N) scores[(int64_t)bq * N + slot] = ok ? mine : NEG_INF;
+        ssh[it][wave * 64 + lane] = ok ? mine : NEG_INF;
         TileStat t;
         t.smin = wave_min(ok ? mine : POS_INF);
         t.smax = wave_max(ok ? mine : NEG_INF);
@@ -317,6 +337,11 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
         if (lane == 0) tst[it][wave] = t;
     }
     __syncthreads();
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        const int64_t slot = (int64_t)tile_of(it) * TILE + threadIdx.x;
+        if (slot < N) scores[(int64_t)bq * N + slot] = ssh[it][threadIdx.x];
+    }
     if (threadIdx.x < IT) {
         const int it = threadIdx.x;
         const int tile = tile_of(it);
