@@ -461,8 +461,8 @@ __device__ void finish_target(uint32_t *bm, int64_t nwords, int64_t n, int32_t K
 
 // ------------------------------------------------------ one-block path
 // One 1024-thread block per query keeps its n <= 32768 scores in registers
-// (slot s in thread s % 1024, so a wave's 64 consecutive slots give two
-// bitmap words straight from one ballot).  With the score range known from
+// (thread t holds slots 32 t .. 32 t + 31, so its 32 comparisons against a
+// threshold are bitmap word t, built without any cross-lane step).  With the score range known from
 // the indexer's tile statistics (else from the scores), the 2048-bin
 // histogram is built from registers, the bin edges of the K-th largest come
 // from a 64-way search in a narrow window around their estimate, and the
@@ -473,6 +473,7 @@ constexpr int ONE_NT = 1024;
 constexpr int64_t ONE_N = 32768;
 constexpr int ONE_SPT = (int)(ONE_N / ONE_NT);
 constexpr int ONE_OUT = 8192;  // output entries staged in LDS
+static_assert(ONE_SPT == 32, "a thread's slots form one bitmap word");
 
 struct OneArgs {
     const float *scores;
@@ -535,27 +536,35 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     // scores (all loads in flight, slots past n read the last slot and are
     // dropped), candidate filter, tile statistics
     float v[ONE_SPT];
+    const int s0 = ONE_SPT * tid;
     const float *sp = a.scores + base;
+    const int32_t *cp = a.cand ? a.cand + base : nullptr;
+    if (s0 + ONE_SPT <= n && ((reinterpret_cast<uintptr_t>(sp) | reinterpret_cast<uintptr_t>(cp)) & 15) == 0) {
+        // whole word in range: 16-byte loads
 #pragma unroll
-    for (int i = 0; i < ONE_SPT; i++) {
-        const uint32_t sl = (uint32_t)(tid + ONE_NT * i);
-        v[i] = sp[sl < (uint32_t)n ? sl : (uint32_t)(n - 1)];
-    }
-    if (a.cand) {
-        const int32_t *cp = a.cand + base;
-        int32_t cv[ONE_SPT];
+        for (int i = 0; i < ONE_SPT; i += 4) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4 *>(sp + s0 + i);
+            v[i] = q4[0], v[i + 1] = q4[1], v[i + 2] = q4[2], v[i + 3] = q4[3];
+        }
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < ONE_SPT; i += 4) {
+                const u32x4 c4 = *reinterpret_cast<const u32x4 *>(cp + s0 + i);
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    if ((int32_t)c4[e] < 0) v[i + e] = NEG_INF;
+            }
+        }
+    } else {
+        // the ragged last word (slots past n read the last slot and are dropped)
 #pragma unroll
         for (int i = 0; i < ONE_SPT; i++) {
-            const uint32_t sl = (uint32_t)(tid + ONE_NT * i);
-            cv[i] = cp[sl < (uint32_t)n ? sl : (uint32_t)(n - 1)];
+            const int sl = s0 + i < n ? s0 + i : n - 1;
+            v[i] = sp[sl];
+            if (cp && cp[sl] < 0) v[i] = NEG_INF;
+            if (s0 + i >= n) v[i] = NEG_INF;
         }
-#pragma unroll
-        for (int i = 0; i < ONE_SPT; i++)
-            if (cv[i] < 0) v[i] = NEG_INF;
     }
-#pragma unroll
-    for (int i = 0; i < ONE_SPT; i++)
-        if (tid + ONE_NT * i >= n) v[i] = NEG_INF;
     for (int i = tid; i < NB; i += ONE_NT) hist[i] = 0;
     float lo = POS_INF, hi = NEG_INF, km = 0.f;
     uint32_t c = 0;
@@ -662,39 +671,34 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
         }
         // IN: x > thi  <=>  x > f_hi;  BAND: x >= tlo  <=>  x >= f_lo  (x is a float)
         const float f_hi = f32_down(thi), f_lo = f32_up(tlo);
-        uint32_t nin = 0;
         int32_t *band = a.band + ((size_t)tg * gridDim.x + bq) * a.band_cap;
-        // a fresh copy of the thread index: slot numbers are recomputed here
-        // rather than kept live (and spilled) from the loads
-        int tidc = tid;
-        asm volatile("" : "+v"(tidc));
-        const int wword = __builtin_amdgcn_readfirstlane(2 * wave);  // this wave's first bitmap word
+        // bit i of word t: slot 32 t + i is IN (resp. BAND); -inf (no score)
+        // is neither, since f_lo is finite
+        const float f_lo2 = fmaxf(f_lo, -__FLT_MAX__);
+        uint32_t win = 0, wbnd = 0;
 #pragma unroll
         for (int i = 0; i < ONE_SPT; i++) {
             const float x = v[i];
-            const bool valid = x != NEG_INF;
-            const bool in = valid && x > f_hi;
-            const bool bnd = valid && !in && x >= f_lo;
-            const uint64_t bal = __ballot(in);
-            const uint64_t bb = __ballot(bnd);
-            const int word0 = (ONE_NT / 32) * i + wword;
-            if (lane == 0) {
-                bm[word0] = (uint32_t)bal;
-                bm[word0 + 1] = (uint32_t)(bal >> 32);
-                nin += (uint32_t)__builtin_popcountll(bal);
-            }
-            if (bb) {
-                int32_t basepos = 0;
-                if (lane == 0) basepos = atomicAdd(&band_cnt_sh, (int32_t)__builtin_popcountll(bb));
-                basepos = __shfl(basepos, 0);
-                if (bnd) {
-                    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bb >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bb, 0u));
-                    band[basepos + (int32_t)below] = tidc + ONE_NT * i;
-                }
-            }
+            win |= (x > f_hi ? 1u : 0u) << i;
+            wbnd |= (x <= f_hi && x >= f_lo2 ? 1u : 0u) << i;
         }
-        if (lane == 0 && nin) atomicAdd(&in_cnt_sh, (int32_t)nin);
+        bm[tid] = win;
+        // band slots: one block-wide counter update per wave, then each lane
+        // writes the slots of its word at its offset within the wave
+        const uint32_t nbw = (uint32_t)__builtin_popcount(wbnd);
+        const uint32_t incl = wave_incl_scan_u32(nbw);
+        const uint32_t wtot = __builtin_amdgcn_readlane(incl, 63);
+        const uint32_t nin = wave_sum_u32((uint32_t)__builtin_popcount(win));
+        int32_t wbase = 0;
+        if (lane == 0) {
+            if (wtot) wbase = atomicAdd(&band_cnt_sh, (int32_t)wtot);
+            if (nin) atomicAdd(&in_cnt_sh, (int32_t)nin);
+        }
+        wbase = __builtin_amdgcn_readlane(wbase, 0);
+        {
+            int32_t pos = wbase + (int32_t)(incl - nbw);
+            for (uint32_t m = wbnd; m; m &= m - 1) band[pos++] = s0 + __builtin_ctz(m);
+        }
         __syncthreads();
         const int32_t in_cnt = in_cnt_sh;
         const int32_t nb = band_cnt_sh;
