@@ -514,15 +514,14 @@ __device__ uint32_t edge_key(uint32_t lk, uint32_t hk, int target, float lo, flo
 
 template <bool CERT>
 __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
+    static_assert(NB == 2 * ONE_NT, "a thread takes two bins of the suffix scan");
     __shared__ uint32_t hist[NB];
-    __shared__ uint32_t cum[NB + 1];
     __shared__ uint32_t bm[ONE_N / 32];
     __shared__ uint32_t red[ONE_NT / 64];
     __shared__ f32x4 rred[ONE_NT / 64];
-    __shared__ uint32_t grp_sum[ONE_NT];
-    __shared__ int bstar_sh;
-    __shared__ uint32_t edge_sh[2];
-    __shared__ int32_t band_cnt_sh, in_cnt_sh;
+    __shared__ int bstar_sh[2];
+    __shared__ double thr_sh[2];
+    __shared__ int32_t band_cnt_sh[2], in_cnt_sh[2];
     // exact mode's finishing scratch
     __shared__ uint64_t key_lds[CERT ? 1 : BANDFAST];
     __shared__ int32_t slot_lds[CERT ? 1 : BANDFAST];
@@ -566,6 +565,11 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
         }
     }
     for (int i = tid; i < NB; i += ONE_NT) hist[i] = 0;
+    if (tid < 2) {
+        bstar_sh[tid] = -1;
+        band_cnt_sh[tid] = 0;
+        in_cnt_sh[tid] = 0;
+    }
     float lo = POS_INF, hi = NEG_INF, km = 0.f;
     uint32_t c = 0;
     const bool have_range = a.stats != nullptr;
@@ -612,62 +616,53 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     for (int i = 0; i < ONE_SPT; i++)
         if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
     __syncthreads();
-    // suffix counts: cum[b] = number of scores in bins >= b
+    // Suffix counts, top bin first: thread t takes bins NB-1-2t and NB-2-2t;
+    // an inclusive scan in thread order gives S = the number of scores in bins
+    // >= NB-2-2t, and the thread whose pair holds the K-th largest score names
+    // its bin b* for each target.
     {
-        constexpr int BPT = NB / ONE_NT;
-        uint32_t hb[BPT], local = 0;
+        const uint32_t h_hi = hist[NB - 1 - 2 * tid], h_lo = hist[NB - 2 - 2 * tid];
+        const uint32_t incl = wave_incl_scan_u32(h_hi + h_lo);
+        if (lane == 63) red[wave] = incl;
+        __syncthreads();
+        uint32_t before = 0;
 #pragma unroll
-        for (int j = 0; j < BPT; j++) {
-            hb[j] = hist[BPT * tid + j];
-            local += hb[j];
+        for (int i = 0; i < ONE_NT / 64; i++) before += i < wave ? red[i] : 0u;
+        const uint32_t S = before + incl;          // scores in bins >= NB-2-2t
+        const uint32_t S_prev = S - h_hi - h_lo;   // scores in bins >= NB-2t
+        const uint32_t c_hi = S_prev + h_hi;       // scores in bins >= NB-1-2t
+        for (int tg = 0; tg < a.ntgt; tg++) {
+            const uint32_t K = (uint32_t)a.K[tg];
+            if (nvalid > K) {
+                if (c_hi >= K && S_prev < K) bstar_sh[tg] = NB - 1 - 2 * tid;
+                else if (S >= K && c_hi < K) bstar_sh[tg] = NB - 2 - 2 * tid;
+            }
         }
-        grp_sum[ONE_NT - 1 - tid] = local;
-        __syncthreads();
-        uint32_t tot;
-        const uint32_t ex = block_excl_scan<ONE_NT>(grp_sum[tid], red, tot);
-        __syncthreads();
-        grp_sum[tid] = ex;
-        __syncthreads();
-        uint32_t run = grp_sum[ONE_NT - 1 - tid];
-#pragma unroll
-        for (int j = BPT - 1; j >= 0; j--) {
-            run += hb[j];
-            cum[BPT * tid + j] = run;
-        }
-        if (tid == 0) cum[NB] = 0;
     }
-    double E = 0.0;
-    if constexpr (CERT)
-        E = score_bound(sqrt((double)km * (1.0 + ldexp(1.0, -10))), sumwq * (1.0 + ldexp(1.0, -30)), a.HI, a.dI);
     __syncthreads();
 
     const int64_t nwords = (a.n + 31) / 32;
     for (int tg = 0; tg < a.ntgt; tg++) {
         const int K = a.K[tg];
-        if (tid == 0) {
-            bstar_sh = -1;
-            band_cnt_sh = 0;
-            in_cnt_sh = 0;
-        }
-        __syncthreads();
-        if (nvalid > (uint32_t)K)
-            for (int b2 = (NB / ONE_NT) * tid; b2 < (NB / ONE_NT) * (tid + 1); b2++)
-                if (cum[b2] >= (uint32_t)K && cum[b2 + 1] < (uint32_t)K) bstar_sh = b2;
-        __syncthreads();
-        const int bstar = bstar_sh;
+        const int bstar = bstar_sh[tg];
         double tlo = -__builtin_inf(), thi = -__builtin_inf();
         if (bstar >= 0) {
-            // [a, z] = float values >= lo whose bin is b* (bin() is monotone)
-            if (wave < 2) {  // wave 0: lower edge, wave 1: upper edge
+            // [a, z] = float values >= lo whose bin is b* (bin() is monotone);
+            // wave 0 finds the lower edge and its threshold, wave 1 the upper
+            if (wave < 2) {
                 const uint32_t lk = fkey(lo), hk = 0xff7fffffu;
                 uint32_t kk = hk;
                 if (wave == 0) kk = edge_key(lk, hk, bstar, lo, inv);
                 else if (bstar + 1 < NB) kk = edge_key(lk, hk, bstar + 1, lo, inv) - 1;
-                if (lane == 0) edge_sh[wave] = kk;
+                double E = 0.0;
+                if constexpr (CERT)
+                    E = score_bound(sqrt((double)km * (1.0 + ldexp(1.0, -10))), sumwq * (1.0 + ldexp(1.0, -30)),
+                                    a.HI, a.dI);
+                if (lane == 0) thr_sh[wave] = wave == 0 ? thr_lo(fkey_inv(kk), E) : thr_hi(fkey_inv(kk), E);
             }
             __syncthreads();
-            tlo = thr_lo(fkey_inv(edge_sh[0]), E);
-            thi = thr_hi(fkey_inv(edge_sh[1]), E);
+            tlo = thr_sh[0];
+            thi = thr_sh[1];
         }
         // IN: x > thi  <=>  x > f_hi;  BAND: x >= tlo  <=>  x >= f_lo  (x is a float)
         const float f_hi = f32_down(thi), f_lo = f32_up(tlo);
@@ -691,8 +686,8 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
         const uint32_t nin = wave_sum_u32((uint32_t)__builtin_popcount(win));
         int32_t wbase = 0;
         if (lane == 0) {
-            if (wtot) wbase = atomicAdd(&band_cnt_sh, (int32_t)wtot);
-            if (nin) atomicAdd(&in_cnt_sh, (int32_t)nin);
+            if (wtot) wbase = atomicAdd(&band_cnt_sh[tg], (int32_t)wtot);
+            if (nin) atomicAdd(&in_cnt_sh[tg], (int32_t)nin);
         }
         wbase = __builtin_amdgcn_readlane(wbase, 0);
         {
@@ -700,8 +695,8 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
             for (uint32_t m = wbnd; m; m &= m - 1) band[pos++] = s0 + __builtin_ctz(m);
         }
         __syncthreads();
-        const int32_t in_cnt = in_cnt_sh;
-        const int32_t nb = band_cnt_sh;
+        const int32_t in_cnt = in_cnt_sh[tg];
+        const int32_t nb = band_cnt_sh[tg];
         if constexpr (CERT) {
             uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
             for (int64_t wd = tid; wd < nwords; wd += ONE_NT) gbm[wd] = bm[wd];
