@@ -769,23 +769,32 @@ __device__ __forceinline__ double dot_vec(double acc, u32x4 q, u32x4 k) {
 }
 
 // Rows of at most RS_ROWB bytes: a block takes RS_EPB consecutive band
-// entries of one query.  Their slots are read speculatively with the target
-// record, their key rows staged once in LDS (one 16-byte load per thread),
-// and each wave runs RS_EPW entries as independent binary64 chains: lane h
-// holds query head h's row in registers and reads the key rows from LDS (the
-// same address in every lane).  Lane e then sums entry e's head terms in
-// order.  Blocks loop over the list when it is longer than the grid.
-constexpr int RS_EPW = 4;                       // entries per wave
+// entries of one query.  Its band slots are read speculatively with the target
+// record; then the query rows of the first 64 heads (coalesced, staged in LDS)
+// and the block's key rows (one 16-byte load per thread, staged in LDS already
+// converted to binary64) are in flight together, so the dot products read the
+// key values as broadcast operands and spend the double-precision unit on the
+// fused multiply-adds alone.  Each wave
+// runs RS_EPW entries as independent binary64 chains (lane h: head h), then
+// lane e sums entry e's head terms in order.  Two entries per wave spread a
+// query's band over about as many waves as the chip has SIMDs.  Blocks loop
+// over the list when it is longer than the grid.
+constexpr int RS_EPW = 2;                       // entries per wave
 constexpr int RS_EPB = RS_EPW * (RS_NT / 64);  // entries per block
 constexpr int RS_ROWB = 512;                    // longest key row staged (bytes)
 constexpr int RS_QCH = 16;                      // query-row vectors per chunk
+constexpr int RS_MAXD = RS_ROWB / 2;            // longest staged row in elements
 
 template <bool F32>
-__global__ __launch_bounds__(RS_NT) void k_sel_rescore(RescoreKArgs a) {
+__global__ __launch_bounds__(RS_NT, 2) void k_sel_rescore(RescoreKArgs a) {
 #pragma clang fp contract(off)
-    __shared__ __attribute__((aligned(16))) u32x4 krow_lds[RS_EPB][RS_ROWB / 16];
+    constexpr int QS = RS_ROWB / 16 + 1;  // LDS stride of a query row in 16-byte vectors (padded)
+    constexpr int QPT = 64 * (RS_ROWB / 16) / RS_NT;
+    __shared__ __attribute__((aligned(16))) double krow_lds[RS_EPB][RS_MAXD];
+    __shared__ u32x4 qsh[64][QS];
     __shared__ double tl[RS_NT / 64][RS_EPW][64];
     constexpr int ESZ = F32 ? 4 : 2;
+    constexpr int EPV = 16 / ESZ;  // elements per 16-byte vector
     const int bq = blockIdx.y;
     const int b = bq / a.Q;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -799,8 +808,18 @@ __global__ __launch_bounds__(RS_NT) void k_sel_rescore(RescoreKArgs a) {
     const int32_t nb0 = sqv.t[0].band_cnt, nb1 = a.ntgt > 1 ? sqv.t[1].band_cnt : 0;
     const int32_t total = nb0 + nb1;
     if (eb0 >= total) return;
+    // query rows of heads 0 .. min(HI, 64) - 1, row-major in 16-byte vectors
+    const int nqv = (a.HI < 64 ? a.HI : 64) * nvec;
+    u32x4 qst[QPT];
+    {
+        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.qI) + (size_t)bq * a.HI * a.dI * ESZ);
+#pragma unroll
+        for (int i = 0; i < QPT; i++)
+            if (tid + RS_NT * i < nqv) qst[i] = qsrc[tid + RS_NT * i];
+    }
+    bool q_staged = false;
     for (int32_t e0 = eb0; e0 < total; e0 += gridDim.x * RS_EPB) {
-        // stage the key rows of entries e0 .. e0 + RS_EPB - 1 (16-byte chunk q of the block's rows)
+        // stage the key rows of entries e0 .. e0 + RS_EPB - 1 as binary64
         for (int q = tid; q < RS_EPB * nvec; q += RS_NT) {
             const int i = q / nvec, c = q - i * nvec;
             const int32_t e = e0 + i;
@@ -809,9 +828,23 @@ __global__ __launch_bounds__(RS_NT) void k_sel_rescore(RescoreKArgs a) {
                                          ? spec
                                          : (e < nb0 ? a.band[row0 + e] : a.band[row1 + (e - nb0)]);
                 const int64_t j = a.cand ? (int64_t)a.cand[(int64_t)bq * a.n + slot] : (int64_t)slot;
-                krow_lds[i][c] = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.kI) +
-                                                                ((size_t)b * a.N + j) * a.dI * ESZ)[c];
+                const u32x4 kv = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.kI) +
+                                                                 ((size_t)b * a.N + j) * a.dI * ESZ)[c];
+                double *dst = &krow_lds[i][c * EPV];
+#pragma unroll
+                for (int x = 0; x < EPV; x++) {
+                    const uint32_t kw = kv[F32 ? x : x >> 1];
+                    dst[x] = (double)__uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
+                }
             }
+        }
+        if (!q_staged) {
+#pragma unroll
+            for (int i = 0; i < QPT; i++) {
+                const int v = tid + RS_NT * i;
+                if (v < nqv) qsh[v / nvec][v % nvec] = qst[i];
+            }
+            q_staged = true;
         }
         __syncthreads();
         const int ew = wave * RS_EPW;  // this wave's first entry in the block
@@ -827,44 +860,50 @@ __global__ __launch_bounds__(RS_NT) void k_sel_rescore(RescoreKArgs a) {
             for (int e = 0; e < RS_EPW; e++) dot[e] = 0.0;
             for (int v0 = 0; v0 < nvec; v0 += RS_QCH) {
                 u32x4 qv[RS_QCH];
+                if (h0 == 0) {
 #pragma unroll
-                for (int u = 0; u < RS_QCH; u++)
-                    if (v0 + u < nvec) qv[u] = qrow[v0 + u];
+                    for (int u = 0; u < RS_QCH; u++)
+                        if (v0 + u < nvec) qv[u] = qsh[lane][v0 + u];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < RS_QCH; u++)
+                        if (v0 + u < nvec) qv[u] = qrow[v0 + u];
+                }
 #pragma unroll
                 for (int u = 0; u < RS_QCH; u++) {
                     if (v0 + u >= nvec) break;
-                    u32x4 kv[RS_EPW];
 #pragma unroll
-                    for (int e = 0; e < RS_EPW; e++) kv[e] = krow_lds[ew + e][v0 + u];
-#pragma unroll
-                    for (int x = 0; x < (F32 ? 4 : 8); x++) {
-                        const uint32_t qw = qv[u][F32 ? x : x >> 1];
-                        const double qd = (double)__uint_as_float(F32 ? qw : ((x & 1) ? (qw & 0xffff0000u) : (qw << 16)));
+                    for (int x = 0; x < EPV; x += 2) {
+                        const uint32_t qw0 = qv[u][F32 ? x : x >> 1];
+                        const uint32_t qw1 = qv[u][F32 ? x + 1 : x >> 1];
+                        const double qd0 = (double)__uint_as_float(F32 ? qw0 : (qw0 << 16));
+                        const double qd1 = (double)__uint_as_float(F32 ? qw1 : (qw1 & 0xffff0000u));
 #pragma unroll
                         for (int e = 0; e < RS_EPW; e++) {
-                            const uint32_t kw = kv[e][F32 ? x : x >> 1];
-                            const double kd =
-                                (double)__uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
-                            dot[e] = __builtin_fma(qd, kd, dot[e]);
+                            const double2 k2 = *reinterpret_cast<const double2 *>(&krow_lds[ew + e][(v0 + u) * EPV + x]);
+                            dot[e] = __builtin_fma(qd0, k2.x, dot[e]);
+                            dot[e] = __builtin_fma(qd1, k2.y, dot[e]);
                         }
                     }
                 }
             }
 #pragma unroll
-            for (int e = 0; e < RS_EPW; e++) tl[wave][e][lane] = wh * (dot[e] > 0.0 ? dot[e] : 0.0);
+            for (int e = 0; e < RS_EPW; e++) tl[wave][e][lane] = h < a.HI ? wh * (dot[e] > 0.0 ? dot[e] : 0.0) : 0.0;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (lane < RS_EPW) {
-                // head terms t_h0, t_h0+1, ... added in order (read 16 at a time)
+                // head terms t_h0, t_h0+1, ... added in order (read 16 at a time);
+                // lanes past the last head hold +0.0, and sc + 0.0 == sc (sc is
+                // never -0.0: it starts at +0.0 and a round-to-nearest sum is
+                // -0.0 only if both addends are)
                 const int hn = a.HI - h0 < 64 ? a.HI - h0 : 64;
                 for (int c0 = 0; c0 < hn; c0 += 16) {
                     double tv[16];
 #pragma unroll
                     for (int i = 0; i < 16; i++) tv[i] = tl[wave][lane][c0 + i];
 #pragma unroll
-                    for (int i = 0; i < 16; i++)
-                        if (c0 + i < hn) sc = sc + tv[i];
+                    for (int i = 0; i < 16; i++) sc = sc + tv[i];
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
