@@ -700,8 +700,10 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
 }
 
 // ----------------------------------------------------------- split merge
-// One thread per 4 channels of one head: the split maxima and sums are read
-// first (all loads in flight), then the 4-channel partial rows of every split.
+// One thread per 4 channels of one head.  Up to COMB_UNROLL splits are read in
+// one round of loads (their maxima, sums and 4-channel partial rows), so the
+// merge waits for memory once; more splits take further rounds, the running
+// maximum rescaling what is already summed.
 constexpr int COMB_UNROLL = 16;
 
 __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ part_o,
@@ -713,39 +715,40 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ 
     const int64_t row = gid / tpr;  // (bq, h)
     const int c4 = (int)(gid % tpr);
     if (row >= (int64_t)BQ * H) return;
-    const int64_t bq = row / H, h = row % H;
-    float M = NEG_INF;
-    for (int s0 = 0; s0 < nsplit; s0 += COMB_UNROLL) {
-        float2 ml[COMB_UNROLL];
-#pragma unroll
-        for (int u = 0; u < COMB_UNROLL; u++)
-            if (s0 + u < nsplit) ml[u] = part_ml[((size_t)bq * H + h) * nsplit + s0 + u];
-#pragma unroll
-        for (int u = 0; u < COMB_UNROLL; u++)
-            if (s0 + u < nsplit) M = fmaxf(M, ml[u].x);
-    }
-    float Ls = 0.f;
+    float M = NEG_INF, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsplit; s0 += COMB_UNROLL) {
         float2 ml[COMB_UNROLL];
         f32x4 po[COMB_UNROLL];
 #pragma unroll
-        for (int u = 0; u < COMB_UNROLL; u++)
-            if (s0 + u < nsplit) {
-                const size_t pi = ((size_t)bq * H + h) * nsplit + s0 + u;
-                ml[u] = part_ml[pi];
-                po[u] = reinterpret_cast<const f32x4 *>(part_o + pi * D)[c4];
-            }
+        for (int u = 0; u < COMB_UNROLL; u++) {
+            // splits past the end read the last one and are dropped
+            const size_t pi = (size_t)row * nsplit + (s0 + u < nsplit ? s0 + u : nsplit - 1);
+            ml[u] = part_ml[pi];
+            po[u] = reinterpret_cast<const f32x4 *>(part_o + pi * D)[c4];
+        }
+        float Mn = M;
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; u++)
-            if (s0 + u < nsplit && ml[u].x != NEG_INF) {
-                const float f = __expf(ml[u].x - M);
-                Ls += ml[u].y * f;
-                acc = acc + po[u] * f;
+            if (s0 + u < nsplit) Mn = fmaxf(Mn, ml[u].x);
+        if (Mn != NEG_INF) {
+            if (M != NEG_INF && M != Mn) {
+                const float f = __expf(M - Mn);
+                Ls *= f;
+                acc = acc * f;
             }
+#pragma unroll
+            for (int u = 0; u < COMB_UNROLL; u++)
+                if (s0 + u < nsplit && ml[u].x != NEG_INF) {
+                    const float f = __expf(ml[u].x - Mn);
+                    Ls += ml[u].y * f;
+                    acc = acc + po[u] * f;
+                }
+            M = Mn;
+        }
     }
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    const size_t oi = ((size_t)bq * H + h) * D + 4 * c4;
+    const size_t oi = (size_t)row * D + 4 * c4;
     if (out_dt == CSA2_F32) {
         *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + oi) = acc * inv;
     } else {
