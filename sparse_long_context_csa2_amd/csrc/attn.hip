@@ -236,28 +236,43 @@ template <int NT, int SPLIT>
 __device__ SplitSel sel_split_in(const SelHandoff &sel, int bq, int e_begin, int ne, uint32_t *scratch, size_t cap,
                                  int32_t *jsh, uint32_t *red) {
     const int tid = threadIdx.x;
-    const SelTarget t = sel.sq[bq].t[0];
     const int64_t nwords = sel.nwords;
     const int64_t nw4 = (nwords + 3) & ~int64_t(3);
     uint32_t *bm = scratch;
     BandEntA *ent = reinterpret_cast<BandEntA *>(scratch + nw4);
+    const uint32_t *gbm = sel.bitmap + (size_t)bq * nwords;
+    const int32_t *list = sel.band + (size_t)bq * sel.band_cap;
+    const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
+    // One round of loads before anything waits: the first NT band entries
+    // (speculatively, before the count is known; past the capacity they read
+    // the last one), the bitmap (four words per load where the rows are
+    // 16-byte aligned) and the target record, which is used only after them.
+    const int32_t spec_i = tid < sel.band_cap ? tid : (int32_t)sel.band_cap - 1;
+    const int32_t sl0 = list[spec_i];
+    const double sc0 = bs[spec_i];
+    constexpr int U = 4;  // NT * U * 4 words per round
+    const bool vec = (nwords & 3) == 0;
+    const int64_t nq = nwords >> 2;
+    u32x4 v[U];
+    if (vec) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t qi = tid + (int64_t)NT * u;
+            v[u] = reinterpret_cast<const u32x4 *>(gbm)[qi < nq ? qi : nq - 1];
+        }
+    }
+    const SelTarget t = sel.sq[bq].t[0];
     SplitSel st;
     st.in_cnt = t.in_cnt;
     st.nb = t.band_cnt;
     st.in_lds = st.nb <= (int32_t)((cap - (size_t)nw4 * 4) / sizeof(BandEntA));
-    const uint32_t *gbm = sel.bitmap + (size_t)bq * nwords;
-    const int32_t *list = sel.band + (size_t)bq * sel.band_cap;
-    const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
-    // one round of loads: the first NT band entries (before the count is known)
-    // and the bitmap, four words per load where the rows are 16-byte aligned
-    const bool spec_ok = tid < sel.band_cap;
-    const int32_t sl0 = spec_ok ? list[tid] : 0;
-    const double sc0 = spec_ok ? bs[tid] : 0.0;
-    if ((nwords & 3) == 0) {
-        constexpr int U = 4;  // NT * U * 4 words per round
-        const int64_t nq = nwords >> 2;
-        for (int64_t q0 = 0; q0 < nq; q0 += (int64_t)NT * U) {
-            u32x4 v[U];
+    if (vec) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t qi = tid + (int64_t)NT * u;
+            if (qi < nq) reinterpret_cast<u32x4 *>(bm)[qi] = v[u];
+        }
+        for (int64_t q0 = (int64_t)NT * U; q0 < nq; q0 += (int64_t)NT * U) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int64_t qi = q0 + tid + (int64_t)NT * u;
