@@ -511,8 +511,8 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
                                                           int Q, int H, int64_t N, const int32_t *__restrict__ idx,
                                                           int k, float scale, int nsplit, int npairs,
                                                           uint16_t *__restrict__ out, float *__restrict__ lse,
-                                                          float *__restrict__ part_o, float2 *__restrict__ part_ml,
-                                                          SelHandoff sel) {
+                                                          uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml,
+                                                          float *__restrict__ part_sc, SelHandoff sel) {
     constexpr int NT = 64 * HB * DS;
     constexpr int KS = D / 32 / DS;  // contraction steps of S owned by this wave (its channel part)
     constexpr int SP = D >= 256 ? 4 : 2;  // channel parts of the S contraction, for every DS
@@ -707,22 +707,45 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
         if (lse && kg == 0 && dt0 == 0) lse[(size_t)bq * H + h] = l_run > 0.f ? m_run + logf(l_run) : NEG_INF;
     } else {
         const size_t pi = ((size_t)bq * H + h) * nsplit + split;  // a head's splits are adjacent
-        float *prow = part_o + pi * D + 16 * dt0 + 4 * kg;
+        // the partial row in fp16 under a power-of-two scale per quarter of the
+        // channels (this wave's part spans 4 / DS quarters): its largest
+        // magnitude lands in [2^14, 2^15), so every value keeps fp16's 11
+        // significant bits and none overflows
+        float mx = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4 *>(prow + 16 * dt) = o[dt];
+        for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) mx = fmaxf(mx, fabsf(o[dt][r]));
+        mx = bfly32(bfly16(mx, OpMax{}), OpMax{});
+        int ex = 0;
+        if (mx > 0.f && mx <= __FLT_MAX__) {
+            frexpf(mx, &ex);
+            ex = min(max(ex - 15, -120), 120);
+        }
+        const float down = ldexpf(1.f, -ex);
+        uint16_t *prow = part_o + pi * D + 16 * dt0 + 4 * kg;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+            *reinterpret_cast<uint2 *>(prow + 16 * dt) =
+                make_uint2(pack_f16_rne(o[dt][0] * down, o[dt][1] * down), pack_f16_rne(o[dt][2] * down, o[dt][3] * down));
+        if (kg == 0) {
+#pragma unroll
+            for (int qq = 0; qq < 4 / DS; qq++) part_sc[pi * 4 + dpart * (4 / DS) + qq] = ldexpf(1.f, ex);
+        }
         if (kg == 0 && dt0 == 0) part_ml[pi] = make_float2(m_run, l_run);
     }
 }
 
 // ----------------------------------------------------------- split merge
 // One thread per 4 channels of one head.  Up to COMB_UNROLL splits are read in
-// one round of loads (their maxima, sums and 4-channel partial rows), so the
-// merge waits for memory once; more splits take further rounds, the running
-// maximum rescaling what is already summed.
+// one round of loads (their maxima, sums, scales and 4-channel fp16 partial
+// rows), so the merge waits for memory once; more splits take further rounds,
+// the running maximum rescaling what is already summed.
 constexpr int COMB_UNROLL = 16;
 
-__global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ part_o,
-                                                      const float2 *__restrict__ part_ml, int BQ, int H, int D,
+__global__ __launch_bounds__(256) void k_attn_combine(const uint16_t *__restrict__ part_o,
+                                                      const float2 *__restrict__ part_ml,
+                                                      const float *__restrict__ part_sc, int BQ, int H, int D,
                                                       int nsplit, void *__restrict__ out, int out_dt,
                                                       float *__restrict__ lse) {
     const int tpr = D / 4;  // threads per head row
@@ -730,17 +753,20 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ 
     const int64_t row = gid / tpr;  // (bq, h)
     const int c4 = (int)(gid % tpr);
     if (row >= (int64_t)BQ * H) return;
+    const int quarter = 4 * c4 / (D / 4);  // the channels' scale slot
     float M = NEG_INF, Ls = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsplit; s0 += COMB_UNROLL) {
         float2 ml[COMB_UNROLL];
-        f32x4 po[COMB_UNROLL];
+        float sc[COMB_UNROLL];
+        uint2 ph[COMB_UNROLL];
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; u++) {
             // splits past the end read the last one and are dropped
             const size_t pi = (size_t)row * nsplit + (s0 + u < nsplit ? s0 + u : nsplit - 1);
             ml[u] = part_ml[pi];
-            po[u] = reinterpret_cast<const f32x4 *>(part_o + pi * D)[c4];
+            sc[u] = part_sc[pi * 4 + quarter];
+            ph[u] = reinterpret_cast<const uint2 *>(part_o + pi * D)[c4];
         }
         float Mn = M;
 #pragma unroll
@@ -757,7 +783,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ 
                 if (s0 + u < nsplit && ml[u].x != NEG_INF) {
                     const float f = __expf(ml[u].x - Mn);
                     Ls += ml[u].y * f;
-                    acc = acc + po[u] * f;
+                    const f16x2 a = __builtin_bit_cast(f16x2, ph[u].x), b = __builtin_bit_cast(f16x2, ph[u].y);
+                    const f32x4 po = {(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+                    acc = acc + po * (f * sc[u]);
                 }
             M = Mn;
         }
@@ -844,7 +872,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
 // heads per block as that allows, so that fewer blocks gather the same rows.
 template <int D, int FMT, int HB, int SPLIT>
 void launch_mfma_hb(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                    float *lse, float *part_o, float2 *part_ml, hipStream_t s, const SelHandoff *sel) {
+                    float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s, const SelHandoff *sel) {
     // two or more waves per head group (each owns a share of the channels)
     // while that stays within 512 threads
     constexpr int DS = HB == 1 ? (D >= 256 ? 4 : 2) : ((HB <= 4 && D >= 128) ? 2 : 1);
@@ -854,33 +882,33 @@ void launch_mfma_hb(const AttnPlan &p, const void *q, const void *kv, const int3
     if (sel)
         hipLaunchKernelGGL((k_attn_mfma<D, FMT, HB, DS, SPLIT, true>), dim3(blocks), dim3(64 * HB * DS), 0, s,
                            static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,
-                           scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, *sel);
+                           scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, part_sc, *sel);
     else
         hipLaunchKernelGGL((k_attn_mfma<D, FMT, HB, DS, SPLIT, false>), dim3(blocks), dim3(64 * HB * DS), 0, s,
                            static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,
-                           scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, SelHandoff{});
+                           scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, part_sc, SelHandoff{});
 }
 
 template <int D, int FMT, int SPLIT>
 void launch_mfma_split(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                       float *lse, float *part_o, float2 *part_ml, hipStream_t s, const SelHandoff *sel) {
+                       float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s, const SelHandoff *sel) {
     const int64_t pairs = (int64_t)p.B * p.Q * p.nsplit;
     const int hgroups = p.H / 16;
     int hb = hgroups;  // head groups per block
     while (hb > 1 && pairs * (hgroups / hb) < 256) hb /= 2;
     switch (hb) {
-        case 1: launch_mfma_hb<D, FMT, 1, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); break;
-        case 2: launch_mfma_hb<D, FMT, 2, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); break;
-        case 4: launch_mfma_hb<D, FMT, 4, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); break;
-        case 8: launch_mfma_hb<D, FMT, 8, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); break;
+        case 1: launch_mfma_hb<D, FMT, 1, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); break;
+        case 2: launch_mfma_hb<D, FMT, 2, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); break;
+        case 4: launch_mfma_hb<D, FMT, 4, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); break;
+        case 8: launch_mfma_hb<D, FMT, 8, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); break;
         default: throw Error(CSA2_EUNSUPPORTED, "matrix-core attention needs H in {16, 32, 64, 128}");
     }
 }
 
 template <int D, int FMT>
 void launch_mfma(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                 float *lse, float *part_o, float2 *part_ml, hipStream_t s, const SelHandoff *sel) {
-    launch_mfma_split<D, FMT, ATT_SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel);
+                 float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s, const SelHandoff *sel) {
+    launch_mfma_split<D, FMT, ATT_SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel);
 }
 
 }  // namespace
@@ -898,8 +926,9 @@ bool attn_supported(const AttnPlan &p) { return p.mfma || (p.D + p.k) <= 16384; 
 size_t attn_workspace(const AttnPlan &p) {
     if (!p.mfma || p.nsplit == 1) return 0;
     Carve c(nullptr, 0);
-    c.take<float>((size_t)p.B * p.Q * p.nsplit * p.H * p.D);
+    c.take<uint16_t>((size_t)p.B * p.Q * p.nsplit * p.H * p.D);
     c.take<float2>((size_t)p.B * p.Q * p.nsplit * p.H);
+    c.take<float>((size_t)p.B * p.Q * p.nsplit * p.H * 4);
     return c.used;
 }
 
@@ -918,18 +947,20 @@ void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *i
         check_launch("attention (vector)");
         return;
     }
-    float *part_o = nullptr;
+    uint16_t *part_o = nullptr;
     float2 *part_ml = nullptr;
+    float *part_sc = nullptr;
     if (p.nsplit > 1) {
         Carve c(ws, ws_bytes);
-        part_o = c.take<float>((size_t)BQ * p.nsplit * p.H * p.D);
+        part_o = c.take<uint16_t>((size_t)BQ * p.nsplit * p.H * p.D);
         part_ml = c.take<float2>((size_t)BQ * p.nsplit * p.H);
+        part_sc = c.take<float>((size_t)BQ * p.nsplit * p.H * 4);
         if (c.used > ws_bytes) throw Error(CSA2_EWORKSPACE, "attention workspace too small");
     }
 #define CSA2_ATT_CASE(d)                                                                             \
     case d:                                                                                          \
-        if (p.kv_dt == CSA2_FP4) launch_mfma<d, CSA2_FP4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel); \
-        else launch_mfma<d, CSA2_BF16>(p, q, kv, idx, scale, out, lse, part_o, part_ml, s, sel);                   \
+        if (p.kv_dt == CSA2_FP4) launch_mfma<d, CSA2_FP4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); \
+        else launch_mfma<d, CSA2_BF16>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel);                   \
         break;
     switch (p.D) {
         CSA2_ATT_CASE(64)
@@ -941,7 +972,7 @@ void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *i
     check_launch("attention");
     if (p.nsplit > 1) {
         const int64_t threads = (int64_t)BQ * p.H * (p.D / 4);
-        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part_o, part_ml,
+        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part_o, part_ml, part_sc,
                            BQ, p.H, p.D, p.nsplit, out, p.q_dt, lse);
         check_launch("attention combine");
     }
