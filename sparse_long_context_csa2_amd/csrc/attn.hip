@@ -91,6 +91,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // of 4 consecutive rows.
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef float __attribute__((ext_vector_type(2))) f32x2;
+typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2v;  // converted to with round-to-nearest-even
 typedef _Float16 __attribute__((ext_vector_type(2))) f16x2;
 
 // FP4 chunk (32 channels: 16 code bytes) with the two E4M3 scales of its
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
     using G = TileGather<D, FMT>;
     constexpr int PER = (G::CHUNKS + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][ATT_SUB * LS];
-    __shared__ int32_t jsh[SPLIT];
+    __shared__ __attribute__((aligned(16))) int32_t jsh[SPLIT];
     // partial logits of each wave's channel part, summed over the head group's DS waves
     __shared__ __attribute__((aligned(16))) f32x4 spart[DS > 1 ? 64 * HB * DS * 2 : 1];
 
@@ -647,11 +649,14 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
         // ---- online softmax for head col; this lane holds entries 16 h2 + 4 kg + i
         float a[8];
         float mt = NEG_INF;
+        // this lane's 8 entries (16 h2 + 4 kg + i): -1 marks an empty one
+        const int4 jv[2] = {*reinterpret_cast<const int4 *>(jt + 4 * kg), *reinterpret_cast<const int4 *>(jt + 16 + 4 * kg)};
 #pragma unroll
         for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const float v = jt[h2 * 16 + 4 * kg + i] >= 0 ? st[h2][i] * qscale : NEG_INF;
+                const int jj = i == 0 ? jv[h2].x : i == 1 ? jv[h2].y : i == 2 ? jv[h2].z : jv[h2].w;
+                const float v = jj >= 0 ? st[h2][i] * qscale : NEG_INF;
                 a[h2 * 4 + i] = v;
                 mt = fmaxf(mt, v);
             }
@@ -666,7 +671,7 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
             const float p1 = a[x + 1] == NEG_INF ? 0.f : __expf(a[x + 1] - m_new);
             psum += p0 + p1;
             if constexpr (FMT == CSA2_FP4) pk[x / 2] = pack_f16_rne(p0, p1);
-            else pk[x / 2] = uint32_t(f32_to_bf16_rne(p0)) | (uint32_t(f32_to_bf16_rne(p1)) << 16);
+            else pk[x / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2v));
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
