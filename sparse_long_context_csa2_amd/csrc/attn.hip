@@ -195,7 +195,8 @@ __device__ __forceinline__ void gather_store(uint16_t *T, const u32x4 *buf, cons
 // the band until sel_split_idx returns.
 struct BandEntA {
     uint64_t key;
-    int32_t slot, pad;
+    int32_t slot;
+    uint32_t nslot;  // ~slot: ascending slot order as descending unsigned order
 };
 
 struct SplitSel {
@@ -295,14 +296,14 @@ __device__ SplitSel sel_split_in(const SelHandoff &sel, int bq, int e_begin, int
             BandEntA e;
             e.key = dkey(sc0);
             e.slot = sl0;
-            e.pad = 0;
+            e.nslot = ~(uint32_t)e.slot;
             ent[tid] = e;
         }
         for (int32_t i = tid + NT; i < st.nb; i += NT) {
             BandEntA e;
             e.key = dkey(bs[i]);
             e.slot = list[i];
-            e.pad = 0;
+            e.nslot = ~(uint32_t)e.slot;
             ent[i] = e;
         }
     }
@@ -334,7 +335,7 @@ __device__ SplitSel sel_split_in(const SelHandoff &sel, int bq, int e_begin, int
 // fly during the ranking.  Ends with jsh complete.
 template <int NT, int SPLIT, class Issue>
 __device__ void sel_split_band(const SelHandoff &sel, int bq, int K, const SplitSel &st, int e_begin, int ne,
-                               uint32_t *scratch, int32_t *jsh, Issue &&issue) {
+                               uint32_t *scratch, size_t cap, int32_t *jsh, Issue &&issue) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t nw4 = (sel.nwords + 3) & ~int64_t(3);
     uint32_t *bm = scratch;
@@ -348,61 +349,74 @@ __device__ void sel_split_band(const SelHandoff &sel, int bq, int K, const Split
         const int32_t p = st.in_cnt + rk - e_begin;
         if (p >= 0 && p < ne) jsh[p] = sel_entry(sel, bq, si);
     };
-    if (r > 0 && nb > 0 && st.in_lds && nb <= NT) {
-        // every wave holds all nb entries in registers (lane l of chunk c: entry
-        // 64 c + l) and ranks the entries i = wave + NW t, four per step: entry
-        // i's key and slot are read out of lane t, each chunk's comparisons
-        // give lane masks, the rank is the sum of their populations
+    if (r > 0 && nb > 0 && st.in_lds && nb <= NT &&
+        (size_t)(nw4 + 4 * nb) * 4 + (size_t)(NT / 64) * NT * 4 <= cap) {
+        // Lane l of chunk c holds entry i = 64 c + l; wave w takes its share of
+        // the partners j, read from LDS as broadcasts.  j is ahead of i iff
+        // (key_j, ~slot_j) > (key_i, ~slot_i) as 96-bit unsigned numbers, i.e.
+        // iff the subtraction (key_i, ~slot_i) - (key_j, ~slot_j) borrows: three
+        // chained subtractions and an add of the borrow, all on the vector
+        // unit.  The waves' counts meet in LDS and thread i sums them.
         constexpr int NW = NT / 64;
         constexpr int MAXC = NT / 64;
+        uint32_t *rkp = scratch + nw4 + 4 * nb;
         const int nch = (nb + 63) / 64;
-        u32x4 jc[MAXC];
+        u32x4 ic[MAXC];
 #pragma unroll
         for (int c = 0; c < MAXC; c++) {
-            const int j = 64 * c + lane;
-            jc[c] = c < nch ? ent4[j < nb ? j : 0] : u32x4{0u, 0u, 0u, 0u};
+            const int i = 64 * c + lane;
+            ic[c] = c < nch ? ent4[i < nb ? i : 0] : u32x4{0u, 0u, 0u, 0u};
         }
-        uint64_t vmask[MAXC];  // lanes of chunk c that hold an entry
+        const bool act = tid < nb;
+        const u32x4 me = ent4[act ? tid : 0];
+        const int32_t my_e = sel_entry(sel, bq, (int32_t)me[2]);  // before the row loads
+        issue();  // global loads go out after these LDS reads
+        uint32_t rk[MAXC];
 #pragma unroll
-        for (int c = 0; c < MAXC; c++) vmask[c] = __ballot(64 * c + lane < nb);
-        const int ni = (nb - wave + NW - 1) / NW;  // <= 64 since nb <= NT
-        const u32x4 mine = ent4[lane < ni ? wave + NW * lane : 0];
-        const int32_t mine_e = sel_entry(sel, bq, (int32_t)mine[2]);  // before the row loads
-        issue();  // global loads go out after the LDS reads of the ranking
-        uint32_t myrank = 0;
-        for (int t0 = 0; t0 < ni; t0 += 4) {
-            uint64_t ki[4];
-            uint32_t si[4], cnt[4];
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const int tt = t0 + u < ni ? t0 + u : ni - 1;
-                ki[u] = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mine[0], tt) |
-                        ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mine[1], tt) << 32);
-                si[u] = (uint32_t)__builtin_amdgcn_readlane((int)mine[2], tt);
-                cnt[u] = 0;
-            }
+        for (int c = 0; c < MAXC; c++) rk[c] = 0;
+        const int jper = (nb + NW - 1) / NW;
+        const int j0 = __builtin_amdgcn_readfirstlane(wave * jper);
+        const int j1 = __builtin_amdgcn_readfirstlane(min(nb, j0 + jper));
+        // (key lo, key hi, slot, ~slot) of partner j against every chunk
+        auto count = [&](const u32x4 &o) {
 #pragma unroll
             for (int c = 0; c < MAXC; c++) {
                 if (c < nch) {
-                    const uint64_t kj = (uint64_t)jc[c][0] | ((uint64_t)jc[c][1] << 32);
-#pragma unroll
-                    for (int u = 0; u < 4; u++) {
-                        // key greater, or equal with a lower slot
-                        const uint64_t gt = __builtin_amdgcn_uicmpl(kj, ki[u], 34);       // unsigned >
-                        const uint64_t eq = __builtin_amdgcn_uicmpl(kj, ki[u], 32);       // ==
-                        const uint64_t lt = __builtin_amdgcn_uicmp(jc[c][2], si[u], 36);  // unsigned <
-                        cnt[u] += (uint32_t)__builtin_popcountll((gt | (eq & lt)) & vmask[c]);
-                    }
+                    uint32_t d;
+                    asm volatile(
+                        "v_sub_co_u32 %0, vcc, %2, %3\n\t"
+                        "v_subb_co_u32 %0, vcc, %4, %5, vcc\n\t"
+                        "v_subb_co_u32 %0, vcc, %6, %7, vcc\n\t"
+                        "v_addc_co_u32 %1, vcc, 0, %1, vcc"
+                        : "=&v"(d), "+v"(rk[c])
+                        : "v"(ic[c][3]), "v"(o[3]), "v"(ic[c][0]), "v"(o[0]), "v"(ic[c][1]), "v"(o[1])
+                        : "vcc");
                 }
             }
+        };
+        int j = j0;
+        for (; j + 4 <= j1; j += 4) {
+            u32x4 o[4];
 #pragma unroll
-            for (int u = 0; u < 4; u++) myrank = lane == t0 + u ? cnt[u] : myrank;
+            for (int u = 0; u < 4; u++) o[u] = ent4[j + u];
+#pragma unroll
+            for (int u = 0; u < 4; u++) count(o[u]);
         }
-        if (lane < ni && myrank < (uint32_t)r) {
-            const int32_t si = (int32_t)mine[2];
-            atomicOr(&bm[si >> 5], 1u << (si & 31));
-            const int32_t p = st.in_cnt + (int32_t)myrank - e_begin;
-            if (p >= 0 && p < ne) jsh[p] = mine_e;
+        for (; j < j1; j++) count(ent4[j]);
+#pragma unroll
+        for (int c = 0; c < MAXC; c++)
+            if (c < nch) rkp[wave * NT + 64 * c + lane] = rk[c];
+        __syncthreads();
+        if (act) {
+            uint32_t rank = 0;
+#pragma unroll
+            for (int w = 0; w < NW; w++) rank += rkp[w * NT + tid];
+            if (rank < (uint32_t)r) {
+                const int32_t si = (int32_t)me[2];
+                atomicOr(&bm[si >> 5], 1u << (si & 31));
+                const int32_t p = st.in_cnt + (int32_t)rank - e_begin;
+                if (p >= 0 && p < ne) jsh[p] = my_e;
+            }
         }
     } else if (r > 0 && nb > 0) {
         // entry i is ranked by P consecutive lanes, each comparing a 1/P share
@@ -566,7 +580,7 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
         const bool early = e_begin + min(ATT_SUB, ne) <= st.in_cnt;
         // (issued unconditionally: a branch around the loads would make later
         // waits for other loads wait for these too; reissued below if not early)
-        sel_split_band<NT, SPLIT>(sel, bq, k, st, e_begin, ne, scr, jsh,
+        sel_split_band<NT, SPLIT>(sel, bq, k, st, e_begin, ne, scr, sizeof(tile), jsh,
                                   [&]() { gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf); });
         sel_split_idx<NT>(sel, bq, k, e_begin, ne, split == 0, scr, sred);
         if (!early) gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf);
