@@ -159,6 +159,27 @@ def test_sparse_attn_matches_oracle(b, B, Q, H, D, N, k, fmt, pad):
     assert_close(lse, rl, atol, rtol, "lse")
 
 
+@pytest.mark.parametrize("e", [24, -24])
+def test_sparse_attn_split_partials_extreme_magnitudes(b, e):
+    """Outputs of magnitude 2^e merged from 16 splits: the split partials are
+    kept in fp16 under a power-of-two scale per quarter of the channels, which
+    must follow the values up to 2^24 and down to 2^-24 without overflow or
+    loss.  The KV rows are scaled by 2^e and the queries by 2^-e, so the
+    logits, and the reference up to the factor 2^e, are the unscaled ones."""
+    rng = np.random.default_rng(23)
+    B, H, D, N, k = 1, 64, 512, 3000, 2048
+    f = 2.0 ** e
+    kv = (synth.normal_bf16(rng, (B, N, D)).float() * f).to(torch.bfloat16)
+    q = (synth.normal_bf16(rng, (B, 1, H, D)).float() / f).to(torch.bfloat16)
+    idx = _idx(rng, B, 1, N, k, 0)
+    scale = 1 / math.sqrt(D)
+    out, lse = b.sparse_attn(dev(q), dev(kv), dev(idx), scale, D=D)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attn(q, kv, idx, scale, D=D)
+    assert_close(host(out).double() / f, np.asarray(ro) / f, ATOL_BF16, RTOL_BF16, "attention output / 2^e")
+    assert_close(lse, rl, ATOL_BF16, RTOL_BF16, "lse")
+
+
 def test_sparse_attn_empty_rows_and_batch_invariance(b):
     rng = np.random.default_rng(11)
     B, H, D, N, k = 16, 64, 512, 700, 1100
