@@ -106,6 +106,10 @@ class Decode:
     P: int = 0
     seed: int = 0
     layers: list = field(default_factory=lambda: ["FULL"])
+    k_reindex: int = 0  # top-k of the Reindex layers (0: the same k as the Full layer)
+
+    def layer_k(self, mode: str) -> int:
+        return self.k_reindex if mode == "REINDEX" and self.k_reindex > 0 else self.k
 
     @property
     def scale(self) -> float:
@@ -161,6 +165,24 @@ def decode_1m_hier(seed: int = 3, B: int = 4, N: int = 262144, P: int = 16384) -
     only the pool; FP4 main KV, 64 heads x 512."""
     return Decode(B=B, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=2048, kv_fmt="fp4", P=P, seed=seed,
                   layers=["FULL"] + ["REINDEX"] * 3)
+
+
+def v41_decoder_schedule(seed: int = 4, B: int = 1, N: int = 1048576, P: int = 16384, k: int = 2048,
+                         k_reindex: int = 512) -> Decode:
+    """V4.1's decoder schedule with one persistent pool: 1 Full + 3 Reuse, then 4
+    groups of 1 Reindex + 3 Reuse; the decoder keeps every token (m = 1), so a
+    1M-token context is N = 1,048,576 entries; the Full layer picks a 16,384-position
+    pool and its top-2048, each Reindex layer its top-512 inside the pool; FP4 main KV."""
+    return Decode(B=B, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=k, kv_fmt="fp4", m=1, P=P, seed=seed,
+                  k_reindex=k_reindex,
+                  layers=["FULL"] + ["REUSE"] * 3 + (["REINDEX"] + ["REUSE"] * 3) * 4)
+
+
+def v41_encoder_schedule(seed: int = 5, B: int = 1, N: int = 524288, k: int = 2048) -> Decode:
+    """V4.1's encoder schedule: 3 groups of 1 Full + 5 Reuse layers at m = 2
+    (a 1M-token context is N = 524,288 entries); FP4 main KV."""
+    return Decode(B=B, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=k, kv_fmt="fp4", m=2, seed=seed,
+                  layers=(["FULL"] + ["REUSE"] * 5) * 3)
 
 
 @dataclass

@@ -49,8 +49,11 @@ def run_group(b, d, q_pos=None):
     atol, rtol = (ATOL_F32, RTOL_F32) if spec.kv_fmt == "f32" else (ATOL_BF16, RTOL_BF16)
     for li, lay in enumerate(d["layers"]):
         mode = lay["mode"]
-        kw = dict(q=dev(lay["q"]), kv=kv, k=spec.k, scale=spec.scale)
-        rkw = dict(q=lay["q"], kv=d["kv"], k=spec.k, scale=spec.scale)
+        k = spec.layer_k(mode)
+        if mode == "REUSE" and g_idx is not None:
+            k = g_idx.shape[-1]  # a Reuse layer takes the previous selection as it is
+        kw = dict(q=dev(lay["q"]), kv=kv, k=k, scale=spec.scale)
+        rkw = dict(q=lay["q"], kv=d["kv"], k=k, scale=spec.scale)
         if mode in ("FULL", "REINDEX"):
             kw.update(qI=dev(lay["qI"]), w=dev(lay["w"]), kI=kI, q_pos=dev(q_pos), m=spec.m)
             rkw.update(qI=lay["qI"], w=lay["w"], kI=d["kI"], q_pos=q_pos, m=spec.m)

@@ -6,6 +6,8 @@
 * 128K-token decode with FP4 KV: one Full layer and five Reuse layers.
 * 1M-token decode (4 x 262,144 entries): Full layer with its 16,384-entry pool,
   then three Reindex layers inside the pool.
+* V4.1's decoder schedule at a 1M-token context (m = 1): 1 Full + 3 Reuse,
+  then 4 x (1 Reindex + 3 Reuse) around one persistent pool.
 * Prefill chunk (4,096 causal queries at the end of a 65,536-token context):
   compression of the whole context on the GPU, then one Full layer over all
   4,096 rows; 64 rows (first and last included) compared with the oracle, and
@@ -65,6 +67,13 @@ def test_decode_128k_fp4_full_plus_five_reuse(b):
 
 def test_decode_1m_pool_and_three_reindex(b):
     run_group(b, synth.make_decode(synth.decode_1m_hier(seed=3)))
+
+
+def test_v41_decoder_schedule_1m(b):
+    """The decoder's 20 layers at a 1M-token context with m = 1 (1,048,576
+    entries): Full picks the 16,384-position pool and its top-2048, each of
+    the 4 Reindex layers its top-512 inside the pool, Reuse layers attend."""
+    run_group(b, synth.make_decode(synth.v41_decoder_schedule(seed=4)))
 
 
 def test_prefill_chunk_sampled_rows(b):

@@ -35,6 +35,17 @@ def test_hierarchical_full_pool_plus_reindex_reduced(b):
     run_group(b, synth.make_decode(spec))
 
 
+def test_v41_decoder_schedule_reduced(b):
+    """V4.1's decoder schedule (1 Full + 3 Reuse, then 4 x (1 Reindex + 3 Reuse),
+    one persistent pool, m = 1, Reindex top-k below the Full layer's), scaled down."""
+    run_group(b, synth.make_decode(synth.v41_decoder_schedule(seed=4, B=2, N=9000, P=2048, k=512, k_reindex=128)))
+
+
+def test_v41_encoder_schedule_reduced(b):
+    """V4.1's encoder schedule (3 x (1 Full + 5 Reuse) at m = 2), scaled down."""
+    run_group(b, synth.make_decode(synth.v41_encoder_schedule(seed=5, B=2, N=4500, k=512)))
+
+
 def test_causal_queries_reduced(b):
     spec = synth.Decode(B=1, Q=6, N=3000, HI=64, dI=128, H=16, D=128, k=256, P=1024, seed=5,
                         layers=["FULL", "REINDEX", "REUSE"])
