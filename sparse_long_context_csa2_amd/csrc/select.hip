@@ -120,53 +120,79 @@ __global__ __launch_bounds__(256) void k_sel_stats(const float *__restrict__ sco
     }
 }
 
-// ---------------------------------------------------------------- 1: hist
-__global__ __launch_bounds__(256) void k_sel_hist(const float *__restrict__ scores, const int32_t *__restrict__ cand,
-                                                  int64_t n, const TileStat *__restrict__ stats, int ntiles,
-                                                  int nchunks, uint32_t *__restrict__ part, SelQuery *__restrict__ sq) {
-    __shared__ uint32_t hist[NB];
-    __shared__ float r_min[256], r_max[256];
-    __shared__ uint32_t r_n[256];
-    const int bq = blockIdx.y, chunk = blockIdx.x;
-    // range of the query's finite scores (fixed reduction order)
+// ---------------------------------------------------------------- 1: range
+// Per query: the finite scores' range [lo, hi] and count from the tile
+// statistics, the bin() parameters into the query record, and the query's
+// histogram cleared for the chunks' counts.
+__global__ __launch_bounds__(256) void k_sel_range(const TileStat *__restrict__ stats, int ntiles,
+                                                   SelQuery *__restrict__ sq, uint32_t *__restrict__ qhist) {
+    __shared__ float r_min[4], r_max[4];
+    __shared__ uint32_t r_n[4];
+    const int bq = blockIdx.x, wave = threadIdx.x >> 6;
     float mn = POS_INF, mx = NEG_INF;
     uint32_t cnt = 0;
     for (int t = threadIdx.x; t < ntiles; t += 256) {
-        TileStat s = stats[(size_t)bq * ntiles + t];
-        mn = fminf(mn, s.smin);
-        mx = fmaxf(mx, s.smax);
-        cnt += s.nvalid;
+        const TileStat st = stats[(size_t)bq * ntiles + t];
+        mn = fminf(mn, st.smin);
+        mx = fmaxf(mx, st.smax);
+        cnt += st.nvalid;
     }
-    r_min[threadIdx.x] = mn;
-    r_max[threadIdx.x] = mx;
-    r_n[threadIdx.x] = cnt;
-    for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    cnt = wave_sum_u32(cnt);
+    if ((threadIdx.x & 63) == 0) {
+        r_min[wave] = mn;
+        r_max[wave] = mx;
+        r_n[wave] = cnt;
+    }
+    for (int i = threadIdx.x; i < NB; i += 256) qhist[(size_t)bq * NB + i] = 0;
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (threadIdx.x < o) {
-            r_min[threadIdx.x] = fminf(r_min[threadIdx.x], r_min[threadIdx.x + o]);
-            r_max[threadIdx.x] = fmaxf(r_max[threadIdx.x], r_max[threadIdx.x + o]);
-            r_n[threadIdx.x] += r_n[threadIdx.x + o];
-        }
-        __syncthreads();
-    }
-    const float lo = r_min[0], hi = r_max[0];
-    const float span = hi - lo;
-    const float inv = (r_n[0] > 0 && span > 0.f) ? (float)NB / span : 0.f;
-    if (chunk == 0 && threadIdx.x == 0) {
+    if (threadIdx.x == 0) {
+        const float lo = fminf(fminf(r_min[0], r_min[1]), fminf(r_min[2], r_min[3]));
+        const float hi = fmaxf(fmaxf(r_max[0], r_max[1]), fmaxf(r_max[2], r_max[3]));
+        const uint32_t nv = r_n[0] + r_n[1] + r_n[2] + r_n[3];
+        const float span = hi - lo;
         sq[bq].lo = lo;
-        sq[bq].inv = inv;
-        sq[bq].nvalid = (int32_t)r_n[0];
+        sq[bq].inv = (nv > 0 && span > 0.f) ? (float)NB / span : 0.f;
+        sq[bq].nvalid = (int32_t)nv;
     }
+}
+
+// ---------------------------------------------------------------- 2: hist
+// Each 8192-slot chunk counts its scores' bins in LDS (slot CH c + t + 256 i
+// in thread t: coalesced loads, all in flight before the counting) and adds
+// its nonzero bins to the query's histogram.
+__global__ __launch_bounds__(256) void k_sel_hist(const float *__restrict__ scores, const int32_t *__restrict__ cand,
+                                                  int64_t n, const SelQuery *__restrict__ sq,
+                                                  uint32_t *__restrict__ qhist) {
+    __shared__ uint32_t hist[NB];
+    const int bq = blockIdx.y, chunk = blockIdx.x;
+    for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
+    const float lo = sq[bq].lo, inv = sq[bq].inv;
     const int64_t base = (int64_t)bq * n;
-    const int64_t s0 = (int64_t)chunk * CH + threadIdx.x * 32;
-    for (int i = 0; i < 32; i++) {
-        float v;
-        if (slot_score(scores, cand, base, s0 + i, n, v)) atomicAdd(&hist[sel_bin(v, lo, inv)], 1u);
+    const int64_t s0 = (int64_t)chunk * CH + threadIdx.x;
+    float v[CH / 256];
+#pragma unroll
+    for (int i = 0; i < CH / 256; i++) {
+        const int64_t sl = s0 + 256 * i;
+        v[i] = sl < n ? scores[base + sl] : NEG_INF;
+    }
+    if (cand) {
+#pragma unroll
+        for (int i = 0; i < CH / 256; i++) {
+            const int64_t sl = s0 + 256 * i;
+            if (sl < n && cand[base + sl] < 0) v[i] = NEG_INF;
+        }
     }
     __syncthreads();
-    uint32_t *dst = part + ((size_t)bq * nchunks + chunk) * NB;
-    for (int i = threadIdx.x; i < NB; i += 256) dst[i] = hist[i];
+#pragma unroll
+    for (int i = 0; i < CH / 256; i++)
+        if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
+    __syncthreads();
+    for (int i = threadIdx.x; i < NB; i += 256) {
+        const uint32_t c = hist[i];
+        if (c) atomicAdd(&qhist[(size_t)bq * NB + i], c);
+    }
 }
 
 __device__ __forceinline__ double thr_lo(float a, double E) {
@@ -178,21 +204,19 @@ __device__ __forceinline__ double thr_hi(float z, double E) {
     return (double)z;
 }
 
-// ---------------------------------------------------------------- 2: find
-__global__ __launch_bounds__(256) void k_sel_find(const uint32_t *__restrict__ part, int nchunks, int K0, int K1,
+// ---------------------------------------------------------------- 3: find
+__global__ __launch_bounds__(256) void k_sel_find(const uint32_t *__restrict__ qhist, int K0, int K1,
                                                   const double *__restrict__ ebound, SelQuery *__restrict__ sq) {
     __shared__ uint32_t cum[NB + 1];
     __shared__ int bstar;
     const int bq = blockIdx.x;
-    // per-thread 8 consecutive bins, summed over chunks
+    // per-thread 8 consecutive bins of the query's histogram
     uint32_t h[8];
     uint32_t local = 0;
+#pragma unroll
     for (int i = 0; i < 8; i++) {
-        uint32_t acc = 0;
-        int b = threadIdx.x * 8 + i;
-        for (int c = 0; c < nchunks; c++) acc += part[((size_t)bq * nchunks + c) * NB + b];
-        h[i] = acc;
-        local += acc;
+        h[i] = qhist[(size_t)bq * NB + threadIdx.x * 8 + i];
+        local += h[i];
     }
     // suffix sums: cum[b] = number of finite scores in bins >= b
     __shared__ uint32_t tot[256];
@@ -260,56 +284,7 @@ __global__ __launch_bounds__(256) void k_sel_find(const uint32_t *__restrict__ p
     }
 }
 
-// ------------------------------------------------------------ 3: classify
-__global__ __launch_bounds__(256) void k_sel_classify(const float *__restrict__ scores,
-                                                      const int32_t *__restrict__ cand, int64_t n, int ntgt,
-                                                      SelQuery *__restrict__ sq, uint32_t *__restrict__ bitmap,
-                                                      int64_t nwords, int32_t *__restrict__ band, int64_t band_cap) {
-    __shared__ uint32_t buf[8];
-    __shared__ uint32_t base_sh;
-    const int bq = blockIdx.y;
-    const int64_t word = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t base = (int64_t)bq * n;
-    float v[32];
-    uint32_t okmask = 0;
-    for (int i = 0; i < 32; i++) {
-        float x = 0.f;
-        if (slot_score(scores, cand, base, word * 32 + i, n, x)) okmask |= 1u << i;
-        v[i] = x;
-    }
-    for (int tgt = 0; tgt < ntgt; tgt++) {
-        const SelTarget t = sq[bq].t[tgt];
-        uint32_t in = 0, bandm = 0;
-        for (int i = 0; i < 32; i++) {
-            if (!((okmask >> i) & 1u)) continue;
-            double x = (double)v[i];
-            if (x > t.hi) in |= 1u << i;
-            else if (x >= t.lo) bandm |= 1u << i;
-        }
-        if (word < nwords) bitmap[((size_t)tgt * gridDim.y + bq) * nwords + word] = in;
-        uint32_t nin = block_sum_u32<256>((uint32_t)__builtin_popcount(in), buf);
-        if (threadIdx.x == 0 && nin) atomicAdd(&sq[bq].t[tgt].in_cnt, (int32_t)nin);
-        uint32_t nb = (uint32_t)__builtin_popcount(bandm), tot;
-        uint32_t off = block_excl_scan<256>(nb, buf, tot);
-        if (threadIdx.x == 0) base_sh = tot ? (uint32_t)atomicAdd(&sq[bq].t[tgt].band_cnt, (int32_t)tot) : 0u;
-        __syncthreads();
-        int32_t *dst = band + ((size_t)tgt * gridDim.y + bq) * band_cap;
-        uint32_t pos = base_sh + off;
-        while (bandm) {
-            int i = __builtin_ctz(bandm);
-            bandm &= bandm - 1;
-            dst[pos++] = (int32_t)(word * 32 + i);
-        }
-        __syncthreads();
-    }
-}
-
-// ------------------------------------------------- shared finishing steps
-
-__device__ __forceinline__ uint32_t load_word(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+// ------------------------------------------------------------ 4: classify
 // Largest float <= d and smallest float >= d (d finite or -inf).
 __device__ __forceinline__ float f32_down(double d) {
     float f = (float)d;
@@ -321,6 +296,106 @@ __device__ __forceinline__ float f32_up(double d) {
     if ((double)f < d) f = nextafterf(f, POS_INF);
     return f;
 }
+
+// A block takes CLS_WPT x 256 consecutive bitmap words; thread t holds words
+// w0 + t + 256 u (slots 32 w .. 32 w + 31, with 16-byte loads where a word is
+// whole), so its comparisons against the thresholds are those words' IN and
+// BAND bits.  Thresholds are the binary64 bounds rounded outward to floats.
+// The counts meet per block first and reach the query record with one atomic
+// update per block and target: the records are shared by every block of a
+// query, and per-wave updates of one address queue up.
+constexpr int CLS_WPT = 4;
+
+__device__ __forceinline__ void load_word_scores(const float *sp, const int32_t *cp, int64_t s0, int64_t n,
+                                                 float *v) {
+    if (s0 + 32 <= n && ((reinterpret_cast<uintptr_t>(sp) | reinterpret_cast<uintptr_t>(cp)) & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4 *>(sp + s0 + i);
+            v[i] = q4[0], v[i + 1] = q4[1], v[i + 2] = q4[2], v[i + 3] = q4[3];
+        }
+        if (cp) {
+#pragma unroll
+            for (int i = 0; i < 32; i += 4) {
+                const u32x4 c4 = *reinterpret_cast<const u32x4 *>(cp + s0 + i);
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    if ((int32_t)c4[e] < 0) v[i + e] = NEG_INF;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const int64_t sl = s0 + i;
+            v[i] = sl < n ? sp[sl] : NEG_INF;
+            if (cp && sl < n && cp[sl] < 0) v[i] = NEG_INF;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_sel_classify(const float *__restrict__ scores,
+                                                      const int32_t *__restrict__ cand, int64_t n, int ntgt,
+                                                      SelQuery *__restrict__ sq, uint32_t *__restrict__ bitmap,
+                                                      int64_t nwords, int32_t *__restrict__ band, int64_t band_cap) {
+    __shared__ uint32_t w_in[4], w_nb[4];
+    __shared__ int32_t base_sh;
+    const int bq = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t wbase0 = (int64_t)blockIdx.x * (256 * CLS_WPT) + threadIdx.x;
+    const float *sp = scores + (int64_t)bq * n;
+    const int32_t *cp = cand ? cand + (int64_t)bq * n : nullptr;
+    float v[CLS_WPT][32];
+#pragma unroll
+    for (int u = 0; u < CLS_WPT; u++) load_word_scores(sp, cp, (wbase0 + 256 * u) * 32, n, v[u]);
+    for (int tgt = 0; tgt < ntgt; tgt++) {
+        const SelTarget t = sq[bq].t[tgt];
+        // IN: x > hi <=> x > f_hi;  BAND: x >= lo <=> x >= f_lo (x a float); -inf
+        // (no score) is neither, since f_lo is made finite
+        const float f_hi = f32_down(t.hi), f_lo = fmaxf(f32_up(t.lo), -__FLT_MAX__);
+        uint32_t bandw[CLS_WPT], nin = 0, nb = 0;
+#pragma unroll
+        for (int u = 0; u < CLS_WPT; u++) {
+            const int64_t word = wbase0 + 256 * u;
+            uint32_t in = 0, bm = 0;
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                in |= (v[u][i] > f_hi ? 1u : 0u) << i;
+                bm |= (v[u][i] <= f_hi && v[u][i] >= f_lo ? 1u : 0u) << i;
+            }
+            if (word < nwords) bitmap[((size_t)tgt * gridDim.y + bq) * nwords + word] = in;
+            bandw[u] = bm;
+            nin += (uint32_t)__builtin_popcount(in);
+            nb += (uint32_t)__builtin_popcount(bm);
+        }
+        const uint32_t incl = wave_incl_scan_u32(nb);
+        const uint32_t wnin = wave_sum_u32(nin);
+        if (lane == 63) w_nb[wave] = incl;
+        if (lane == 0) w_in[wave] = wnin;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t bin = w_in[0] + w_in[1] + w_in[2] + w_in[3];
+            const uint32_t bnb = w_nb[0] + w_nb[1] + w_nb[2] + w_nb[3];
+            if (bin) atomicAdd(&sq[bq].t[tgt].in_cnt, (int32_t)bin);
+            base_sh = bnb ? atomicAdd(&sq[bq].t[tgt].band_cnt, (int32_t)bnb) : 0;
+        }
+        __syncthreads();
+        int32_t pos = base_sh + (int32_t)(incl - nb);
+        for (int w = 0; w < wave; w++) pos += (int32_t)w_nb[w];
+        int32_t *dst = band + ((size_t)tgt * gridDim.y + bq) * band_cap;
+#pragma unroll
+        for (int u = 0; u < CLS_WPT; u++) {
+            const int64_t s0 = (wbase0 + 256 * u) * 32;
+            for (uint32_t m = bandw[u]; m; m &= m - 1) dst[pos++] = (int32_t)(s0 + __builtin_ctz(m));
+        }
+        __syncthreads();  // w_in, w_nb and base_sh are reused by the next target
+    }
+}
+
+// ------------------------------------------------- shared finishing steps
+
+__device__ __forceinline__ uint32_t load_word(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 
 // Smallest order-preserving float key in [L, R] whose bin is >= target
 // (R + 1 if none), by a 64-way search run by one whole wave.
@@ -351,6 +426,68 @@ __device__ uint32_t wave_search_bin(uint32_t L, uint32_t R, int target, float lo
 }
 
 
+// The r best of nb <= 2 NT band entries by (key descending, slot ascending),
+// set in the bitmap: a radix select of the r-th largest 96-bit composite
+// (key, ~slot), one byte per pass from the top.  Composites are unique (slots
+// are), so exactly r entries are at or above it.  Entries live in registers
+// (two per thread); `hist` is LDS scratch of at least 258 words.
+template <int NT>
+__device__ void radix_pick(uint32_t *bm, int32_t nb, int32_t r, const uint64_t (&key)[2], const int32_t (&slot)[2],
+                           uint32_t *hist) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    bool live[2], take[2];
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+        live[e] = tid + NT * e < nb;
+        take[e] = false;
+    }
+    uint32_t need = (uint32_t)r;
+    auto digit = [&](int e, int p) -> uint32_t {  // byte p of the composite, 11 = most significant
+        return p >= 4 ? (uint32_t)(key[e] >> (8 * (p - 4))) & 0xffu : (~(uint32_t)slot[e] >> (8 * p)) & 0xffu;
+    };
+    for (int p = 11; p >= 0; p--) {
+        for (int i = tid; i < 256; i += NT) hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 2; e++)
+            if (live[e]) atomicAdd(&hist[digit(e, p)], 1u);
+        __syncthreads();
+        if (tid < 64) {
+            // suffix counts over the 256 digits, lane l holding digits 4 (63 - l) .. +3
+            uint32_t h[4], loc = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                h[j] = hist[4 * (63 - lane) + j];
+                loc += h[j];
+            }
+            const uint32_t incl = wave_incl_scan_u32(loc);  // counts of digits >= 4 (63 - l)
+            uint32_t above = incl - loc;                     // counts of digits > 4 (63 - l) + 3
+#pragma unroll
+            for (int j = 3; j >= 0; j--) {
+                if (above < need && above + h[j] >= need) {
+                    hist[256] = 4 * (63 - lane) + j;
+                    hist[257] = need - above;
+                }
+                above += h[j];
+            }
+        }
+        __syncthreads();
+        const uint32_t d = hist[256];
+        need = hist[257];
+#pragma unroll
+        for (int e = 0; e < 2; e++)
+            if (live[e]) {
+                const uint32_t g = digit(e, p);
+                take[e] |= g > d;
+                live[e] = g == d;
+            }
+        __syncthreads();  // hist is cleared by the next pass
+    }
+#pragma unroll
+    for (int e = 0; e < 2; e++)
+        if (take[e] || live[e]) atomicOr(&bm[slot[e] >> 5], 1u << (slot[e] & 31));
+}
+
 // Pick the best r = K - |IN| BAND entries of one target by (exact score
 // descending, slot ascending) and set their bits in the LDS bitmap `bm`, then
 // compact the bitmap in slot order into the ascending index list (-1 padded).
@@ -364,7 +501,20 @@ __device__ void finish_target(uint32_t *bm, int64_t nwords, int64_t n, int32_t K
                               bool preloaded = false) {
     const int32_t r = K - in_cnt;
     auto exact_key = [&](int32_t i) -> uint64_t { return dkey(bs ? bs[i] : (double)scores_q[list[i]]); };
-    if (r > 0 && nb > 0) {
+    if (r > 0 && nb > 0 && r < nb && nb > 256 && nb <= 2 * NT) {
+        // many entries: radix select, O(nb) work per pass instead of O(nb^2) comparisons
+        uint64_t kk[2];
+        int32_t ss[2];
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const int32_t i = threadIdx.x + NT * e;
+            const int32_t ii = i < nb ? i : nb - 1;
+            kk[e] = preloaded ? key_lds[ii] : exact_key(ii);
+            ss[e] = preloaded ? slot_lds[ii] : list[ii];
+        }
+        __syncthreads();  // the LDS entries are read before key_lds becomes the histogram
+        radix_pick<NT>(bm, nb, r, kk, ss, reinterpret_cast<uint32_t *>(key_lds));
+    } else if (r > 0 && nb > 0) {
         if (nb <= BANDFAST) {
             if (!preloaded)
                 for (int32_t i = threadIdx.x; i < nb; i += NT) {
@@ -1185,7 +1335,7 @@ static bool small_path(const SelPlan &p) { return p.n <= ONE_N; }
 size_t sel_workspace(const SelPlan &p, bool own_stats) {
     Carve c(nullptr, 0);
     if (own_stats && !small_path(p)) c.take<TileStat>((size_t)p.BQ * p.ntiles);
-    c.take<uint32_t>((size_t)p.BQ * p.nchunks * NB);
+    c.take<uint32_t>((size_t)p.BQ * NB);
     c.take<SelQuery>((size_t)p.BQ);
     c.take<double>((size_t)p.BQ);  // error bounds
     c.take<uint32_t>((size_t)p.ntgt * p.BQ * p.nwords);
@@ -1202,7 +1352,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     Carve c(ws, ws_bytes);
     TileStat *stats = const_cast<TileStat *>(stats_in);
     if (!stats && !small_path(p)) stats = c.take<TileStat>((size_t)p.BQ * p.ntiles);
-    uint32_t *part = c.take<uint32_t>((size_t)p.BQ * p.nchunks * NB);
+    uint32_t *qhist = c.take<uint32_t>((size_t)p.BQ * NB);
     SelQuery *sq = c.take<SelQuery>((size_t)p.BQ);
     double *ebuf = c.take<double>((size_t)p.BQ);
     uint32_t *bitmap = c.take<uint32_t>((size_t)p.ntgt * p.BQ * p.nwords);
@@ -1246,13 +1396,13 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         }
         if (p.certified)
             launch_err_bound_from_norms(rs->sumwq, p.BQ, rs->HI, rs->dI, stats, p.ntiles, ebuf, s);
-        hipLaunchKernelGGL(k_sel_hist, dim3(p.nchunks, p.BQ), dim3(256), 0, s, scores, cand, p.n, stats, p.ntiles,
-                           p.nchunks, part, sq);
+        hipLaunchKernelGGL(k_sel_range, dim3(p.BQ), dim3(256), 0, s, stats, p.ntiles, sq, qhist);
+        check_launch("selection range");
+        hipLaunchKernelGGL(k_sel_hist, dim3(p.nchunks, p.BQ), dim3(256), 0, s, scores, cand, p.n, sq, qhist);
         check_launch("selection histogram");
-        hipLaunchKernelGGL(k_sel_find, dim3(p.BQ), dim3(256), 0, s, part, p.nchunks, p.K0, p.K1,
-                           p.certified ? ebuf : nullptr, sq);
+        hipLaunchKernelGGL(k_sel_find, dim3(p.BQ), dim3(256), 0, s, qhist, p.K0, p.K1, p.certified ? ebuf : nullptr, sq);
         check_launch("selection find");
-        const int nblk = (int)((p.nwords + 255) / 256);
+        const int nblk = (int)((p.nwords + 256 * CLS_WPT - 1) / (256 * CLS_WPT));
         hipLaunchKernelGGL(k_sel_classify, dim3(nblk, p.BQ), dim3(256), 0, s, scores, cand, p.n, p.ntgt, sq, bitmap,
                            p.nwords, band, p.band_cap);
         check_launch("selection classify");
@@ -1276,8 +1426,11 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         r.band_cap = p.band_cap;
         const int rowb = rs->dI * (rs->dt == CSA2_F32 ? 4 : 2);
         if (rowb <= RS_ROWB) {
-            // about 256 entries per query per round; the grid stays small enough to be resident at once
-            int nblk = 256 / RS_EPB;
+            // about 256 entries per query per round at 32,768 slots, more for longer
+            // rows of scores (the band grows with the density of scores); the grid
+            // stays small enough to be resident at once, and idle blocks exit at once
+            int64_t want = (int64_t)256 * ((p.n + ONE_N - 1) / ONE_N);
+            int nblk = (int)((want < 1024 ? want : 1024) / RS_EPB);
             if ((int64_t)nblk * p.BQ > 2048) nblk = (int)(2048 / p.BQ) > 1 ? (int)(2048 / p.BQ) : 1;
             if (rs->dt == CSA2_F32) hipLaunchKernelGGL(k_sel_rescore<true>, dim3(nblk, p.BQ), dim3(RS_NT), 0, s, r);
             else hipLaunchKernelGGL(k_sel_rescore<false>, dim3(nblk, p.BQ), dim3(RS_NT), 0, s, r);
