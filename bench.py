@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["decode-128k", "v41-decoder-1m"], default="decode-128k",
+                    help="decode-128k: one Full layer of the 128K-context decode (the default line); "
+                         "v41-decoder-1m: the 20-layer V4.1 decoder schedule at a 1M-token context")
     ap.add_argument("--only", choices=["indexer", "attention", "layer", "copy"], default=None,
                     help="launch only this part, for counter collection (prints no JSON); 'copy' is a plain "
                          "1 GiB device-to-device copy that calibrates the byte counters")
@@ -118,6 +121,108 @@ def cpu_baseline(torch, oracle, s0, budget_s):
                       f"(indexer, top-2048, attention) in binary64; {total:.1f} s total"}
 
 
+E2M1_BOUNDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)  # the synthetic generator's midpoints between E2M1 magnitudes
+
+
+def fp4_rows_gpu(torch, g, B, N, D):
+    """FP4 rows [B, N, D/2 + D/16] drawn on the GPU as the synthetic generator
+    does: N(0,1) values to their E2M1 codes, E4M3 scales log-uniform in
+    [2^-4, 2^4]; one sequence at a time to bound the temporaries."""
+    bounds = torch.tensor(E2M1_BOUNDS, device="cuda")
+    out = torch.empty(B, N, D // 2 + D // 16, dtype=torch.uint8, device="cuda")
+    for bb in range(B):
+        x = torch.randn(N, D, generator=g, device="cuda")
+        code = torch.bucketize(x.abs(), bounds, right=True).to(torch.uint8) | ((x < 0).to(torch.uint8) << 3)
+        del x
+        out[bb, :, : D // 2] = code[:, 0::2] | (code[:, 1::2] << 4)
+        del code
+        u = torch.rand(N, D // 16, generator=g, device="cuda") * 8.0 - 4.0
+        ex = torch.floor(u)
+        mant = torch.floor((torch.exp2(u - ex) - 1.0) * 8.0).clamp(0, 7)
+        out[bb, :, D // 2:] = ((ex + 7).to(torch.uint8) << 3) | mant.to(torch.uint8)
+    return out
+
+
+def run_v41_decoder(a, torch, b):
+    """V4.1's decoder schedule as one step: 1 Full + 3 Reuse, then 4 x (1 Reindex
+    + 3 Reuse), around one persistent 16,384-position pool; every token kept
+    (m = 1), so a 1M-token context is 1,048,576 entries per sequence; Full
+    top-2048, Reindex top-512; FP4 main KV (64 heads x 512), bf16 indexer 64 x 128."""
+    B, N, HI, dI, H, D, k, kr, P = 16, 1 << 20, 64, 128, 64, 512, 2048, 512, 16384
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    kI = torch.randn(B, N, dI, generator=g, device="cuda").to(torch.bfloat16)
+    kv = fp4_rows_gpu(torch, g, B, N, D)
+    scale = D ** -0.5
+    modes = ["FULL"] + ["REUSE"] * 3 + (["REINDEX"] + ["REUSE"] * 3) * 4
+
+    def qI_w():
+        return (torch.randn(B, 1, HI, dI, generator=g, device="cuda").to(torch.bfloat16),
+                torch.rand(B, 1, HI, generator=g, device="cuda"))
+
+    layers, pool, idx = [], None, None
+    for mode in modes:
+        q = torch.randn(B, 1, H, D, generator=g, device="cuda").to(torch.bfloat16)
+        if mode == "FULL":
+            qi, w = qI_w()
+            L = b.Layer("FULL", q=q, kv=kv, k=k, scale=scale, qI=qi, w=w, kI=kI, m=1, P=P)
+            pool, idx = L.pool, L.idx
+        elif mode == "REINDEX":
+            qi, w = qI_w()
+            L = b.Layer("REINDEX", q=q, kv=kv, k=kr, scale=scale, qI=qi, w=w, kI=kI, m=1, pool=pool)
+            idx = L.idx
+        else:
+            L = b.Layer("REUSE", q=q, kv=kv, k=idx.shape[-1], scale=scale, idx=idx)
+        layers.append(L)
+    torch.cuda.synchronize()
+
+    def step():
+        for L in layers:
+            L.run()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / a.steps
+
+    full = layers[0]
+    sc = torch.empty(B, 1, N, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, b._index_ws(b.BF16, B, 1, HI, dI, N, 0)), dtype=torch.uint8, device="cuda")
+    qi0, w0 = full.tensors["qI"], full.tensors["w"]
+    run_idx = lambda i: b.index_score(qi0, w0, kI, want_err=False, scores=sc, ws=ws)
+    run_idx(0)
+    t_idx_ms = event_time(torch, run_idx, max(10, a.steps))
+    idx_bytes = B * N * dI * 2 + B * HI * (dI * 2 + 4) + B * N * 4
+    gbs = idx_bytes / (t_idx_ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode query-tokens/s through the V4.1 decoder schedule (20 layers) at 1M ctx",
+        "value": B / t_step,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "V4.1 decoder schedule: 1 Full (pool 16,384, top-2048) + 3 Reuse, then 4 x "
+                               "(1 Reindex top-512 + 3 Reuse); 16 seqs x 1 query, 1,048,576 entries (1M tokens, "
+                               "m = 1), indexer 64x128 bf16, FP4 KV 64 heads x 512",
+                   "global_batch": B, "seq_len": N},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "indexer score of the Full layer (1,048,576 entries)",
+                     "algorithmic_bytes": idx_bytes, "launch_ms": t_idx_ms},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -127,6 +232,9 @@ def main():
     import torch
     from sparse_long_context_csa2_amd import binding as b
 
+    if a.workload == "v41-decoder-1m":
+        run_v41_decoder(a, torch, b)
+        return
     if a.only == "copy":
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
