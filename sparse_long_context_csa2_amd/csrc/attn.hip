@@ -756,36 +756,37 @@ __global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *_
 }
 
 // ----------------------------------------------------------- split merge
-// One thread per 4 channels of one head.  Up to COMB_UNROLL splits are read in
-// one round of loads (their maxima, sums, scales and 4-channel fp16 partial
-// rows), so the merge waits for memory once; more splits take further rounds,
-// the running maximum rescaling what is already summed.
+// One thread per 8 channels of one head.  Up to COMB_UNROLL splits are read in
+// one round of loads (their maxima, sums, scales and 8-channel fp16 partial
+// rows, 16 bytes each), so the merge waits for memory once; more splits take
+// further rounds, the running maximum rescaling what is already summed.
 constexpr int COMB_UNROLL = 16;
+constexpr int COMB_CPT = 8;  // channels per thread (a quarter of D is a multiple of 8 for D >= 32)
 
 __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t *__restrict__ part_o,
                                                       const float2 *__restrict__ part_ml,
                                                       const float *__restrict__ part_sc, int BQ, int H, int D,
                                                       int nsplit, void *__restrict__ out, int out_dt,
                                                       float *__restrict__ lse) {
-    const int tpr = D / 4;  // threads per head row
+    const int tpr = D / COMB_CPT;  // threads per head row
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = gid / tpr;  // (bq, h)
-    const int c4 = (int)(gid % tpr);
+    const int c8 = (int)(gid % tpr);
     if (row >= (int64_t)BQ * H) return;
-    const int quarter = 4 * c4 / (D / 4);  // the channels' scale slot
+    const int quarter = COMB_CPT * c8 / (D / 4);  // the channels' scale slot
     float M = NEG_INF, Ls = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsplit; s0 += COMB_UNROLL) {
         float2 ml[COMB_UNROLL];
         float sc[COMB_UNROLL];
-        uint2 ph[COMB_UNROLL];
+        uint4 ph[COMB_UNROLL];
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; u++) {
             // splits past the end read the last one and are dropped
             const size_t pi = (size_t)row * nsplit + (s0 + u < nsplit ? s0 + u : nsplit - 1);
             ml[u] = part_ml[pi];
             sc[u] = part_sc[pi * 4 + quarter];
-            ph[u] = reinterpret_cast<const uint2 *>(part_o + pi * D)[c4];
+            ph[u] = reinterpret_cast<const uint4 *>(part_o + pi * D)[c8];
         }
         float Mn = M;
 #pragma unroll
@@ -795,7 +796,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t *__restrict
             if (M != NEG_INF && M != Mn) {
                 const float f = __expf(M - Mn);
                 Ls *= f;
-                acc = acc * f;
+                acc0 = acc0 * f;
+                acc1 = acc1 * f;
             }
 #pragma unroll
             for (int u = 0; u < COMB_UNROLL; u++)
@@ -803,22 +805,31 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t *__restrict
                     const float f = __expf(ml[u].x - Mn);
                     Ls += ml[u].y * f;
                     const f16x2 a = __builtin_bit_cast(f16x2, ph[u].x), b = __builtin_bit_cast(f16x2, ph[u].y);
-                    const f32x4 po = {(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
-                    acc = acc + po * (f * sc[u]);
+                    const f16x2 c = __builtin_bit_cast(f16x2, ph[u].z), d = __builtin_bit_cast(f16x2, ph[u].w);
+                    const f32x4 p0 = {(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+                    const f32x4 p1 = {(float)c[0], (float)c[1], (float)d[0], (float)d[1]};
+                    const float fs = f * sc[u];
+                    acc0 = acc0 + p0 * fs;
+                    acc1 = acc1 + p1 * fs;
                 }
             M = Mn;
         }
     }
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    const size_t oi = (size_t)row * D + 4 * c4;
+    const size_t oi = (size_t)row * D + COMB_CPT * c8;
     if (out_dt == CSA2_F32) {
-        *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + oi) = acc * inv;
+        f32x4 *o = reinterpret_cast<f32x4 *>(static_cast<float *>(out) + oi);
+        o[0] = acc0 * inv;
+        o[1] = acc1 * inv;
     } else {
-        const uint32_t w0 = uint32_t(f32_to_bf16_rne(acc[0] * inv)) | (uint32_t(f32_to_bf16_rne(acc[1] * inv)) << 16);
-        const uint32_t w1 = uint32_t(f32_to_bf16_rne(acc[2] * inv)) | (uint32_t(f32_to_bf16_rne(acc[3] * inv)) << 16);
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + oi) = make_uint2(w0, w1);
+        uint4 w;
+        w.x = uint32_t(f32_to_bf16_rne(acc0[0] * inv)) | (uint32_t(f32_to_bf16_rne(acc0[1] * inv)) << 16);
+        w.y = uint32_t(f32_to_bf16_rne(acc0[2] * inv)) | (uint32_t(f32_to_bf16_rne(acc0[3] * inv)) << 16);
+        w.z = uint32_t(f32_to_bf16_rne(acc1[0] * inv)) | (uint32_t(f32_to_bf16_rne(acc1[1] * inv)) << 16);
+        w.w = uint32_t(f32_to_bf16_rne(acc1[2] * inv)) | (uint32_t(f32_to_bf16_rne(acc1[3] * inv)) << 16);
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + oi) = w;
     }
-    if (lse && c4 == 0) lse[row] = Ls > 0.f ? M + logf(Ls) : NEG_INF;
+    if (lse && c8 == 0) lse[row] = Ls > 0.f ? M + logf(Ls) : NEG_INF;
 }
 
 // ------------------------------------------------------------ VALU kernel
@@ -990,7 +1001,7 @@ void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *i
 #undef CSA2_ATT_CASE
     check_launch("attention");
     if (p.nsplit > 1) {
-        const int64_t threads = (int64_t)BQ * p.H * (p.D / 4);
+        const int64_t threads = (int64_t)BQ * p.H * (p.D / COMB_CPT);
         hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, part_o, part_ml, part_sc,
                            BQ, p.H, p.D, p.nsplit, out, p.q_dt, lse);
         check_launch("attention combine");

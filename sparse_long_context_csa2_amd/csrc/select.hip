@@ -445,7 +445,35 @@ __device__ void radix_pick(uint32_t *bm, int32_t nb, int32_t r, const uint64_t (
     auto digit = [&](int e, int p) -> uint32_t {  // byte p of the composite, 11 = most significant
         return p >= 4 ? (uint32_t)(key[e] >> (8 * (p - 4))) & 0xffu : (~(uint32_t)slot[e] >> (8 * p)) & 0xffu;
     };
-    for (int p = 11; p >= 0; p--) {
+    // bytes above the highest one in which two entries differ select nothing:
+    // OR of every composite XOR entry 0's, reduced per wave, then in LDS
+    if (tid == 0) {
+        hist[260] = (uint32_t)key[0];
+        hist[261] = (uint32_t)(key[0] >> 32);
+        hist[262] = (uint32_t)slot[0];
+        hist[263] = hist[264] = hist[265] = 0;
+    }
+    __syncthreads();
+    const uint64_t k0 = (uint64_t)hist[260] | ((uint64_t)hist[261] << 32);
+    const uint32_t s0 = hist[262];
+    uint32_t dx[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 2; e++)
+        if (live[e]) {
+            dx[0] |= (uint32_t)(key[e] ^ k0);
+            dx[1] |= (uint32_t)((key[e] ^ k0) >> 32);
+            dx[2] |= (uint32_t)slot[e] ^ s0;
+        }
+#pragma unroll
+    for (int i = 0; i < 3; i++) {
+        for (int o = 32; o > 0; o >>= 1) dx[i] |= (uint32_t)__shfl_xor((int)dx[i], o);
+        if (lane == 0 && dx[i]) atomicOr(&hist[263 + i], dx[i]);
+    }
+    __syncthreads();
+    const uint32_t kxl = hist[263], kxh = hist[264], sx = hist[265];
+    const int ptop = kxh ? 8 + (31 - __builtin_clz(kxh)) / 8
+                         : kxl ? 4 + (31 - __builtin_clz(kxl)) / 8 : sx ? (31 - __builtin_clz(sx)) / 8 : 0;
+    for (int p = ptop; p >= 0; p--) {
         for (int i = tid; i < 256; i += NT) hist[i] = 0;
         __syncthreads();
 #pragma unroll
@@ -467,6 +495,7 @@ __device__ void radix_pick(uint32_t *bm, int32_t nb, int32_t r, const uint64_t (
                 if (above < need && above + h[j] >= need) {
                     hist[256] = 4 * (63 - lane) + j;
                     hist[257] = need - above;
+                    hist[258] = h[j];
                 }
                 above += h[j];
             }
@@ -474,18 +503,103 @@ __device__ void radix_pick(uint32_t *bm, int32_t nb, int32_t r, const uint64_t (
         __syncthreads();
         const uint32_t d = hist[256];
         need = hist[257];
+        const bool done = hist[258] == need;  // every entry left in digit d is taken
 #pragma unroll
         for (int e = 0; e < 2; e++)
             if (live[e]) {
                 const uint32_t g = digit(e, p);
-                take[e] |= g > d;
-                live[e] = g == d;
+                take[e] |= g > d || (done && g == d);
+                live[e] = !done && g == d;
             }
         __syncthreads();  // hist is cleared by the next pass
+        if (done) break;
     }
 #pragma unroll
     for (int e = 0; e < 2; e++)
         if (take[e] || live[e]) atomicOr(&bm[slot[e] >> 5], 1u << (slot[e] & 31));
+}
+
+// Write the set bits of the bitmap `bm` (LDS or global) in slot order as the
+// ascending index list dst[0, K) (mapped through cand_q when given, -1
+// padded) and the count.  Each wave sweeps 2048 consecutive words per round
+// with coalesced 16-byte loads (lane l holds words 4 l .. 4 l + 3 of each
+// 256-word group); positions come from wave scans of the popcounts and one
+// exchange of the wave totals.  The list is staged in LDS (out_cap ints) when
+// it fits, for coalesced writes; sweeping stops once K entries are placed.
+template <int NT>
+__device__ void compact_bits(const uint32_t *bm, int64_t nwords, int32_t K, const int32_t *cand_q, int32_t *dst,
+                             int32_t *count_dst, int32_t *out_lds, int out_cap, uint32_t *red) {
+    constexpr int NW = NT / 64, G = 4;
+    constexpr int64_t WSPAN = 256 * G, SPAN = WSPAN * NW;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool staged = K <= out_cap;
+    const bool vec = (reinterpret_cast<uintptr_t>(bm) & 15) == 0;
+    uint32_t base = 0;
+    for (int64_t c0 = 0; c0 < nwords && base < (uint32_t)K; c0 += SPAN) {
+        const int64_t wb = c0 + wave * WSPAN + 4 * lane;
+        uint32_t v[G][4];
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            const int64_t w = wb + 256 * g;
+            if (vec && w + 3 < nwords) {
+                const u32x4 t = *reinterpret_cast<const u32x4 *>(bm + w);
+#pragma unroll
+                for (int j = 0; j < 4; j++) v[g][j] = t[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++) v[g][j] = w + j < nwords ? bm[w + j] : 0u;
+            }
+        }
+        uint32_t ex[G], gt[G], wt = 0;
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            const uint32_t c = __builtin_popcount(v[g][0]) + __builtin_popcount(v[g][1]) +
+                               __builtin_popcount(v[g][2]) + __builtin_popcount(v[g][3]);
+            const uint32_t incl = wave_incl_scan_u32(c);
+            ex[g] = incl - c;
+            gt[g] = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            wt += gt[g];
+        }
+        if (lane == 0) red[wave] = wt;
+        __syncthreads();
+        uint32_t pos0 = base, all = 0;
+        for (int i = 0; i < NW; i++) {
+            const uint32_t t = red[i];
+            if (i < wave) pos0 += t;
+            all += t;
+        }
+        __syncthreads();  // red is rewritten next round
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            uint32_t pos = pos0 + ex[g];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                uint32_t bits = v[g][j];
+                while (bits) {
+                    const int i = __builtin_ctz(bits);
+                    bits &= bits - 1;
+                    if (pos < (uint32_t)K) {
+                        const int64_t sl = (wb + 256 * g + j) * 32 + i;
+                        const int32_t val = cand_q ? cand_q[sl] : (int32_t)sl;
+                        if (staged) out_lds[pos] = val;
+                        else dst[pos] = val;
+                    }
+                    pos++;
+                }
+            }
+            pos0 += gt[g];
+        }
+        base += all;
+    }
+    const uint32_t kept = base < (uint32_t)K ? base : (uint32_t)K;
+    if (staged) {
+        __syncthreads();
+        for (int32_t i = threadIdx.x; i < K; i += NT) dst[i] = i < (int32_t)kept ? out_lds[i] : -1;
+    } else {
+        for (int32_t i = kept + threadIdx.x; i < K; i += NT) dst[i] = -1;
+    }
+    if (count_dst && threadIdx.x == 0) *count_dst = (int32_t)kept;
+    __syncthreads();
 }
 
 // Pick the best r = K - |IN| BAND entries of one target by (exact score
@@ -576,37 +690,11 @@ __device__ void finish_target(uint32_t *bm, int64_t nwords, int64_t n, int32_t K
             }
         }
     }
+    // the picks (global atomics when the bitmap is not in LDS) are complete and
+    // visible before the bitmap is read
+    __threadfence();
     __syncthreads();
-    const int64_t per = (nwords + NT - 1) / NT;
-    const int64_t w0 = (int64_t)threadIdx.x * per;
-    uint32_t mine = 0;
-    for (int64_t w = w0; w < w0 + per && w < nwords; w++) mine += __builtin_popcount(bm[w]);
-    uint32_t tot;
-    uint32_t pos = block_excl_scan<NT>(mine, red, tot);
-    const bool staged = K <= out_cap;
-    for (int64_t w = w0; w < w0 + per && w < nwords; w++) {
-        uint32_t bits = bm[w];
-        while (bits) {
-            const int i = __builtin_ctz(bits);
-            bits &= bits - 1;
-            const int64_t slot = w * 32 + i;
-            if (pos < (uint32_t)K) {
-                const int32_t v = cand_q ? cand_q[slot] : (int32_t)slot;
-                if (staged) out_lds[pos] = v;
-                else dst[pos] = v;
-            }
-            pos++;
-        }
-    }
-    const uint32_t kept = tot < (uint32_t)K ? tot : (uint32_t)K;
-    if (staged) {
-        __syncthreads();
-        for (int32_t i = threadIdx.x; i < K; i += NT) dst[i] = i < (int32_t)kept ? out_lds[i] : -1;
-    } else {
-        for (int32_t i = kept + threadIdx.x; i < K; i += NT) dst[i] = -1;
-    }
-    if (count_dst && threadIdx.x == 0) *count_dst = (int32_t)kept;
-    __syncthreads();
+    compact_bits<NT>(bm, nwords, K, cand_q, dst, count_dst, out_lds, out_cap, red);
 }
 
 // ------------------------------------------------------ one-block path
@@ -1247,8 +1335,8 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_finish_one(const float *__restri
 }
 
 // ------------------------------------------------------------------ finish
-// One block per query: band pick + compaction for each target, the bitmap
-// staged in LDS when it fits.
+// One block per query and target: band pick + compaction, the bitmap staged
+// in LDS when it fits.
 constexpr int FIN_NT = 1024;
 constexpr int64_t FIN_BM = 8192;   // bitmap words kept in LDS
 constexpr int FIN_OUT = 16384;     // output entries staged in LDS
@@ -1269,15 +1357,15 @@ struct FinishArgs {
 };
 
 __global__ __launch_bounds__(FIN_NT) void k_sel_finish(FinishArgs a) {
-    __shared__ uint32_t bm_lds[FIN_BM];
+    __shared__ __attribute__((aligned(16))) uint32_t bm_lds[FIN_BM];
     __shared__ uint64_t key_lds[BANDFAST];
     __shared__ int32_t slot_lds[BANDFAST];
     __shared__ int32_t out_lds[FIN_OUT];
     __shared__ uint32_t red[FIN_NT / 64];
     const int bq = blockIdx.x;
-    const SelQuery sqv = a.sq[bq];
-    for (int tg = a.tg0; tg < a.ntgt; tg++) {
-        const SelTarget t = sqv.t[tg];
+    {
+        const int tg = a.tg0 + blockIdx.y;  // the targets of a query are finished by separate blocks
+        const SelTarget t = a.sq[bq].t[tg];
         uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
         const int32_t *list = a.band + ((size_t)tg * gridDim.x + bq) * a.band_cap;
         const double *bs = a.band_score ? a.band_score + ((size_t)tg * gridDim.x + bq) * a.band_cap : nullptr;
@@ -1470,7 +1558,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     f.count0 = count0;
     f.out1 = out1;
     f.tg0 = tg0;
-    hipLaunchKernelGGL(k_sel_finish, dim3(p.BQ), dim3(FIN_NT), 0, s, f);
+    hipLaunchKernelGGL(k_sel_finish, dim3(p.BQ, p.ntgt - tg0), dim3(FIN_NT), 0, s, f);
     check_launch("selection finish");
 }
 
