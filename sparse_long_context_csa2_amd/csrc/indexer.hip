@@ -441,22 +441,6 @@ __global__ __launch_bounds__(256) void k_err_bound(const void *__restrict__ qI, 
     }
 }
 
-__global__ __launch_bounds__(256) void k_err_from_norms(const double *__restrict__ sumwq, int HI, int dI,
-                                                       const TileStat *__restrict__ stats, int ntiles,
-                                                       double *__restrict__ err64) {
-    __shared__ float kred[4];
-    const int bq = blockIdx.x;
-    float km = 0.f;
-    for (int t = threadIdx.x; t < ntiles; t += 256) km = fmaxf(km, stats[(size_t)bq * ntiles + t].kmax2);
-    km = wave_max(km);
-    if ((threadIdx.x & 63) == 0) kred[threadIdx.x >> 6] = km;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const float k2 = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
-        err64[bq] = score_bound(sqrt((double)k2 * (1.0 + ldexp(1.0, -10))), sumwq[bq] * (1.0 + ldexp(1.0, -30)), HI, dI);
-    }
-}
-
 // Registers of the streaming kernel: query fragments HI*DI/128 plus key
 // fragments DI/2.
 constexpr bool stream_fits(int HI, int DI) { return HI * DI / 128 + DI / 2 <= 128; }
@@ -520,12 +504,6 @@ void launch_index_score(const void *qI, int dt, const float *w, const void *kI, 
                            scores, stats, ntiles, sumwq);
     }
     check_launch("index score");
-}
-
-void launch_err_bound_from_norms(const double *sumwq, int BQ, int HI, int dI, const TileStat *stats, int ntiles,
-                                 double *err64, hipStream_t s) {
-    hipLaunchKernelGGL(k_err_from_norms, dim3(BQ), dim3(256), 0, s, sumwq, HI, dI, stats, ntiles, err64);
-    check_launch("error bound");
 }
 
 void launch_err_bound(const void *qI, int dt, const float *w, int BQ, int HI, int dI, const TileStat *stats,

@@ -13,8 +13,6 @@ void launch_index_score(const void *qI, int dt, const float *w, const void *kI, 
                         TileStat *stats, double *sumwq, hipStream_t s);
 void launch_err_bound(const void *qI, int dt, const float *w, int BQ, int HI, int dI, const TileStat *stats,
                       int ntiles, float *err32, double *err64, hipStream_t s);
-void launch_err_bound_from_norms(const double *sumwq, int BQ, int HI, int dI, const TileStat *stats, int ntiles,
-                                 double *err64, hipStream_t s);
 
 // -------------------------------------------------------------- selection
 // Per-query selection records (certified mode): for each target, the value

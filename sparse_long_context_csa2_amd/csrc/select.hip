@@ -34,6 +34,7 @@ namespace csa2 {
 
 constexpr int NB = 2048;        // histogram bins
 constexpr int CH = 8192;        // slots per chunk (256 threads x 32)
+constexpr int HIST_CPB = 4;     // chunks per histogram block
 constexpr int BANDFAST = 2048;  // largest band ranked by pairwise counting
 
 namespace {
@@ -122,27 +123,42 @@ __global__ __launch_bounds__(256) void k_sel_stats(const float *__restrict__ sco
 
 // ---------------------------------------------------------------- 1: range
 // Per query: the finite scores' range [lo, hi] and count from the tile
-// statistics, the bin() parameters into the query record, and the query's
-// histogram cleared for the chunks' counts.
+// statistics, the bin() parameters into the query record, the query's
+// histogram cleared for the chunks' counts, and (certified mode) the score
+// error bound from the tiles' largest key norm.
 __global__ __launch_bounds__(256) void k_sel_range(const TileStat *__restrict__ stats, int ntiles,
-                                                   SelQuery *__restrict__ sq, uint32_t *__restrict__ qhist) {
-    __shared__ float r_min[4], r_max[4];
+                                                   SelQuery *__restrict__ sq, uint32_t *__restrict__ qhist,
+                                                   const double *__restrict__ sumwq, int HI, int dI,
+                                                   double *__restrict__ err64) {
+    __shared__ float r_min[4], r_max[4], r_k[4];
     __shared__ uint32_t r_n[4];
     const int bq = blockIdx.x, wave = threadIdx.x >> 6;
-    float mn = POS_INF, mx = NEG_INF;
+    float mn = POS_INF, mx = NEG_INF, km = 0.f;
     uint32_t cnt = 0;
-    for (int t = threadIdx.x; t < ntiles; t += 256) {
-        const TileStat st = stats[(size_t)bq * ntiles + t];
-        mn = fminf(mn, st.smin);
-        mx = fmaxf(mx, st.smax);
-        cnt += st.nvalid;
+    // eight tile records in flight per thread
+    for (int t0 = threadIdx.x; t0 < ntiles; t0 += 8 * 256) {
+        TileStat st[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int t = t0 + 256 * u;
+            st[u] = stats[(size_t)bq * ntiles + (t < ntiles ? t : t0)];  // past the end: repeat the first
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            mn = fminf(mn, st[u].smin);
+            mx = fmaxf(mx, st[u].smax);
+            km = fmaxf(km, st[u].kmax2);
+            if (t0 + 256 * u < ntiles) cnt += st[u].nvalid;
+        }
     }
     mn = wave_min(mn);
     mx = wave_max(mx);
+    km = wave_max(km);
     cnt = wave_sum_u32(cnt);
     if ((threadIdx.x & 63) == 0) {
         r_min[wave] = mn;
         r_max[wave] = mx;
+        r_k[wave] = km;
         r_n[wave] = cnt;
     }
     for (int i = threadIdx.x; i < NB; i += 256) qhist[(size_t)bq * NB + i] = 0;
@@ -155,6 +171,12 @@ __global__ __launch_bounds__(256) void k_sel_range(const TileStat *__restrict__ 
         sq[bq].lo = lo;
         sq[bq].inv = (nv > 0 && span > 0.f) ? (float)NB / span : 0.f;
         sq[bq].nvalid = (int32_t)nv;
+        if (err64) {
+            // the score error bound from the largest key norm and the query's sum of w |q|
+            const float k2 = fmaxf(fmaxf(r_k[0], r_k[1]), fmaxf(r_k[2], r_k[3]));
+            err64[bq] = score_bound(sqrt((double)k2 * (1.0 + ldexp(1.0, -10))),
+                                    sumwq[bq] * (1.0 + ldexp(1.0, -30)), HI, dI);
+        }
     }
 }
 
@@ -166,28 +188,33 @@ __global__ __launch_bounds__(256) void k_sel_hist(const float *__restrict__ scor
                                                   int64_t n, const SelQuery *__restrict__ sq,
                                                   uint32_t *__restrict__ qhist) {
     __shared__ uint32_t hist[NB];
-    const int bq = blockIdx.y, chunk = blockIdx.x;
+    const int bq = blockIdx.y;
     for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
     const float lo = sq[bq].lo, inv = sq[bq].inv;
     const int64_t base = (int64_t)bq * n;
-    const int64_t s0 = (int64_t)chunk * CH + threadIdx.x;
-    float v[CH / 256];
-#pragma unroll
-    for (int i = 0; i < CH / 256; i++) {
-        const int64_t sl = s0 + 256 * i;
-        v[i] = sl < n ? scores[base + sl] : NEG_INF;
-    }
-    if (cand) {
+    __syncthreads();
+    // HIST_CPB consecutive chunks per block into one LDS histogram, so that
+    // fewer partial histograms are added into the query's
+    for (int c = 0; c < HIST_CPB; c++) {
+        const int64_t s0 = ((int64_t)blockIdx.x * HIST_CPB + c) * CH + threadIdx.x;
+        if (s0 - threadIdx.x >= n) break;
+        float v[CH / 256];
 #pragma unroll
         for (int i = 0; i < CH / 256; i++) {
             const int64_t sl = s0 + 256 * i;
-            if (sl < n && cand[base + sl] < 0) v[i] = NEG_INF;
+            v[i] = sl < n ? scores[base + sl] : NEG_INF;
         }
-    }
-    __syncthreads();
+        if (cand) {
 #pragma unroll
-    for (int i = 0; i < CH / 256; i++)
-        if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
+            for (int i = 0; i < CH / 256; i++) {
+                const int64_t sl = s0 + 256 * i;
+                if (sl < n && cand[base + sl] < 0) v[i] = NEG_INF;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CH / 256; i++)
+            if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < NB; i += 256) {
         const uint32_t c = hist[i];
@@ -219,11 +246,10 @@ __global__ __launch_bounds__(256) void k_sel_find(const uint32_t *__restrict__ q
         local += h[i];
     }
     // suffix sums: cum[b] = number of finite scores in bins >= b
-    __shared__ uint32_t tot[256];
-    tot[threadIdx.x] = local;
-    __syncthreads();
-    uint32_t run = 0;
-    for (int t = threadIdx.x + 1; t < 256; t++) run += tot[t];
+    __shared__ uint32_t tot[4];
+    uint32_t all;
+    const uint32_t before = block_excl_scan<256>(local, tot, all);
+    uint32_t run = all - before - local;  // finite scores in the bins of later threads
     for (int i = 7; i >= 0; i--) {
         run += h[i];
         cum[threadIdx.x * 8 + i] = run;
@@ -1482,11 +1508,12 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
                                stats);
             check_launch("selection stats");
         }
-        if (p.certified)
-            launch_err_bound_from_norms(rs->sumwq, p.BQ, rs->HI, rs->dI, stats, p.ntiles, ebuf, s);
-        hipLaunchKernelGGL(k_sel_range, dim3(p.BQ), dim3(256), 0, s, stats, p.ntiles, sq, qhist);
+        hipLaunchKernelGGL(k_sel_range, dim3(p.BQ), dim3(256), 0, s, stats, p.ntiles, sq, qhist,
+                           p.certified ? rs->sumwq : nullptr, p.certified ? rs->HI : 0, p.certified ? rs->dI : 0,
+                           p.certified ? ebuf : nullptr);
         check_launch("selection range");
-        hipLaunchKernelGGL(k_sel_hist, dim3(p.nchunks, p.BQ), dim3(256), 0, s, scores, cand, p.n, sq, qhist);
+        hipLaunchKernelGGL(k_sel_hist, dim3((p.nchunks + HIST_CPB - 1) / HIST_CPB, p.BQ), dim3(256), 0, s, scores,
+                           cand, p.n, sq, qhist);
         check_launch("selection histogram");
         hipLaunchKernelGGL(k_sel_find, dim3(p.BQ), dim3(256), 0, s, qhist, p.K0, p.K1, p.certified ? ebuf : nullptr, sq);
         check_launch("selection find");
