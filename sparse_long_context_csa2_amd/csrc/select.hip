@@ -231,11 +231,15 @@ __device__ __forceinline__ double thr_hi(float z, double E) {
     return (double)z;
 }
 
+// Order-preserving key of the bin edge: defined with the one-block path.
+__device__ uint32_t edge_key(uint32_t lk, uint32_t hk, int target, float lo, float inv);
+
 // ---------------------------------------------------------------- 3: find
 __global__ __launch_bounds__(256) void k_sel_find(const uint32_t *__restrict__ qhist, int K0, int K1,
                                                   const double *__restrict__ ebound, SelQuery *__restrict__ sq) {
     __shared__ uint32_t cum[NB + 1];
     __shared__ int bstar;
+    __shared__ uint32_t edge[2];
     const int bq = blockIdx.x;
     // per-thread 8 consecutive bins of the query's histogram
     uint32_t h[8];
@@ -270,6 +274,17 @@ __global__ __launch_bounds__(256) void k_sel_find(const uint32_t *__restrict__ q
             }
         }
         __syncthreads();
+        // [a, z] = the float values >= lo whose bin is b* (bin() is monotone):
+        // wave 0 finds the lower edge a, wave 1 the upper edge z
+        if (bstar >= 0 && threadIdx.x < 128) {
+            const int wave = threadIdx.x >> 6;
+            const uint32_t lk = fkey(q.lo), hk = 0xff7fffffu;  // hk: key of the largest finite float
+            uint32_t kk = hk;
+            if (wave == 0) kk = edge_key(lk, hk, bstar, q.lo, q.inv);
+            else if (bstar + 1 < NB) kk = edge_key(lk, hk, bstar + 1, q.lo, q.inv) - 1;
+            if ((threadIdx.x & 63) == 0) edge[wave] = kk;
+        }
+        __syncthreads();
         if (threadIdx.x == 0) {
             SelTarget t;
             t.K = K;
@@ -280,29 +295,8 @@ __global__ __launch_bounds__(256) void k_sel_find(const uint32_t *__restrict__ q
                 t.lo = -__builtin_inf();
                 t.hi = -__builtin_inf();
             } else {
-                // [a, z] = the float values >= lo whose bin is b* (bisection on the
-                // order-preserving key; bin() is monotone)
-                const uint32_t lo_k = fkey(q.lo);
-                const uint32_t hi_k = 0xff7fffffu;  // key of the largest finite float
-                // a: smallest key with bin >= b*
-                uint32_t L = lo_k, R = hi_k;
-                while (L < R) {
-                    uint32_t M = L + (R - L) / 2;
-                    if (sel_bin(fkey_inv(M), q.lo, q.inv) >= bstar) R = M;
-                    else L = M + 1;
-                }
-                const float a = fkey_inv(L);
-                // z: largest key with bin <= b*
-                L = lo_k;
-                R = hi_k;
-                while (L < R) {
-                    uint32_t M = L + (R - L + 1) / 2;
-                    if (sel_bin(fkey_inv(M), q.lo, q.inv) <= bstar) L = M;
-                    else R = M - 1;
-                }
-                const float z = fkey_inv(L);
-                t.lo = thr_lo(a, E);
-                t.hi = thr_hi(z, E);
+                t.lo = thr_lo(fkey_inv(edge[0]), E);
+                t.hi = thr_hi(fkey_inv(edge[1]), E);
             }
             sq[bq].t[tgt] = t;
         }
