@@ -42,7 +42,10 @@ def _lib():
         lib.ora_topk.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_int, c_void_p, c_void_p]
         lib.ora_sparse_attn.argtypes = [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int64,
                                         c_void_p, c_int, c_double, c_void_p, c_void_p]
-        for f in ("ora_decode_row", "ora_compress", "ora_index_score", "ora_topk", "ora_sparse_attn"):
+        lib.ora_window_idx.argtypes = [c_void_p, c_int64, c_int, c_void_p]
+        lib.ora_merge_attn.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p]
+        for f in ("ora_decode_row", "ora_compress", "ora_index_score", "ora_topk", "ora_sparse_attn",
+                  "ora_window_idx", "ora_merge_attn"):
             getattr(lib, f).restype = None
         _LIB = lib
     return _LIB
@@ -236,6 +239,50 @@ def sparse_attn(q, kv, idx, scale: float, D: int | None = None):
     _lib().ora_sparse_attn(_ptr(qa), qdt, _ptr(ka), kdt, B, Q, H, D, N, _ptr(ia), k, float(scale),
                            _ptr(out), _ptr(lse))
     return out, lse
+
+
+# -------------------------------------------------------------- SWA branch
+
+def window_idx(q_pos, W: int) -> np.ndarray:
+    """Sliding-window entry list [B,Q,W] int32: positions p - W + 1 .. p of the
+    query's own token and the W - 1 before it, ascending, -1 below 0.
+
+    Video transcript on V4.1 Flash (prism.simon-ai.net), passages on the SWA
+    branch: a 128-token window per layer, uncompressed, not shared across
+    layers.  Reading: the query's own token is the newest of the W.
+    """
+    qp = _i64(q_pos)
+    idx = np.empty(qp.shape + (W,), dtype=np.int32)
+    _lib().ora_window_idx(_ptr(qp), int(qp.size), int(W), _ptr(idx))
+    return idx
+
+
+def merge_attn(o_a, lse_a, o_b, lse_b):
+    """(out, lse) of one softmax over the union of two disjoint entry sets,
+    from each set's attention output and log-sum-exp (all float64).
+
+    Reading (the pages give no rule for combining the SWA and CSA2 branches):
+    both sets enter a single softmax, so each branch is weighted by its share
+    exp(lse) of the joint denominator.
+    """
+    oa = np.ascontiguousarray(o_a, dtype=np.float64)
+    ob = np.ascontiguousarray(o_b, dtype=np.float64)
+    la = np.ascontiguousarray(lse_a, dtype=np.float64)
+    lb = np.ascontiguousarray(lse_b, dtype=np.float64)
+    if oa.shape != ob.shape or la.shape != lb.shape or oa.shape[:-1] != la.shape:
+        raise ValueError("shape mismatch")
+    D = oa.shape[-1]
+    out = np.empty_like(oa)
+    lse = np.empty_like(la)
+    _lib().ora_merge_attn(_ptr(oa), _ptr(la), _ptr(ob), _ptr(lb), int(la.size), int(D), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def swa_attn(q, swa_kv, q_pos, W: int, scale: float):
+    """The sliding-window branch: shared-KV attention of every query head over
+    the layer's own uncompressed window rows (the same row form as the global
+    KV, one vector per token used as key and value)."""
+    return sparse_attn(q, swa_kv, window_idx(q_pos, W), scale)
 
 
 # ------------------------------------------------------------------- modes

@@ -344,3 +344,55 @@ void ora_sparse_attn(const void *q, int q_dt, const void *kv, int kv_dt, int B, 
         free(num);
     }
 }
+
+/* ------------------------------------------------------------ SWA branch */
+
+/*
+ * Window list of the sliding-window branch: the W most recent token
+ * positions up to and including the query's own, p - W + 1 .. p in
+ * ascending order, those below 0 given as -1.
+ * Video transcript on V4.1 Flash (prism.simon-ai.net), the passages on the
+ * SWA branch: a 128-token window per layer, kept uncompressed and never shared
+ * across layers.  The window's exact edge is not stated; this reading counts
+ * the query's own token as the newest of the W.
+ */
+void ora_window_idx(const int64_t *q_pos, int64_t BQ, int W, int32_t *idx)
+{
+    for (int64_t bq = 0; bq < BQ; bq++)
+        for (int i = 0; i < W; i++) {
+            int64_t j = q_pos[bq] - (int64_t)W + 1 + i;
+            idx[bq * W + i] = j < 0 ? -1 : (int32_t)j;
+        }
+}
+
+/*
+ * Merge of two attention results over disjoint entry sets into the result of
+ * one softmax over their union (the CSA2 branch and the SWA branch).  With
+ * lse the log of each branch's softmax denominator:
+ *   M = max(lse_a, lse_b),  u = exp(lse_a - M),  v = exp(lse_b - M)
+ *   out = (u o_a + v o_b) / (u + v),   lse = M + ln(u + v)
+ * A branch with lse = -inf (no entry) has weight 0; both empty: out = 0,
+ * lse = -inf.  The pages do not state how the branches are combined; this is
+ * the reading in which both sets enter a single softmax.
+ * R rows of D values each, all arrays in doubles.
+ */
+void ora_merge_attn(const double *o_a, const double *lse_a, const double *o_b, const double *lse_b, int64_t R,
+                    int D, double *out, double *lse)
+{
+    for (int64_t r = 0; r < R; r++) {
+        double la = lse_a[r], lb = lse_b[r];
+        double *o = out + r * D;
+        if (la == -INFINITY && lb == -INFINITY) {
+            for (int d = 0; d < D; d++)
+                o[d] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double M = la > lb ? la : lb;
+        double u = exp(la - M), v = exp(lb - M);
+        double s = u + v;
+        for (int d = 0; d < D; d++)
+            o[d] = (u * o_a[r * D + d] + v * o_b[r * D + d]) / s;
+        lse[r] = M + log(s);
+    }
+}
