@@ -210,6 +210,46 @@ typedef struct {
 CSA2_API size_t csa2_layer_workspace_size(const csa2_layer_args *a);
 CSA2_API int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * csa2_swa_attn -- the sliding-window (SWA) branch, optionally merged with the
+ * CSA2 branch's result.
+ *
+ * Video transcript on V4.1 Flash (prism.simon-ai.net), passages on the SWA
+ * branch: each layer keeps its own uncompressed KV of the most recent 128
+ * tokens (not shared across layers) beside the shared global KV.  Readings
+ * (the pages state neither): the window of a query at token position p is
+ * the rows p - W + 1 .. p, its own token the newest; the rows have the form
+ * of the global KV (one D-vector per token, key and value of every head);
+ * the two branches combine as one softmax over the union of their entries.
+ *
+ * q [B,Q,H,D] in q_dt; swa_kv [B,T,row] in kv_dt (formats as csa2_sparse_attn);
+ * q_pos [B,Q] int64 token positions (rows past T - 1 or below 0 are skipped);
+ * W >= 1 window length.  Computes o_swa, lse_swa = attention over the window.
+ * csa_out [B,Q,H,D] in q_dt and csa_lse [B,Q,H] fp32: the CSA2 branch's
+ *   result (csa2_layer / csa2_sparse_attn with lse); both NULL for the window
+ *   branch alone.  With them, out = (u csa_out + v o_swa) / (u + v) with
+ *   u = exp(csa_lse - M), v = exp(lse_swa - M), M the larger lse, and
+ *   lse = M + ln(u + v).  out may be csa_out (merged in place).
+ * out [B,Q,H,D] in q_dt; lse [B,Q,H] fp32 or NULL.
+ * ------------------------------------------------------------------------- */
+CSA2_API size_t csa2_swa_attn_workspace_size(int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H, int32_t D,
+                                             int32_t W);
+CSA2_API int csa2_swa_attn(const void *q, const void *swa_kv, int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H,
+                           int32_t D, int64_t T, const int64_t *q_pos, int32_t W, float scale, const void *csa_out,
+                           const float *csa_lse, void *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * csa2_merge_attn -- one softmax over the union of two disjoint entry sets
+ * from each set's attention output and lse (the merge step of csa2_swa_attn
+ * on its own; same reading).
+ *
+ * o_a, o_b, out [R,D] in dt (CSA2_F32 or CSA2_BF16), D % 8 == 0; lse_a, lse_b
+ * [R] fp32; lse [R] fp32 or NULL.  A set with lse = -inf has weight 0; both
+ * empty give out = 0, lse = -inf.  out may alias o_a or o_b.
+ * ------------------------------------------------------------------------- */
+CSA2_API int csa2_merge_attn(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int dt,
+                             int64_t R, int32_t D, void *out, float *lse, void *stream);
+
 /* Message of the last non-OK status returned on the calling thread. */
 CSA2_API const char *csa2_last_error(void);
 /* Library version string. */

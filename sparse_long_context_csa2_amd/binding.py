@@ -58,6 +58,10 @@ _topk = _sig("csa2_topk", ctypes.c_int, [_vp, _i32, _i32, _i64, _vp, _i32, _vp, 
 _attn_ws = _sig("csa2_sparse_attn_workspace_size", _sz, [ctypes.c_int, ctypes.c_int, _i32, _i32, _i32, _i32, _i32])
 _attn = _sig("csa2_sparse_attn", ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.c_int, _i32, _i32, _i32, _i32, _i64,
                                                 _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp])
+_swa_ws = _sig("csa2_swa_attn_workspace_size", _sz, [ctypes.c_int, ctypes.c_int, _i32, _i32, _i32, _i32, _i32])
+_swa = _sig("csa2_swa_attn", ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.c_int, _i32, _i32, _i32, _i32, _i64, _vp,
+                                            _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_merge = _sig("csa2_merge_attn", ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _vp, _vp, _vp])
 _layer_ws = _sig("csa2_layer_workspace_size", _sz, [ctypes.POINTER(LayerArgs)])
 _layer = _sig("csa2_layer", ctypes.c_int, [ctypes.POINTER(LayerArgs), _vp, _sz, _vp])
 _last_error = _sig("csa2_last_error", ctypes.c_char_p, [])
@@ -65,6 +69,7 @@ _version = _sig("csa2_version", ctypes.c_char_p, [])
 
 EXPORTS = ["csa2_compress_workspace_size", "csa2_compress", "csa2_index_score_workspace_size", "csa2_index_score",
            "csa2_topk_workspace_size", "csa2_topk", "csa2_sparse_attn_workspace_size", "csa2_sparse_attn",
+           "csa2_swa_attn_workspace_size", "csa2_swa_attn", "csa2_merge_attn",
            "csa2_layer_workspace_size", "csa2_layer", "csa2_last_error", "csa2_version"]
 
 
@@ -182,6 +187,37 @@ def sparse_attn(q, kv, idx, scale, D=None, want_lse=True, out=None, ws=None):
     wsb = _workspace(nws, q.device, ws)
     _check(_attn(_p(q), _p(kv), q_dt, kv_dt, B, Q, H, D, N, _p(idx), k, scale, _p(out), _p(lse), _p(wsb), nws,
                  _stream()))
+    return out, lse
+
+
+def swa_attn(q, swa_kv, q_pos, W, scale, csa_out=None, csa_lse=None, want_lse=True, out=None, ws=None):
+    """The sliding-window branch over the layer's own rows swa_kv [B,T,row]
+    (window p - W + 1 .. p of each query position), merged with the CSA2
+    branch's (csa_out, csa_lse) when given.  out may be csa_out."""
+    _dev(q, swa_kv, q_pos, csa_out, csa_lse)
+    B, Q, H, D = q.shape
+    T = swa_kv.shape[1]
+    q_dt, kv_dt = _dt(q), _dt(swa_kv)
+    if out is None:
+        out = torch.empty(B, Q, H, D, dtype=q.dtype, device=q.device)
+    lse = torch.empty(B, Q, H, dtype=torch.float32, device=q.device) if want_lse else None
+    nws = _swa_ws(q_dt, kv_dt, B, Q, H, D, W)
+    wsb = _workspace(nws, q.device, ws)
+    _check(_swa(_p(q), _p(swa_kv), q_dt, kv_dt, B, Q, H, D, T, _p(q_pos), W, scale, _p(csa_out), _p(csa_lse),
+                _p(out), _p(lse), _p(wsb), nws, _stream()))
+    return out, lse
+
+
+def merge_attn(o_a, lse_a, o_b, lse_b, out=None, want_lse=True):
+    """One softmax over the union of two disjoint entry sets from each set's
+    attention output [..., D] and lse [...]."""
+    _dev(o_a, lse_a, o_b, lse_b)
+    D = o_a.shape[-1]
+    R = lse_a.numel()
+    if out is None:
+        out = torch.empty_like(o_a)
+    lse = torch.empty_like(lse_a) if want_lse else None
+    _check(_merge(_p(o_a), _p(lse_a), _p(o_b), _p(lse_b), _dt(o_a), R, D, _p(out), _p(lse), _stream()))
     return out, lse
 
 

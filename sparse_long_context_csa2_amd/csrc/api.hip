@@ -246,6 +246,91 @@ int csa2_sparse_attn(const void *q, const void *kv, int q_dt, int kv_dt, int32_t
     });
 }
 
+namespace {
+struct SwaSizes {
+    size_t attn, idx, lse, total;
+};
+SwaSizes swa_sizes(int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H, int32_t D, int32_t W) {
+    SwaSizes z{};
+    const csa2::AttnPlan p = csa2::attn_plan(q_dt, kv_dt, B, Q, H, D, 1, W);
+    csa2::Carve c(nullptr, 0);
+    c.take<int32_t>((size_t)B * Q * W);
+    c.take<float>((size_t)B * Q * H);
+    c.take<uint8_t>((size_t)B * Q * H * D * (q_dt == CSA2_F32 ? 4 : 2));
+    z.attn = csa2::attn_workspace(p);
+    c.take<uint8_t>(z.attn);
+    z.total = c.used;
+    return z;
+}
+}  // namespace
+
+size_t csa2_swa_attn_workspace_size(int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H, int32_t D, int32_t W) {
+    if (B < 1 || Q < 1 || H < 1 || D < 1 || W < 1) return 0;
+    return swa_sizes(q_dt, kv_dt, B, Q, H, D, W).total;
+}
+
+int csa2_swa_attn(const void *q, const void *swa_kv, int q_dt, int kv_dt, int32_t B, int32_t Q, int32_t H, int32_t D,
+                  int64_t T, const int64_t *q_pos, int32_t W, float scale, const void *csa_out, const float *csa_lse,
+                  void *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    return guarded([&] {
+        if (B < 1 || Q < 1 || H < 1 || D < 1 || T < 1 || W < 1)
+            throw Error(CSA2_EINVAL, "B, Q, H, D, T and W must be >= 1");
+        need_plain_dt(q_dt, "q dtype");
+        if (kv_dt != CSA2_F32 && kv_dt != CSA2_BF16 && kv_dt != CSA2_FP4) throw Error(CSA2_EINVAL, "unknown kv format");
+        if (kv_dt == CSA2_FP4 && (D % 16 || q_dt != CSA2_BF16))
+            throw Error(CSA2_EINVAL, "FP4 kv needs D % 16 == 0 and bf16 queries");
+        if (kv_dt == CSA2_BF16 && D % 8) throw Error(CSA2_EINVAL, "bf16 kv rows need D % 8 == 0");
+        need_ptr(q, "q");
+        need_ptr(swa_kv, "swa_kv");
+        need_ptr(q_pos, "q_pos");
+        need_ptr(out, "out");
+        opt_ptr(lse, "lse");
+        if ((csa_out == nullptr) != (csa_lse == nullptr))
+            throw Error(CSA2_EINVAL, "csa_out and csa_lse are given together or not at all");
+        if (csa_out) {
+            opt_ptr(csa_out, "csa_out");
+            opt_ptr(csa_lse, "csa_lse");
+            if (D % 8) throw Error(CSA2_EINVAL, "the merge needs D % 8 == 0");
+        }
+        const csa2::AttnPlan p = csa2::attn_plan(q_dt, kv_dt, B, Q, H, D, T, W);
+        if (!csa2::attn_supported(p))
+            throw Error(CSA2_EUNSUPPORTED, "no attention kernel for this shape (vector path needs D + W <= 16384)");
+        const SwaSizes z = swa_sizes(q_dt, kv_dt, B, Q, H, D, W);
+        need_ws(ws, ws_bytes, z.total);
+        hipStream_t s = (hipStream_t)stream;
+        csa2::Carve c(ws, ws_bytes);
+        int32_t *idx = c.take<int32_t>((size_t)B * Q * W);
+        float *lse_w = c.take<float>((size_t)B * Q * H);
+        void *out_w = c.take<uint8_t>((size_t)B * Q * H * D * (q_dt == CSA2_F32 ? 4 : 2));
+        void *aws = c.take<uint8_t>(z.attn);
+        const int64_t BQ = (int64_t)B * Q;
+        csa2::launch_window_idx(q_pos, BQ, W, T, idx, s);
+        if (!csa_out) {
+            csa2::attn_run(p, q, swa_kv, idx, scale, out, lse, aws, z.attn, s);
+            return;
+        }
+        // the window branch goes to the workspace (out may be csa_out), then
+        // the two are merged into out
+        csa2::attn_run(p, q, swa_kv, idx, scale, out_w, lse_w, aws, z.attn, s);
+        csa2::launch_merge_attn(q_dt, csa_out, csa_lse, out_w, lse_w, BQ * H, D, out, lse, s);
+    });
+}
+
+int csa2_merge_attn(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int dt, int64_t R,
+                    int32_t D, void *out, float *lse, void *stream) {
+    return guarded([&] {
+        if (R < 1 || D < 8 || D % 8) throw Error(CSA2_EINVAL, "R >= 1 and D a positive multiple of 8 are needed");
+        need_plain_dt(dt, "dtype");
+        need_ptr(o_a, "o_a");
+        need_ptr(lse_a, "lse_a");
+        need_ptr(o_b, "o_b");
+        need_ptr(lse_b, "lse_b");
+        need_ptr(out, "out");
+        opt_ptr(lse, "lse");
+        csa2::launch_merge_attn(dt, o_a, lse_a, o_b, lse_b, R, D, out, lse, (hipStream_t)stream);
+    });
+}
+
 size_t csa2_layer_workspace_size(const csa2_layer_args *a) {
     if (!a || a->B < 1 || a->Q < 1 || a->k < 1 || a->H < 1 || a->D < 1) return 0;
     return layer_sizes(a).total;

@@ -98,4 +98,9 @@ size_t compress_workspace(int dt, int64_t n_out, int D, int m, int halo);
 void compress_run(const void *x, int dt, int64_t n_out, int D, int m, int halo, const void *wz, const float *bias,
                   void *out, void *ws, size_t ws_bytes, hipStream_t s);
 
+// ------------------------------------------------------------- SWA branch
+void launch_window_idx(const int64_t *q_pos, int64_t BQ, int W, int64_t T, int32_t *idx, hipStream_t s);
+void launch_merge_attn(int dt, const void *oa, const float *la, const void *ob, const float *lb, int64_t R, int D,
+                       void *out, float *lse, hipStream_t s);
+
 }  // namespace csa2

@@ -1,0 +1,109 @@
+"""Parity of the sliding-window (SWA) branch and its merge with the CSA2
+branch (through the C ABI) against the CPU oracle.  Reading: one softmax over
+the union of both branches' entries; the window of a query at position p is
+p - W + 1 .. p."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import ATOL_BF16, ATOL_F32, RTOL_BF16, RTOL_F32, assert_close, dev, host
+from sparse_long_context_csa2_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_long_context_csa2_amd import binding
+    return binding
+
+
+def _positions(T, W):
+    # before the first full window, at its edge, past it, the last row
+    return [0, 1, min(W - 2, T - 1), min(W - 1, T - 1), min(W, T - 1), T - 1]
+
+
+@pytest.mark.parametrize("fmt,H,D,W,T", [
+    ("bf16", 64, 512, 128, 300),   # the pages' window, V4.1 head shape
+    ("bf16", 16, 128, 37, 90),     # ragged window
+    ("f32", 8, 128, 128, 200),     # fp32 (vector path)
+])
+def test_window_branch_alone(b, fmt, H, D, W, T):
+    rng = np.random.default_rng(W + T)
+    B, Q = 2, 6
+    draw = synth.normal_bf16 if fmt == "bf16" else synth.normal_f32
+    q, kv = draw(rng, (B, Q, H, D)), draw(rng, (B, T, D))
+    pos = torch.tensor([_positions(T, W), _positions(T, W)[::-1]], dtype=torch.int64)
+    scale = 1 / math.sqrt(D)
+    ro, rl = oracle.swa_attn(q, kv, pos, W, scale)
+    out, lse = b.swa_attn(dev(q), dev(kv), dev(pos), W, scale)
+    torch.cuda.synchronize()
+    atol, rtol = (ATOL_F32, RTOL_F32) if fmt == "f32" else (ATOL_BF16, RTOL_BF16)
+    assert_close(out, ro, atol, rtol, "out")
+    assert_close(lse, rl, atol, rtol, "lse")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_merge_alone(b, dt):
+    rng = np.random.default_rng(7)
+    R, D = 300, 64
+    draw = synth.normal_bf16 if dt == "bf16" else synth.normal_f32
+    oa, ob = draw(rng, (R, D)), draw(rng, (R, D))
+    la = torch.from_numpy(rng.normal(0, 4, R).astype(np.float32))
+    lb = torch.from_numpy(rng.normal(0, 4, R).astype(np.float32))
+    la[::7] = -math.inf    # branch a empty
+    lb[::11] = -math.inf   # branch b empty (row 0 and 77: both)
+    oa[::7] = 0
+    ob[::11] = 0
+    ro, rl = oracle.merge_attn(oa.double().numpy(), la.double().numpy(), ob.double().numpy(), lb.double().numpy())
+    out, lse = b.merge_attn(dev(oa), dev(la), dev(ob), dev(lb))
+    torch.cuda.synchronize()
+    atol, rtol = (ATOL_F32, RTOL_F32) if dt == "f32" else (ATOL_BF16, RTOL_BF16)
+    assert_close(out, ro, atol, rtol, "out")
+    assert_close(lse, rl, 1e-5, 1e-5, "lse")
+    # a row with one empty branch is the other branch exactly
+    g = host(out)
+    only_b = [r for r in range(R) if r % 7 == 0 and r % 11 != 0]
+    only_a = [r for r in range(R) if r % 11 == 0 and r % 7 != 0]
+    assert torch.equal(g[only_b], ob[only_b].to(g.dtype))
+    assert torch.equal(g[only_a], oa[only_a].to(g.dtype))
+
+
+def test_csa2_and_window_merged_equal_one_softmax_over_both(b):
+    """FP4 global KV through the CSA2 branch (k selected entries), bf16 window
+    rows through the SWA branch, merged in place; against the oracle's single
+    attention over the union (FP4 values are exact in bf16, so the two row
+    sets are concatenated as one bf16 matrix)."""
+    rng = np.random.default_rng(11)
+    B, Q, H, D, N, k, T, W = 2, 4, 64, 512, 700, 96, 400, 128
+    kv = synth.fp4_rows(rng, (B, N), D)
+    swa = synth.normal_bf16(rng, (B, T, D))
+    q = synth.normal_bf16(rng, (B, Q, H, D))
+    idx = np.full((B, Q, k), -1, dtype=np.int32)
+    for bb in range(B):
+        for qq in range(Q):
+            kk = [k, k - 5, 0, 40][qq]            # full, ragged, empty CSA2 branch, short
+            idx[bb, qq, :kk] = np.sort(rng.choice(N, size=kk, replace=False))
+    idx = torch.from_numpy(idx)
+    pos = torch.tensor([[T - 1, 0, 200, -1], [130, T - 1, 5, 127]], dtype=torch.int64)  # -1: empty window
+    scale = 1 / math.sqrt(D)
+    # oracle: one softmax over both row sets
+    dec = torch.from_numpy(oracle.decode_rows(kv, D))                     # [B,N,D] float64
+    assert torch.equal(dec.to(torch.bfloat16).double(), dec)              # exact in bf16
+    cat = torch.cat([dec.to(torch.bfloat16), swa], dim=1)                 # [B,N+T,D]
+    win = torch.from_numpy(oracle.window_idx(pos, W))
+    union = torch.cat([idx, torch.where(win >= 0, win + N, win)], dim=-1)
+    ro, rl = oracle.sparse_attn(q, cat, union, scale)
+    # GPU: CSA2 branch, then the window branch merged into it in place
+    qd = dev(q)
+    co, cl = b.sparse_attn(qd, dev(kv), dev(idx), scale, D=D)
+    out, lse = b.swa_attn(qd, dev(swa), dev(pos), W, scale, csa_out=co, csa_lse=cl, out=co)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == co.data_ptr()
+    assert_close(out, ro, ATOL_BF16, RTOL_BF16, "merged out")
+    assert_close(lse, rl, ATOL_BF16, RTOL_BF16, "merged lse")
