@@ -43,9 +43,10 @@ def _lib():
         lib.ora_sparse_attn.argtypes = [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int64,
                                         c_void_p, c_int, c_double, c_void_p, c_void_p]
         lib.ora_window_idx.argtypes = [c_void_p, c_int64, c_int, c_void_p]
+        lib.ora_quantize_fp4.argtypes = [c_void_p, c_int, c_int64, c_int, c_void_p]
         lib.ora_merge_attn.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p]
         for f in ("ora_decode_row", "ora_compress", "ora_index_score", "ora_topk", "ora_sparse_attn",
-                  "ora_window_idx", "ora_merge_attn"):
+                  "ora_window_idx", "ora_merge_attn", "ora_quantize_fp4"):
             getattr(lib, f).restype = None
         _LIB = lib
     return _LIB
@@ -139,6 +140,27 @@ def decode_rows(rows, D: int) -> np.ndarray:
         row = np.ascontiguousarray(flat[r])
         lib.ora_decode_row(_ptr(row), dt, D, out[r].ctypes.data_as(ctypes.c_void_p))
     return out.reshape(*lead, D)
+
+
+def quantize_fp4(x) -> np.ndarray:
+    """FP4 rows [..., D/2 + D/16] uint8 of fp32/bf16 rows x [..., D] (cache writes).
+
+    "Recall之王 祭出Reuse", section "把KV Cache压到极致的几把杀手锏": E2M1 values
+    with one E4M3 scale per 16 channels.  Reading (the pages give no recipe):
+    the smallest E4M3 scale s with 6 s >= the group's largest magnitude, each
+    code the E2M1 value nearest to x / s, ties to the even code.
+    """
+    a, dt = _raw(x)
+    if dt == FP4:
+        raise TypeError("quantize_fp4 takes fp32 or bf16 rows")
+    D = a.shape[-1]
+    if D % 16:
+        raise ValueError("D must be a multiple of 16")
+    lead = a.shape[:-1]
+    flat = np.ascontiguousarray(a.reshape(-1, D))
+    out = np.empty((flat.shape[0], D // 2 + D // 16), dtype=np.uint8)
+    _lib().ora_quantize_fp4(_ptr(flat), dt, int(flat.shape[0]), int(D), _ptr(out))
+    return out.reshape(*lead, D // 2 + D // 16)
 
 
 # ------------------------------------------------------------- compression

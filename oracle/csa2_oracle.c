@@ -396,3 +396,67 @@ void ora_merge_attn(const double *o_a, const double *lse_a, const double *o_b, c
         lse[r] = M + log(s);
     }
 }
+
+/* ---------------------------------------------------- FP4 cache writes */
+
+/*
+ * FP4 quantizer for main-KV cache writes ("Recall之王 祭出Reuse", section
+ * "把KV Cache压到极致的几把杀手锏": the main KV is stored as E2M1 values with
+ * one E4M3 scale per 16 channels).  The pages do not say how the scale and
+ * codes are chosen; the reading taken, per group of 16 channels:
+ *   scale s = the smallest non-negative E4M3 value with 6 s >= max |x|
+ *             (6 is the largest E2M1 magnitude, so no code saturates),
+ *             448 if no such value exists (then codes saturate at 6);
+ *   code    = the E2M1 value nearest to x / s, ties to the even code
+ *             (mantissa bit 0), the sign of x in bit 3 (a zero is +0);
+ *             with s = 0 every code is 0.
+ * Every comparison is exact in binary64: 6 s and (midpoint * s) have at most
+ * seven significant bits.  x: n rows of D values in dt (CSA2_F32 or BF16);
+ * out: n FP4 rows (layout as ora_decode_row).
+ */
+void ora_quantize_fp4(const void *x, int dt, int64_t n, int D, uint8_t *out)
+{
+    const int64_t rb = row_bytes(ORA_FP4, D);
+    for (int64_t r = 0; r < n; r++) {
+        uint8_t *codes = out + r * rb;
+        uint8_t *scales = codes + D / 2;
+        for (int g = 0; g < D / 16; g++) {
+            double v[16], amax = 0.0;
+            for (int i = 0; i < 16; i++) {
+                v[i] = elem(x, dt, r * D + g * 16 + i);
+                if (fabs(v[i]) > amax)
+                    amax = fabs(v[i]);
+            }
+            /* the smallest E4M3 byte (0x00 .. 0x7E, increasing values) with 6 s >= amax */
+            unsigned sb = 0x7Eu;
+            for (unsigned b = 0; b <= 0x7Eu; b++)
+                if (6.0 * ora_e4m3(b) >= amax) {
+                    sb = b;
+                    break;
+                }
+            double s = ora_e4m3(sb);
+            scales[g] = (uint8_t)sb;
+            for (int i = 0; i < 16; i++) {
+                unsigned best = 0;
+                if (s > 0.0) {
+                    /* nearest of the 8 magnitudes; on a tie the even code */
+                    double a = fabs(v[i]), bd = INFINITY;
+                    for (unsigned c = 0; c < 8; c++) {
+                        double d = fabs(a - ora_e2m1(c) * s);
+                        if (d < bd || (d == bd && (c & 1u) == 0)) {
+                            bd = d;
+                            best = c;
+                        }
+                    }
+                    if (v[i] < 0.0 && best != 0)
+                        best |= 8u;
+                }
+                int c = g * 16 + i;
+                if (c % 2 == 0)
+                    codes[c / 2] = (uint8_t)best;
+                else
+                    codes[c / 2] |= (uint8_t)(best << 4);
+            }
+        }
+    }
+}
