@@ -98,6 +98,27 @@ CSA2_API int csa2_compress(const void *x, int dt, int64_t n_out, int32_t D, int3
                            void *stream);
 
 /* ---------------------------------------------------------------------------
+ * csa2_quantize_fp4 -- FP4 rows for main-KV cache writes.
+ *
+ * "Recall之王 祭出Reuse", section "把KV Cache压到极致的几把杀手锏": the main KV
+ * cache holds E2M1 values with one E4M3 scale per 16 channels.  Reading (the
+ * pages give no recipe), per group of 16 channels: the scale is the smallest
+ * non-negative E4M3 value s with 6 s >= the group's largest |x| (448 if none
+ * is, then codes saturate at +-6); each code is the E2M1 value nearest to
+ * x / s, ties to the even code, a zero stored as +0 (s = 0: all codes 0).
+ * Typical use, decode-time append: csa2_compress of the last 2m tokens
+ * (n_out = 1, halo = 1) into a bf16 row, then this call into the cache.
+ *
+ * x [n, D] in dt (CSA2_F32 or CSA2_BF16), finite, D % 16 == 0.
+ * cache: FP4 rows of D/2 + D/16 bytes (layout as CSA2_FP4); row r of x is
+ *   written to cache row dst_row[r] (int64 [n] on the device), or to row r
+ *   when dst_row is NULL.  Destination rows must be distinct; other rows of
+ *   the cache are not touched.  Bit-exact: the result does not depend on n.
+ * ------------------------------------------------------------------------- */
+CSA2_API int csa2_quantize_fp4(const void *x, int dt, int64_t n, int32_t D, void *cache, const int64_t *dst_row,
+                               void *stream);
+
+/* ---------------------------------------------------------------------------
  * csa2_index_score -- lightning-indexer scores.
  *
  * "读完这篇，你就搞懂 DeepSeek v4 了", section "闪电索引机制（对应步骤二）", eq. (8):

@@ -61,6 +61,7 @@ _attn = _sig("csa2_sparse_attn", ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.c
 _swa_ws = _sig("csa2_swa_attn_workspace_size", _sz, [ctypes.c_int, ctypes.c_int, _i32, _i32, _i32, _i32, _i32])
 _swa = _sig("csa2_swa_attn", ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.c_int, _i32, _i32, _i32, _i32, _i64, _vp,
                                             _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_quant = _sig("csa2_quantize_fp4", ctypes.c_int, [_vp, ctypes.c_int, _i64, _i32, _vp, _vp, _vp])
 _merge = _sig("csa2_merge_attn", ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _vp, _vp, _vp])
 _layer_ws = _sig("csa2_layer_workspace_size", _sz, [ctypes.POINTER(LayerArgs)])
 _layer = _sig("csa2_layer", ctypes.c_int, [ctypes.POINTER(LayerArgs), _vp, _sz, _vp])
@@ -69,7 +70,7 @@ _version = _sig("csa2_version", ctypes.c_char_p, [])
 
 EXPORTS = ["csa2_compress_workspace_size", "csa2_compress", "csa2_index_score_workspace_size", "csa2_index_score",
            "csa2_topk_workspace_size", "csa2_topk", "csa2_sparse_attn_workspace_size", "csa2_sparse_attn",
-           "csa2_swa_attn_workspace_size", "csa2_swa_attn", "csa2_merge_attn",
+           "csa2_swa_attn_workspace_size", "csa2_swa_attn", "csa2_merge_attn", "csa2_quantize_fp4",
            "csa2_layer_workspace_size", "csa2_layer", "csa2_last_error", "csa2_version"]
 
 
@@ -188,6 +189,18 @@ def sparse_attn(q, kv, idx, scale, D=None, want_lse=True, out=None, ws=None):
     _check(_attn(_p(q), _p(kv), q_dt, kv_dt, B, Q, H, D, N, _p(idx), k, scale, _p(out), _p(lse), _p(wsb), nws,
                  _stream()))
     return out, lse
+
+
+def quantize_fp4(x, cache=None, dst_row=None):
+    """FP4 rows of x [n, D] (fp32/bf16) written into cache rows dst_row (int64
+    [n]; rows 0..n-1 when None).  cache: uint8 [rows, D/2 + D/16], allocated
+    for n rows when None."""
+    _dev(x, cache, dst_row)
+    n, D = x.shape
+    if cache is None:
+        cache = torch.empty(n, D // 2 + D // 16, dtype=torch.uint8, device=x.device)
+    _check(_quant(_p(x), _dt(x), n, D, _p(cache), _p(dst_row), _stream()))
+    return cache
 
 
 def swa_attn(q, swa_kv, q_pos, W, scale, csa_out=None, csa_lse=None, want_lse=True, out=None, ws=None):

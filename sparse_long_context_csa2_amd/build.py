@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["api.hip", "indexer.hip", "select.hip", "attn.hip", "compress.hip", "swa.hip"]
+SOURCES = ["api.hip", "indexer.hip", "select.hip", "attn.hip", "compress.hip", "swa.hip", "quant.hip"]
 HEADERS = ["common.h", "internal.h"]
 
 ARCH = os.environ.get("CSA2_ARCH", "gfx950")

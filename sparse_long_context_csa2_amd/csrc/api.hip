@@ -331,6 +331,18 @@ int csa2_merge_attn(const void *o_a, const float *lse_a, const void *o_b, const 
     });
 }
 
+int csa2_quantize_fp4(const void *x, int dt, int64_t n, int32_t D, void *cache, const int64_t *dst_row,
+                      void *stream) {
+    return guarded([&] {
+        if (n < 1 || D < 16 || D % 16) throw Error(CSA2_EINVAL, "n >= 1 and D a positive multiple of 16 are needed");
+        need_plain_dt(dt, "x dtype");
+        need_ptr(x, "x");
+        if (!cache) throw Error(CSA2_EINVAL, "cache is NULL");  // rows are byte-addressed: no alignment needed
+        if (dst_row && (reinterpret_cast<uintptr_t>(dst_row) & 7u)) throw Error(CSA2_EINVAL, "dst_row is not aligned");
+        csa2::launch_quantize_fp4(x, dt, n, D, static_cast<uint8_t *>(cache), dst_row, (hipStream_t)stream);
+    });
+}
+
 size_t csa2_layer_workspace_size(const csa2_layer_args *a) {
     if (!a || a->B < 1 || a->Q < 1 || a->k < 1 || a->H < 1 || a->D < 1) return 0;
     return layer_sizes(a).total;

@@ -103,4 +103,8 @@ void launch_window_idx(const int64_t *q_pos, int64_t BQ, int W, int64_t T, int32
 void launch_merge_attn(int dt, const void *oa, const float *la, const void *ob, const float *lb, int64_t R, int D,
                        void *out, float *lse, hipStream_t s);
 
+// ------------------------------------------------------- FP4 cache writes
+void launch_quantize_fp4(const void *x, int dt, int64_t n, int D, uint8_t *cache, const int64_t *dst_row,
+                         hipStream_t s);
+
 }  // namespace csa2
