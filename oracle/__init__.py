@@ -199,6 +199,15 @@ def index_score(qI, w, kI, q_pos=None, m: int = 1, cand=None) -> np.ndarray:
     """
     qa, dt = _raw(qI)
     ka, kdt = _raw(kI)
+    if kdt == FP4:
+        # FP4 indexer keys (same page, the passage on V4's FP4 indexer q/K): the
+        # decoded values (at most 6 significant bits) are exact in fp32, and so
+        # are the bf16 or fp32 queries; the formula is then the fp32 one
+        dI = qa.shape[-1]
+        ka = decode_rows(ka, dI).astype(np.float32)
+        if dt == BF16:
+            qa = (qa.astype(np.uint32) << 16).view(np.float32)
+        dt = kdt = F32
     if kdt != dt:
         raise TypeError("qI and kI must share a dtype")
     wa = _f32(w)

@@ -123,3 +123,19 @@ def test_bf16_values_score_like_their_f32_copies():
     a = oracle.index_score(qI, w, kI)
     b = oracle.index_score(qI.float(), w, kI.float())
     assert np.array_equal(a, b)
+
+
+def test_fp4_keys_score_as_their_decoded_values():
+    # FP4 indexer keys: scores equal those of the independently decoded rows
+    # (golden E2M1 table, torch E4M3) given as fp32, bit for bit
+    from oracle_helpers import decode_fp4_independent
+    rng = np.random.default_rng(21)
+    B, Q, N, HI, dI = 2, 2, 90, 8, 64
+    kI = synth.fp4_rows(rng, (B, N), dI)
+    qI = synth.normal_bf16(rng, (B, Q, HI, dI))
+    w = synth.uniform_f32(rng, (B, Q, HI))
+    dec = decode_fp4_independent(kI.numpy(), dI)
+    assert np.array_equal(dec.astype(np.float32).astype(np.float64), dec)
+    ref = oracle.index_score(qI.float(), w, torch.from_numpy(dec.astype(np.float32)))
+    got = oracle.index_score(qI, w, kI)
+    assert np.array_equal(got, ref)
