@@ -128,6 +128,11 @@ CSA2_API int csa2_quantize_fp4(const void *x, int dt, int64_t n, int32_t D, void
  * One key row per entry is shared by all heads.
  *
  * qI [B,Q,HI,dI] and kI [B,N,dI] in dt (CSA2_F32 or CSA2_BF16); w [B,Q,HI] fp32.
+ * dt = CSA2_FP4: FP4 indexer keys -- kI holds FP4 rows of dI/2 + dI/16 bytes
+ *   (layout as CSA2_FP4, e.g. written by csa2_quantize_fp4) and qI is bf16
+ *   (an FP4 query is passed decoded, exactly, in bf16).  Needs dI % 64 == 0
+ *   and a matrix-core shape.  Same page, the passage on V4's FP4 indexer q/K
+ *   (the scores stay at higher precision; here fp32 with the bound below).
  * q_pos [B,Q] absolute token positions, or NULL: with q_pos, entry j is visible
  *   to the query only if (j+1)*m <= q_pos+1 (complete groups); without it all
  *   N entries are visible.
@@ -208,7 +213,8 @@ typedef struct {
     int64_t N;            /* compressed entries per sequence */
     int32_t m;            /* group size (for q_pos visibility) */
     int32_t HI, dI;       /* indexer heads and dim */
-    int32_t idx_dt;       /* dtype of qI and kI (CSA2_F32 or CSA2_BF16) */
+    int32_t idx_dt;       /* dtype of qI and kI (CSA2_F32 or CSA2_BF16), or CSA2_FP4: FP4 kI, bf16 qI
+                             (as csa2_index_score; dI % 64 == 0, dI <= 256) */
     int32_t k;            /* top-k (>= 1) */
     int32_t P;            /* FULL: pool size (0 = no pool); REINDEX: pool slots */
     int32_t H, D;         /* attention heads and dim (kv row width D) */

@@ -152,7 +152,7 @@ def index_score(qI, w, kI, q_pos=None, m=1, cand=None, want_err=True, scores=Non
     N = kI.shape[1]
     P = cand.shape[-1] if cand is not None else 0
     n = P if cand is not None else N
-    dt = _dt(qI)
+    dt = FP4 if kI.dtype == torch.uint8 else _dt(qI)  # FP4 indexer keys with bf16 queries
     if scores is None:
         scores = torch.empty(B, Q, n, dtype=torch.float32, device=qI.device)
     err = torch.empty(B, Q, dtype=torch.float32, device=qI.device) if want_err else None
@@ -249,7 +249,8 @@ class Layer:
         a.H, a.D, a.q_dt, a.kv_dt, a.scale, a.k = H, D, _dt(q), _dt(kv), float(scale), k
         self.tensors = {"q": q, "kv": kv}
         if mode_i != REUSE:
-            a.HI, a.dI, a.idx_dt = qI.shape[2], qI.shape[3], _dt(qI)
+            a.HI, a.dI = qI.shape[2], qI.shape[3]
+            a.idx_dt = FP4 if kI.dtype == torch.uint8 else _dt(qI)
             self.tensors.update(qI=qI, w=w, kI=kI, q_pos=q_pos)
             if mode_i == FULL:
                 a.P = P

@@ -49,7 +49,9 @@ int guarded(F &&f) {
 
 // ------------------------------------------------------------- indexer
 void check_index_args(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t N, int32_t P) {
-    need_plain_dt(dt, "indexer dtype");
+    if (dt != CSA2_FP4) need_plain_dt(dt, "indexer dtype");
+    if (dt == CSA2_FP4 && !csa2::index_mfma_supported(dt, HI, dI))
+        throw Error(CSA2_EUNSUPPORTED, "FP4 indexer keys need a matrix-core shape with dI % 64 == 0");
     if (B < 1 || Q < 1 || HI < 1 || dI < 1 || N < 1) throw Error(CSA2_EINVAL, "B, Q, HI, dI and N must be >= 1");
     if (N > INT32_MAX || P < 0) throw Error(CSA2_EINVAL, "N must fit int32 and P must be >= 0");
     if (!csa2::index_mfma_supported(dt, HI, dI) && !csa2::index_valu_supported(HI, dI))
@@ -122,7 +124,8 @@ void check_layer(const csa2_layer_args *a) {
     if (a->q_pos && a->m < 1) throw Error(CSA2_EINVAL, "m must be >= 1 with q_pos");
     if (!csa2::rescore_supported(a->idx_dt, a->dI))
         throw Error(CSA2_EUNSUPPORTED, "certified selection needs indexer rows of whole 16-byte vectors "
-                                       "(dI % 4 == 0 for fp32, dI % 8 == 0 for bf16)");
+                                       "(dI % 4 == 0 for fp32, dI % 8 == 0 for bf16, dI % 64 == 0 and "
+                                       "dI <= 256 for FP4 keys)");
     if (a->mode == CSA2_FULL) {
         if (a->P < 0) throw Error(CSA2_EINVAL, "P must be >= 0");
         if (a->P > 0) need_ptr(a->pool, "pool");

@@ -62,7 +62,33 @@ __device__ void reduce_tile_stat(float smin, float smax, uint32_t nval, float km
 // A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16]; the result tile has
 // D[4*(l/16) + r][l%16] in element r.  Both operands use the same lane ->
 // k mapping, so every product pairs q[h][d] with k[j][d] for the same d.
-template <int HI, int DI>
+// FP4 indexer keys (KFP4): rows of DI/2 code bytes and DI/16 E4M3 scale
+// bytes; lane l loads the 4 code bytes of its 8 channels per contraction step
+// and their scale byte, and decodes them to bf16 in registers (exact: at most
+// 6 significant bits), so the matrix-core step and everything after it are
+// the bf16 path's.
+template <int DI>
+__device__ __forceinline__ u32x4 fp4_keys_to_bf16x8(uint32_t word, uint32_t sbyte) {
+    const uint32_t e = (sbyte >> 3) & 15u, mt = sbyte & 7u;
+    float sc = e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0.001953125f;
+    if (sbyte & 0x80u) sc = -sc;
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        uint32_t h[2];
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const uint32_t c = (word >> (8 * i + 4 * k)) & 15u;
+            const uint32_t ce = (c >> 1) & 3u, mb = c & 1u;
+            const uint32_t mag = ce ? (((ce + 126u) << 23) | (mb << 22)) : (mb ? 0x3f000000u : 0u);
+            h[k] = __float_as_uint(__uint_as_float(mag | ((c & 8u) << 28)) * sc) >> 16;  // exact in bf16
+        }
+        r[i] = h[0] | (h[1] << 16);
+    }
+    return r;
+}
+
+template <int HI, int DI, bool KFP4>
 __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restrict__ qI, const float *__restrict__ w,
                                                        const uint16_t *__restrict__ kI, int Q, int64_t N,
                                                        const int64_t *__restrict__ q_pos, int m,
@@ -92,15 +118,27 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
         valid[g] = (j >= 0) && (j < nvis);
         jrow[g] = valid[g] ? j : 0;
     }
-    // Issue every key load of the wave first (64 B per lane per group).
+    // Issue every key load of the wave first (64 B per lane per group; FP4:
+    // 16 code bytes and 4 scale bytes, decoded after the query loads).
     u32x4 kb[G][KS];
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    uint32_t kw4[KFP4 ? G : 1][KS], ks4[KFP4 ? G : 1][KS];
 #pragma unroll
     for (int g = 0; g < G; g++) {
-        const uint16_t *krow = kI + ((size_t)b * N + jrow[g]) * DI + 8 * kg;
+        if constexpr (KFP4) {
+            constexpr int RB = DI / 2 + DI / 16;
+            const uint8_t *krow = reinterpret_cast<const uint8_t *>(kI) + ((size_t)b * N + jrow[g]) * RB;
 #pragma unroll
-        for (int s = 0; s < KS; s++)
-            kb[g][s] = valid[g] ? *reinterpret_cast<const u32x4 *>(krow + 32 * s) : zero;
+            for (int s = 0; s < KS; s++) {
+                kw4[g][s] = valid[g] ? *reinterpret_cast<const uint32_t *>(krow + 16 * s + 4 * kg) : 0u;
+                ks4[g][s] = valid[g] ? (uint32_t)krow[DI / 2 + 2 * s + kg / 2] : 0u;
+            }
+        } else {
+            const uint16_t *krow = kI + ((size_t)b * N + jrow[g]) * DI + 8 * kg;
+#pragma unroll
+            for (int s = 0; s < KS; s++)
+                kb[g][s] = valid[g] ? *reinterpret_cast<const u32x4 *>(krow + 32 * s) : zero;
+        }
     }
     // Query heads (A operand) and the weights of the result rows this lane holds.
     u32x4 qa[HT][KS];
@@ -120,6 +158,10 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
     uint32_t nval = 0;
 #pragma unroll
     for (int g = 0; g < G; g++) {
+        if constexpr (KFP4) {
+#pragma unroll
+            for (int s = 0; s < KS; s++) kb[g][s] = fp4_keys_to_bf16x8<DI>(kw4[g][s], ks4[g][s]);
+        }
         f32x4 acc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -449,7 +491,16 @@ constexpr int64_t STREAM_MIN_TILES = 1024;  // below this, one tile per block fi
 template <int HI, int DI>
 void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, int64_t N, const int64_t *q_pos,
                  int m, const int32_t *cand, int P, float *scores, TileStat *stats, int ntiles, double *sumwq,
-                 hipStream_t s) {
+                 bool kfp4, hipStream_t s) {
+    if (kfp4) {
+        if constexpr (DI % 64 == 0) {
+            dim3 grid(ntiles, B * Q);
+            hipLaunchKernelGGL((k_index_mfma<HI, DI, true>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI),
+                               w, static_cast<const uint16_t *>(kI), Q, N, q_pos, m, cand, P, scores, stats, ntiles,
+                               sumwq);
+        }
+        return;
+    }
     if constexpr (stream_fits(HI, DI)) {
         if (!cand && (int64_t)B * Q * ntiles >= STREAM_MIN_TILES) {
             dim3 grid((ntiles + 3) / 4, B * Q);
@@ -459,14 +510,14 @@ void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, i
         }
     }
     dim3 grid(ntiles, B * Q);
-    hipLaunchKernelGGL((k_index_mfma<HI, DI>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
+    hipLaunchKernelGGL((k_index_mfma<HI, DI, false>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
                        static_cast<const uint16_t *>(kI), Q, N, q_pos, m, cand, P, scores, stats, ntiles, sumwq);
 }
 
 }  // namespace
 
 bool index_mfma_supported(int dt, int HI, int dI) {
-    if (dt != CSA2_BF16) return false;
+    if (dt != CSA2_BF16 && !(dt == CSA2_FP4 && dI % 64 == 0)) return false;
     switch (HI * 1000 + dI) {
         case 16032: case 16064: case 16128: case 16256:
         case 32032: case 32064: case 32128: case 32256:
@@ -488,7 +539,7 @@ void launch_index_score(const void *qI, int dt, const float *w, const void *kI, 
     if (index_mfma_supported(dt, HI, dI)) {
 #define CSA2_IDX_CASE(h, d)                                                                        \
     case h * 1000 + d:                                                                              \
-        launch_mfma<h, d>(qI, w, kI, B, Q, N, q_pos, m, cand, P, scores, stats, ntiles, sumwq, s); \
+        launch_mfma<h, d>(qI, w, kI, B, Q, N, q_pos, m, cand, P, scores, stats, ntiles, sumwq, dt == CSA2_FP4, s); \
         break;
         switch (HI * 1000 + dI) {
             CSA2_IDX_CASE(16, 32) CSA2_IDX_CASE(16, 64) CSA2_IDX_CASE(16, 128) CSA2_IDX_CASE(16, 256)
@@ -508,7 +559,8 @@ void launch_index_score(const void *qI, int dt, const float *w, const void *kI, 
 
 void launch_err_bound(const void *qI, int dt, const float *w, int BQ, int HI, int dI, const TileStat *stats,
                       int ntiles, float *err32, double *err64, hipStream_t s) {
-    hipLaunchKernelGGL(k_err_bound, dim3(BQ), dim3(256), 0, s, qI, dt, w, HI, dI, stats, ntiles, err32, err64);
+    const int qdt = dt == CSA2_FP4 ? CSA2_BF16 : dt;  // FP4 keys come with bf16 queries
+    hipLaunchKernelGGL(k_err_bound, dim3(BQ), dim3(256), 0, s, qI, qdt, w, HI, dI, stats, ntiles, err32, err64);
     check_launch("error bound");
 }
 

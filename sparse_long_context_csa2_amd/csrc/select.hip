@@ -995,6 +995,7 @@ constexpr int RS_VB = 16;      // 16-byte vectors per row batch
 struct RescoreKArgs {
     const void *qI;
     int dt;
+    int kfp4;  // key rows in FP4 (queries bf16)
     const float *w;
     const void *kI;
     int Q, HI, dI;
@@ -1086,13 +1087,31 @@ __global__ __launch_bounds__(RS_NT, 2) void k_sel_rescore(RescoreKArgs a) {
                                          ? spec
                                          : (e < nb0 ? a.band[row0 + e] : a.band[row1 + (e - nb0)]);
                 const int64_t j = a.cand ? (int64_t)a.cand[(int64_t)bq * a.n + slot] : (int64_t)slot;
-                const u32x4 kv = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.kI) +
-                                                                 ((size_t)b * a.N + j) * a.dI * ESZ)[c];
                 double *dst = &krow_lds[i][c * EPV];
+                if (!F32 && a.kfp4) {
+                    // 8 channels: 4 code bytes and their E4M3 scale, decoded exactly
+                    const uint8_t *krow = static_cast<const uint8_t *>(a.kI) +
+                                          ((size_t)b * a.N + j) * (size_t)(a.dI / 2 + a.dI / 16);
+                    const uint32_t cw = *reinterpret_cast<const uint32_t *>(krow + 4 * c);
+                    const uint32_t sb = krow[a.dI / 2 + c / 2];
+                    const uint32_t se = (sb >> 3) & 15u, sm = sb & 7u;
+                    double sc = se ? (double)(8u + sm) * __builtin_ldexp(1.0, (int)se - 10) : (double)sm * 0x1p-9;
+                    if (sb & 0x80u) sc = -sc;
 #pragma unroll
-                for (int x = 0; x < EPV; x++) {
-                    const uint32_t kw = kv[F32 ? x : x >> 1];
-                    dst[x] = (double)__uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
+                    for (int x = 0; x < 8; x++) {
+                        const uint32_t cd = (cw >> (4 * x)) & 15u;
+                        const uint32_t ce = (cd >> 1) & 3u, mb = cd & 1u;
+                        const double mag = ce ? (1.0 + 0.5 * mb) * __builtin_ldexp(1.0, (int)ce - 1) : 0.5 * mb;
+                        dst[x] = ((cd & 8u) ? -mag : mag) * sc;
+                    }
+                } else {
+                    const u32x4 kv = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.kI) +
+                                                                     ((size_t)b * a.N + j) * a.dI * ESZ)[c];
+#pragma unroll
+                    for (int x = 0; x < EPV; x++) {
+                        const uint32_t kw = kv[F32 ? x : x >> 1];
+                        dst[x] = (double)__uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
+                    }
                 }
             }
         }
@@ -1421,7 +1440,10 @@ __global__ __launch_bounds__(FIN_NT) void k_sel_finish(FinishArgs a) {
 
 // ------------------------------------------------------------------ host
 
-bool rescore_supported(int dt, int dI) { return dI >= 1 && (dI * (dt == CSA2_F32 ? 4 : 2)) % 16 == 0; }
+bool rescore_supported(int dt, int dI) {
+    if (dt == CSA2_FP4) return dI % 64 == 0 && dI * 2 <= RS_ROWB;  // staged kernel only
+    return dI >= 1 && (dI * (dt == CSA2_F32 ? 4 : 2)) % 16 == 0;
+}
 
 SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified) {
     SelPlan p;
@@ -1520,6 +1542,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         RescoreKArgs r{};
         r.qI = rs->qI;
         r.dt = rs->dt;
+        r.kfp4 = rs->dt == CSA2_FP4;
         r.w = rs->w;
         r.kI = rs->kI;
         r.Q = rs->Q;

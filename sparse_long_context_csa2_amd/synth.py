@@ -100,7 +100,7 @@ class Decode:
     H: int
     D: int
     k: int
-    idx_dtype: str = "bf16"  # "bf16" or "f32"
+    idx_dtype: str = "bf16"  # "bf16", "f32", or "fp4" (FP4 indexer keys, bf16 queries)
     kv_fmt: str = "bf16"     # "bf16", "f32" or "fp4"
     m: int = 4
     P: int = 0
@@ -120,9 +120,12 @@ def make_decode(spec: Decode) -> dict:
     """Draw, in this order: kI, kv, then per layer (qI, w if the layer runs the
     indexer) and q."""
     rng = np.random.default_rng(spec.seed)
-    idx_draw = normal_bf16 if spec.idx_dtype == "bf16" else normal_f32
+    idx_draw = normal_f32 if spec.idx_dtype == "f32" else normal_bf16
     out = {"spec": spec}
-    out["kI"] = idx_draw(rng, (spec.B, spec.N, spec.dI))
+    if spec.idx_dtype == "fp4":
+        out["kI"] = fp4_rows(rng, (spec.B, spec.N), spec.dI)
+    else:
+        out["kI"] = idx_draw(rng, (spec.B, spec.N, spec.dI))
     if spec.kv_fmt == "fp4":
         out["kv"] = fp4_rows(rng, (spec.B, spec.N), spec.D)
     elif spec.kv_fmt == "bf16":

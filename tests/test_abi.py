@@ -57,8 +57,11 @@ def test_topk_rejects_bad_arguments_without_launching():
 
 def test_index_score_rejects_and_reports_unsupported():
     ws = 1 << 30
-    # dtype not f32/bf16
-    assert b._index(A, A, A, 2, 1, 1, 4, 64, 100, None, 1, None, 0, A2, None, A, ws, None) == 1
+    # unknown dtype
+    assert b._index(A, A, A, 3, 1, 1, 4, 64, 100, None, 1, None, 0, A2, None, A, ws, None) == 1
+    # FP4 keys without a matrix-core shape (HI = 4), and with dI % 64 != 0
+    assert b._index(A, A, A, 2, 1, 1, 4, 64, 100, None, 1, None, 0, A2, None, A, ws, None) == 2
+    assert b._index(A, A, A, 2, 1, 1, 64, 32, 100, None, 1, None, 0, A2, None, A, ws, None) == 2
     # HI * dI beyond every kernel
     assert b._index(A, A, A, 0, 1, 1, 512, 512, 100, None, 1, None, 0, A2, None, A, ws, None) == 2
     # cand with P = 0

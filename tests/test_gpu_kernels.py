@@ -211,3 +211,15 @@ def test_compress_matches_oracle(b, n_out, D, m, halo, dt):
     ref = oracle.compress(x, n_out, m, halo, wz, bias)
     atol, rtol = (ATOL_F32, RTOL_F32) if dt == "f32" else (ATOL_BF16, RTOL_BF16)
     assert_close(out, ref, atol, rtol, "compressed entries")
+
+
+@pytest.mark.parametrize("B,Q,N,HI,dI", [(2, 1, 1000, 64, 128), (1, 2, 777, 16, 64), (1, 1, 513, 32, 256)])
+def test_index_score_fp4_keys_within_reported_bound(b, B, Q, N, HI, dI):
+    rng = np.random.default_rng(N + dI)
+    kI = synth.fp4_rows(rng, (B, N), dI)
+    qI, w = synth.normal_bf16(rng, (B, Q, HI, dI)), synth.uniform_f32(rng, (B, Q, HI))
+    ref = oracle.index_score(qI, w, kI)
+    s, e = b.index_score(dev(qI), dev(w), dev(kI))
+    torch.cuda.synchronize()
+    worst = assert_scores_within_bound(s, e, ref)
+    print(f"max |s - ref| / E = {worst:.3e}")

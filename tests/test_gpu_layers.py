@@ -98,3 +98,13 @@ def test_full_layer_tied_index_keys(b, N, distinct, k):
     reps = torch.arange(N) % distinct
     d["kI"] = d["kI"][:, reps].contiguous()
     run_group(b, d)
+
+
+@pytest.mark.parametrize("N", [20000, 70001])
+def test_fp4_indexer_keys_full_pool_reindex(b, N):
+    """FP4 indexer keys (bf16 queries): Full layer with a pool, Reindex layers in
+    the pool, Reuse; index sets bit-exact.  70,001 entries take the selection
+    path for more than 32,768 slots."""
+    spec = synth.Decode(B=2, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=512, kv_fmt="fp4", P=2048, seed=13,
+                        idx_dtype="fp4", layers=["FULL", "REINDEX", "REUSE"])
+    run_group(b, synth.make_decode(spec))
