@@ -38,8 +38,10 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["decode-128k", "v41-decoder-1m"], default="decode-128k",
+    ap.add_argument("--workload", choices=["decode-128k", "decode-128k-fp4idx", "v41-decoder-1m"],
+                    default="decode-128k",
                     help="decode-128k: one Full layer of the 128K-context decode (the default line); "
+                         "decode-128k-fp4idx: the same with the indexer keys quantized to FP4 on the device; "
                          "v41-decoder-1m: the 20-layer V4.1 decoder schedule at a 1M-token context")
     ap.add_argument("--only", choices=["indexer", "attention", "layer", "copy"], default=None,
                     help="launch only this part, for counter collection (prints no JSON); 'copy' is a plain "
@@ -247,6 +249,14 @@ def main():
     W = WORKLOAD
     scale = W["D"] ** -0.5
     sets = make_sets(torch, max(1, a.sets))
+    fp4idx = a.workload == "decode-128k-fp4idx"
+    if fp4idx:
+        # FP4 indexer keys: the bf16 keys quantized on the device (E2M1 + E4M3 per 16 channels)
+        for s in sets:
+            kI = s["kI"]
+            s["kI"] = b.quantize_fp4(kI.reshape(-1, W["dI"])).reshape(W["B"], W["N"], -1)
+            del kI
+        torch.cuda.synchronize()
     layers = [b.Layer("FULL", q=s["q"], kv=s["kv"], k=W["k"], scale=scale, qI=s["qI"], w=s["w"], kI=s["kI"])
               for s in sets]
     idx_scores = [torch.empty(W["B"], W["Q"], W["N"], dtype=torch.float32, device="cuda") for _ in sets]
@@ -288,7 +298,8 @@ def main():
     t_idx_ms = event_time(torch, run_indexer, reps)
     t_att_ms = event_time(torch, run_attention, reps)
 
-    idx_bytes = (W["B"] * W["N"] * W["dI"] * 2          # keys
+    key_row = (W["dI"] // 2 + W["dI"] // 16) if fp4idx else W["dI"] * 2
+    idx_bytes = (W["B"] * W["N"] * key_row              # keys
                  + W["B"] * W["Q"] * W["HI"] * (W["dI"] * 2 + 4)  # queries, weights
                  + W["B"] * W["Q"] * W["N"] * 4)        # fp32 scores written
     att_bytes = (W["B"] * W["Q"] * W["k"] * (W["D"] * 2 + 4)     # gathered rows + indices
@@ -296,7 +307,7 @@ def main():
     idx_gbs = idx_bytes / (t_idx_ms * 1e-3) / 1e9
     att_gbs = att_bytes / (t_att_ms * 1e-3) / 1e9
     ksrc = src_hash("indexer.hip", "common.h")
-    traffic = traffic_from_profile(ksrc)
+    traffic = None if fp4idx else traffic_from_profile(ksrc)
 
     res = {
         "metric": "decode query-tokens/s at 128K ctx + indexer/gather HBM GB/s as % of peak",
@@ -312,17 +323,21 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "CSA2 Full-layer decode, 128K tokens/seq compressed at m=4 to 32,768 entries, "
-                               "16 seqs x 1 query, indexer 64x128 bf16, top-2048, 64 heads x 512 bf16 shared KV",
+                               "16 seqs x 1 query, indexer 64x128 " + ("FP4 keys (bf16 queries)" if fp4idx else "bf16")
+                               + ", top-2048, 64 heads x 512 bf16 shared KV",
                    "global_batch": W["B"] * W["Q"], "seq_len": W["ctx_tokens"], "input_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": idx_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": idx_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "indexer score (k_index_stream<64,128>)", "algorithmic_bytes": idx_bytes,
+                     "kernel": "indexer score (" + ("k_index_mfma<64,128,FP4 keys>" if fp4idx else "k_index_stream<64,128>")
+                               + ")", "algorithmic_bytes": idx_bytes,
                      "launch_ms": t_idx_ms},
         "gather": {"kernel": "attention (k_attn_mfma<512,bf16> + combine)", "achieved": att_gbs,
                    "frac": att_gbs / HBM_PEAK_GBS, "algorithmic_bytes": att_bytes, "launch_ms": t_att_ms},
         "kernel_src_sha": ksrc,
     }
-    if not a.no_cpu_baseline:
+    if fp4idx:
+        res["metric"] = "decode query-tokens/s at 128K ctx with FP4 indexer keys + indexer HBM GB/s as % of peak"
+    if not a.no_cpu_baseline and not fp4idx:
         import oracle
         res["cpu_baseline"] = cpu_baseline(torch, oracle, sets[0], a.cpu_seconds)
     print(json.dumps(res), flush=True)

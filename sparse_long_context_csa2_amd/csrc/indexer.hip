@@ -67,24 +67,29 @@ __device__ void reduce_tile_stat(float smin, float smax, uint32_t nval, float km
 // and their scale byte, and decodes them to bf16 in registers (exact: at most
 // 6 significant bits), so the matrix-core step and everything after it are
 // the bf16 path's.
+typedef float __attribute__((ext_vector_type(2))) idx_f32x2;
+typedef __bf16 __attribute__((ext_vector_type(2))) idx_bf16x2;  // converted to with round-to-nearest-even
+
 template <int DI>
 __device__ __forceinline__ u32x4 fp4_keys_to_bf16x8(uint32_t word, uint32_t sbyte) {
+    // scale = pow2 * f: the conversion instruction applies the power of two,
+    // an fp32 multiply the mantissa factor f = +-1.mmm (at most 4 significant
+    // bits); every product is exact, and so is its bf16 rounding
     const uint32_t e = (sbyte >> 3) & 15u, mt = sbyte & 7u;
     float sc = e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0.001953125f;
     if (sbyte & 0x80u) sc = -sc;
+    const uint32_t sb = __float_as_uint(sc);
+    const float pow2 = __uint_as_float(sb & 0x7f800000u);
+    const float f = sc == 0.f ? 0.f : __uint_as_float((sb & 0x807fffffu) | 0x3f800000u);
     u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        uint32_t h[2];
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const uint32_t c = (word >> (8 * i + 4 * k)) & 15u;
-            const uint32_t ce = (c >> 1) & 3u, mb = c & 1u;
-            const uint32_t mag = ce ? (((ce + 126u) << 23) | (mb << 22)) : (mb ? 0x3f000000u : 0u);
-            h[k] = __float_as_uint(__uint_as_float(mag | ((c & 8u) << 28)) * sc) >> 16;  // exact in bf16
-        }
-        r[i] = h[0] | (h[1] << 16);
-    }
+    idx_f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, pow2, 0);
+    idx_f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, pow2, 1);
+    idx_f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, pow2, 2);
+    idx_f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, pow2, 3);
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0 * f, idx_bf16x2));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1 * f, idx_bf16x2));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2 * f, idx_bf16x2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v3 * f, idx_bf16x2));
     return r;
 }
 
@@ -126,13 +131,29 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
 #pragma unroll
     for (int g = 0; g < G; g++) {
         if constexpr (KFP4) {
+            // lane group kg holds channels kg DI/4 .. + DI/4 - 1 (step s: + 8 s ..
+            // + 8 s + 7): its DI/8 code bytes and DI/64 scale bytes are contiguous
             constexpr int RB = DI / 2 + DI / 16;
             const uint8_t *krow = reinterpret_cast<const uint8_t *>(kI) + ((size_t)b * N + jrow[g]) * RB;
+            const uint8_t *kc = krow + kg * (DI / 8);
+            if constexpr (RB % 8 == 0 && DI % 64 == 0 && (DI / 8) % 8 == 0) {
 #pragma unroll
-            for (int s = 0; s < KS; s++) {
-                kw4[g][s] = valid[g] ? *reinterpret_cast<const uint32_t *>(krow + 16 * s + 4 * kg) : 0u;
-                ks4[g][s] = valid[g] ? (uint32_t)krow[DI / 2 + 2 * s + kg / 2] : 0u;
+                for (int s = 0; s < KS; s += 2) {
+                    const uint2 v = valid[g] ? *reinterpret_cast<const uint2 *>(kc + 4 * s) : make_uint2(0u, 0u);
+                    kw4[g][s] = v.x;
+                    kw4[g][s + 1] = v.y;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < KS; s++) kw4[g][s] = valid[g] ? *reinterpret_cast<const uint32_t *>(kc + 4 * s) : 0u;
             }
+            const uint8_t *ksc = krow + DI / 2 + kg * (DI / 64);
+            uint32_t sw = 0;
+            if constexpr (DI / 64 == 4) sw = valid[g] ? *reinterpret_cast<const uint32_t *>(ksc) : 0u;
+            else if constexpr (DI / 64 == 2) sw = valid[g] ? (uint32_t)*reinterpret_cast<const uint16_t *>(ksc) : 0u;
+            else sw = valid[g] ? (uint32_t)*ksc : 0u;
+#pragma unroll
+            for (int s = 0; s < KS; s++) ks4[g][s] = (sw >> (8 * (s / 2))) & 0xffu;
         } else {
             const uint16_t *krow = kI + ((size_t)b * N + jrow[g]) * DI + 8 * kg;
 #pragma unroll
@@ -147,7 +168,8 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
     for (int ht = 0; ht < HT; ht++)
 #pragma unroll
         for (int s = 0; s < KS; s++)
-            qa[ht][s] = *reinterpret_cast<const u32x4 *>(qrow + (ht * 16 + col) * DI + 32 * s + 8 * kg);
+            qa[ht][s] = *reinterpret_cast<const u32x4 *>(qrow + (ht * 16 + col) * DI +
+                                                        (KFP4 ? kg * (DI / 4) + 8 * s : 32 * s + 8 * kg));
     float wv[HT][4];
 #pragma unroll
     for (int ht = 0; ht < HT; ht++)
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
 // are kept in LDS and written after the last pass, in coalesced stores;
 // each tile's statistics are the min / max / count of its 4 waves'
 // reductions.
-template <int HI, int DI>
+template <int HI, int DI, bool KFP4>
 __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restrict__ qI, const float *__restrict__ w,
                                                          const uint16_t *__restrict__ kI, int Q, int64_t N,
                                                          const int64_t *__restrict__ q_pos, int m,
@@ -264,6 +286,32 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
         const int64_t j = step0(it) + g * 16 + col;
         return kb0 + (size_t)(j < last ? j : last) * DI;
     };
+    // FP4 keys: lane group kg holds channels kg DI/4 .. + DI/4 - 1 of its row
+    // (contiguous code and scale bytes, see k_index_mfma), decoded to bf16 just
+    // before the group's matrix-core steps
+    constexpr int RB = DI / 2 + DI / 16;
+    const uint8_t *kq0 = reinterpret_cast<const uint8_t *>(kI) + (size_t)b * N * RB;
+    uint32_t kw[KFP4 ? G : 1][KS], kscl[KFP4 ? G : 1];
+    auto load_fp4 = [&](int it, int g) {
+        const int64_t j0 = step0(it) + g * 16 + col;
+        const uint8_t *row = kq0 + (size_t)(j0 < last ? j0 : last) * RB;
+        const uint8_t *kc = row + kg * (DI / 8);
+        if constexpr (RB % 8 == 0 && (DI / 8) % 8 == 0) {
+#pragma unroll
+            for (int s = 0; s < KS; s += 2) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(kc + 4 * s);
+                kw[g][s] = v.x;
+                kw[g][s + 1] = v.y;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KS; s++) kw[g][s] = *reinterpret_cast<const uint32_t *>(kc + 4 * s);
+        }
+        const uint8_t *ksc = row + DI / 2 + kg * (DI / 64);
+        if constexpr (DI / 64 == 4) kscl[g] = *reinterpret_cast<const uint32_t *>(ksc);
+        else if constexpr (DI / 64 == 2) kscl[g] = (uint32_t)*reinterpret_cast<const uint16_t *>(ksc);
+        else kscl[g] = (uint32_t)*ksc;
+    };
     // the query heads first, so that waiting for them never waits for key rows
     // (the guard is compiled out when the pieces split evenly over the block:
     // a conditional load would be sunk below the key loads)
@@ -278,12 +326,16 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
     f32x4 wv[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ht++) wv[ht] = *reinterpret_cast<const f32x4 *>(w + (size_t)bq * HI + ht * 16 + 4 * kg);
-    u32x4 kb[G][KS];
+    u32x4 kb[KFP4 ? 1 : G][KS];
 #pragma unroll
     for (int g = 0; g < G; g++) {
-        const uint16_t *kr = krow(0, g);
+        if constexpr (KFP4) {
+            load_fp4(0, g);
+        } else {
+            const uint16_t *kr = krow(0, g);
 #pragma unroll
-        for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
+            for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
+        }
     }
 #pragma unroll
     for (int i = 0; i < QPT; i++)
@@ -294,7 +346,8 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
     for (int ht = 0; ht < HT; ht++)
 #pragma unroll
         for (int s = 0; s < KS; s++)
-            qa[ht][s] = *reinterpret_cast<const u32x4 *>(qsh + (ht * 16 + col) * DI + 32 * s + 8 * kg);
+            qa[ht][s] = *reinterpret_cast<const u32x4 *>(qsh + (ht * 16 + col) * DI +
+                                                        (KFP4 ? kg * (DI / 4) + 8 * s : 32 * s + 8 * kg));
     if (sumwq && blockIdx.x == 0 && wave == 0) {
         // sum_h |w_h| ||q_h|| in binary64 from the query fragments in
         // registers (lane (col, kg) holds 8 KS elements of head 16 ht + col),
@@ -327,6 +380,12 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
         float part[G], ss[G];
 #pragma unroll
         for (int g = 0; g < G; g++) {
+            u32x4 kd[KS];  // this group's key fragments
+#pragma unroll
+            for (int s = 0; s < KS; s++) {
+                if constexpr (KFP4) kd[s] = fp4_keys_to_bf16x8<DI>(kw[g][s], (kscl[g] >> (8 * (s / 2))) & 0xffu);
+                else kd[s] = kb[g][s];
+            }
             f32x4 acc[HT];
 #pragma unroll
             for (int ht = 0; ht < HT; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -335,21 +394,25 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
 #pragma unroll
                 for (int ht = 0; ht < HT; ht++)
                     acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ht][s]),
-                                                                      __builtin_bit_cast(bf16x8, kb[g][s]),
+                                                                      __builtin_bit_cast(bf16x8, kd[s]),
                                                                       acc[ht], 0, 0, 0);
             float q2 = 0.f;
 #pragma unroll
             for (int s = 0; s < KS; s++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    bf16x2 v = __builtin_bit_cast(bf16x2, kb[g][s][e]);
+                    bf16x2 v = __builtin_bit_cast(bf16x2, kd[s][e]);
                     q2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, q2, false);
                 }
             ss[g] = q2;
             if (it + 1 < IT) {  // this group's rows of the next pass
-                const uint16_t *kr = krow(it + 1, g);
+                if constexpr (KFP4) {
+                    load_fp4(it + 1, g);
+                } else {
+                    const uint16_t *kr = krow(it + 1, g);
 #pragma unroll
-                for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
+                    for (int s = 0; s < KS; s++) kb[g][s] = *reinterpret_cast<const u32x4 *>(kr + 32 * s);
+                }
             }
             float p = 0.f;
 #pragma unroll
@@ -494,6 +557,15 @@ void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, i
                  bool kfp4, hipStream_t s) {
     if (kfp4) {
         if constexpr (DI % 64 == 0) {
+            if constexpr (stream_fits(HI, DI)) {
+                if (!cand && (int64_t)B * Q * ntiles >= STREAM_MIN_TILES) {
+                    dim3 grid((ntiles + 3) / 4, B * Q);
+                    hipLaunchKernelGGL((k_index_stream<HI, DI, true>), grid, dim3(256), 0, s,
+                                       static_cast<const uint16_t *>(qI), w, static_cast<const uint16_t *>(kI), Q, N,
+                                       q_pos, m, scores, stats, ntiles, sumwq);
+                    return;
+                }
+            }
             dim3 grid(ntiles, B * Q);
             hipLaunchKernelGGL((k_index_mfma<HI, DI, true>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI),
                                w, static_cast<const uint16_t *>(kI), Q, N, q_pos, m, cand, P, scores, stats, ntiles,
@@ -504,7 +576,7 @@ void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, i
     if constexpr (stream_fits(HI, DI)) {
         if (!cand && (int64_t)B * Q * ntiles >= STREAM_MIN_TILES) {
             dim3 grid((ntiles + 3) / 4, B * Q);
-            hipLaunchKernelGGL((k_index_stream<HI, DI>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
+            hipLaunchKernelGGL((k_index_stream<HI, DI, false>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
                                static_cast<const uint16_t *>(kI), Q, N, q_pos, m, scores, stats, ntiles, sumwq);
             return;
         }
