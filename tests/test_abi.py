@@ -99,3 +99,29 @@ def test_layer_mode_pointer_mismatch():
     need = b._layer_ws(ctypes.byref(a))
     assert need > 0
     assert b._layer(ctypes.byref(a), A, need - 256, None) == 3   # workspace one block short
+
+
+def test_swa_merge_and_quantize_validation():
+    ws = 1 << 30
+    assert b._swa_ws(b.BF16, b.BF16, 2, 1, 64, 512, 128) >= 2 * 64 * 512 * 2   # the window branch's own output
+    assert b._swa_ws(b.BF16, b.BF16, 2, 1, 64, 512, 0) == 0
+    # csa2_swa_attn(q, swa_kv, q_dt, kv_dt, B, Q, H, D, T, q_pos, W, scale, csa_out, csa_lse, out, lse, ws, bytes, s)
+    assert b._swa(A, A, b.BF16, b.BF16, 1, 1, 64, 512, 100, A, 0, 0.1, None, None, A2, None, A, ws, None) == 1  # W = 0
+    assert b._swa(A, A, b.BF16, b.BF16, 1, 1, 64, 512, 100, A, 128, 0.1, A, None, A2, None, A, ws, None) == 1  # lse missing
+    assert b._swa(A, A, b.BF16, b.BF16, 1, 1, 64, 512, 100, None, 128, 0.1, None, None, A2, None, A, ws, None) == 1
+    assert b._swa(MIS, A, b.BF16, b.BF16, 1, 1, 64, 512, 100, A, 128, 0.1, None, None, A2, None, A, ws, None) == 1
+    assert b._swa(A, A, b.BF16, b.FP4, 1, 1, 64, 40, 100, A, 128, 0.1, None, None, A2, None, A, ws, None) == 1
+    assert b._swa(A, A, b.BF16, b.BF16, 1, 1, 64, 512, 100, A, 128, 0.1, None, None, A2, None, A, 16, None) == 3
+    # csa2_merge_attn(o_a, lse_a, o_b, lse_b, dt, R, D, out, lse, s)
+    assert b._merge(A, A, A, A, b.BF16, 10, 12, A2, None, None) == 1       # D % 8
+    assert b._merge(A, A, A, A, b.BF16, 0, 64, A2, None, None) == 1        # R = 0
+    assert b._merge(A, A, A, A, b.FP4, 10, 64, A2, None, None) == 1        # not a plain dtype
+    assert b._merge(A, None, A, A, b.BF16, 10, 64, A2, None, None) == 1    # lse_a NULL
+    # csa2_quantize_fp4(x, dt, n, D, cache, dst_row, s)
+    assert b._quant(A, b.BF16, 10, 24, A2, None, None) == 1                # D % 16
+    assert b._quant(A, b.BF16, 0, 64, A2, None, None) == 1                 # n = 0
+    assert b._quant(A, b.FP4, 10, 64, A2, None, None) == 1                 # FP4 input
+    assert b._quant(None, b.BF16, 10, 64, A2, None, None) == 1             # x NULL
+    assert b._quant(A, b.BF16, 10, 64, None, None, None) == 1              # cache NULL
+    assert b._quant(A, b.BF16, 10, 64, A2, MIS, None) == 1                 # dst_row misaligned
+    assert "aligned" in b._last_error().decode()
