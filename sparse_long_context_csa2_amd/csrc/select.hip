@@ -1560,10 +1560,11 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         if (rowb <= RS_ROWB) {
             // about 256 entries per query per round at 32,768 slots, more for longer
             // rows of scores (the band grows with the density of scores); the grid
-            // stays small enough to be resident at once, and idle blocks exit at once
+            // stays resident at once (two blocks per CU: longer bands loop over
+            // rounds instead of queueing blocks), and idle blocks exit at once
             int64_t want = (int64_t)256 * ((p.n + ONE_N - 1) / ONE_N);
             int nblk = (int)((want < 1024 ? want : 1024) / RS_EPB);
-            if ((int64_t)nblk * p.BQ > 2048) nblk = (int)(2048 / p.BQ) > 1 ? (int)(2048 / p.BQ) : 1;
+            if ((int64_t)nblk * p.BQ > 512) nblk = (int)(512 / p.BQ) > 1 ? (int)(512 / p.BQ) : 1;
             if (rs->dt == CSA2_F32) hipLaunchKernelGGL(k_sel_rescore<true>, dim3(nblk, p.BQ), dim3(RS_NT), 0, s, r);
             else hipLaunchKernelGGL(k_sel_rescore<false>, dim3(nblk, p.BQ), dim3(RS_NT), 0, s, r);
         } else {
