@@ -116,3 +116,37 @@ def test_prefill_chunk_sampled_rows(b):
     assert np.array_equal(host(L.count)[:, rows].numpy(), r["count"])
     assert_close(host(L.out)[:, rows], r["out"], ATOL_BF16, RTOL_BF16, "prefill output rows")
     assert_close(host(L.lse)[:, rows], r["lse"], ATOL_BF16, RTOL_BF16, "prefill lse rows")
+
+
+def test_decode_128k_fp4_indexer_keys(b):
+    """The 128K decode Full layer (16 x 32,768 entries, top-2048) with the
+    indexer keys in FP4: index sets bit-exact for every query."""
+    import dataclasses
+    run_group(b, synth.make_decode(dataclasses.replace(synth.decode_128k(seed=6), idx_dtype="fp4")))
+
+
+def test_swa_branch_merged_decode_shape(b):
+    """The SWA branch at the decode shape (16 queries, 64 heads x 512, window
+    128) merged into a top-2048 CSA2 branch over FP4 KV, against the oracle's
+    single softmax over both row sets."""
+    import math
+    rng = np.random.default_rng(31)
+    B, H, D, N, k, T, W = 16, 64, 512, 4096, 2048, 1000, 128
+    kv = synth.fp4_rows(rng, (B, N), D)
+    swa = synth.normal_bf16(rng, (B, T, D))
+    q = synth.normal_bf16(rng, (B, 1, H, D))
+    idx = torch.from_numpy(np.sort(np.stack([rng.choice(N, size=k, replace=False) for _ in range(B)]),
+                                   axis=-1).astype(np.int32)[:, None, :])
+    pos = torch.from_numpy(rng.integers(0, T, size=(B, 1)).astype(np.int64))
+    pos[0, 0], pos[1, 0] = 0, T - 1
+    scale = 1 / math.sqrt(D)
+    dec = torch.from_numpy(oracle.decode_rows(kv, D)).to(torch.bfloat16)          # exact
+    win = torch.from_numpy(oracle.window_idx(pos, W))
+    union = torch.cat([idx, torch.where(win >= 0, win + N, win)], dim=-1)
+    ro, rl = oracle.sparse_attn(q, torch.cat([dec, swa], dim=1), union, scale)
+    qd = dev(q)
+    co, cl = b.sparse_attn(qd, dev(kv), dev(idx), scale, D=D)
+    out, lse = b.swa_attn(qd, dev(swa), dev(pos), W, scale, csa_out=co, csa_lse=cl, out=co)
+    torch.cuda.synchronize()
+    assert_close(out, ro, ATOL_BF16, RTOL_BF16, "merged out")
+    assert_close(lse, rl, ATOL_BF16, RTOL_BF16, "merged lse")
