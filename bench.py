@@ -328,7 +328,7 @@ def main():
                    "global_batch": W["B"] * W["Q"], "seq_len": W["ctx_tokens"], "input_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": idx_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": idx_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "indexer score (" + ("k_index_mfma<64,128,FP4 keys>" if fp4idx else "k_index_stream<64,128>")
+                     "kernel": "indexer score (" + ("k_index_stream<64,128,FP4 keys>" if fp4idx else "k_index_stream<64,128>")
                                + ")", "algorithmic_bytes": idx_bytes,
                      "launch_ms": t_idx_ms},
         "gather": {"kernel": "attention (k_attn_mfma<512,bf16> + combine)", "achieved": att_gbs,

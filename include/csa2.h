@@ -15,7 +15,8 @@
  *  - Temporary memory comes only from the caller's workspace (ws, ws_bytes),
  *    sized by the matching *_workspace_size function; NULL with 0 bytes is
  *    allowed when that function returns 0.  Workspace must be 256-byte aligned.
- *  - `stream` is the caller's hipStream_t (NULL = the default stream).  Work is
+ *  - `stream` is the caller's hipStream_t passed as void * (so that this header
+ *    needs no HIP include; NULL = the default stream).  Work is
  *    enqueued asynchronously on it; no call synchronises with the host, and no
  *    call records a memset node, so a call may be captured into a HIP graph.
  *  - Return value: CSA2_OK, or an error status.  Arguments are validated before
@@ -24,8 +25,11 @@
  *    message of the last failure on the calling thread is csa2_last_error().
  *    No C++ exception crosses this interface.
  *  - Preconditions that are documented but not checked: floating inputs are
- *    finite; E4M3 scale bytes are not NaN; outputs do not alias inputs; the
- *    stream is valid on the current device.
+ *    finite; outputs do not alias inputs; candidate rows are strictly
+ *    ascending over their non-negative entries; the stream is valid on the
+ *    current device.
+ *  - B * Q (query rows per call) is at most 65535; larger calls return
+ *    CSA2_EUNSUPPORTED before anything is enqueued.
  *  - Calls that overlap on one stream are ordered by that stream; concurrent
  *    calls on different streams must use different workspaces.
  */
@@ -58,8 +62,12 @@ typedef enum {
  *   covering channels 16b..16b+15.  Value = e2m1(code) * e4m3(scale), which
  *   is exactly representable in bf16.  ("Recall之王 祭出Reuse", section
  *   "把KV Cache压到极致的几把杀手锏": FP4 main KV cache, E2M1 with one E4M3
- *   scale per 16 channels.)  Main KV only. */
-typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_FP4 = 2 } csa2_dtype;
+ *   scale per 16 channels.)  Every scale byte is accepted: zero and negative
+ *   zero, subnormals and sign-set bytes are their E4M3 values; the E4M3 NaN
+ *   code S.1111.111 (never written by csa2_quantize_fp4) saturates to +-448.
+ *   Main KV, and indexer keys (csa2_index_score).
+ *   CSA2_FP4E2M1_S16E4M3 is the same format under its descriptive name. */
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_FP4 = 2, CSA2_FP4E2M1_S16E4M3 = 2 } csa2_dtype;
 
 /* Layer modes (V4.1 Flash video transcript on prism.simon-ai.net, the passage
  * introducing CSA2's three modes; "Recall之王 祭出Reuse", same section):
@@ -160,7 +168,10 @@ CSA2_API int csa2_index_score(const void *qI, const float *w, const void *kI, in
  *
  * scores [B,Q,n] fp32; cand [B,Q,n] or NULL (entry index of slot p is cand[p],
  *   else p; cand rows must be strictly ascending over their non-negative
- *   entries, which the pool produced by csa2_layer is).
+ *   entries, which the pool produced by csa2_layer is -- not checked).
+ *   A slot a query may not select (past its visible count, or an empty
+ *   candidate) is given as a -inf score, which is how csa2_index_score marks
+ *   invisible entries; there is no separate per-query valid count.
  * idx [B,Q,k] int32 out; count [B,Q] int32 out or NULL.  1 <= k.
  * The result is bit-exact (pure comparison, no arithmetic on the scores).
  * ------------------------------------------------------------------------- */
@@ -235,7 +246,10 @@ typedef struct {
 } csa2_layer_args;
 
 CSA2_API size_t csa2_layer_workspace_size(const csa2_layer_args *a);
+/* The same size under its short name. */
+CSA2_API size_t csa2_workspace_size(const csa2_layer_args *a);
 CSA2_API int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream);
+
 
 /* ---------------------------------------------------------------------------
  * csa2_swa_attn -- the sliding-window (SWA) branch, optionally merged with the

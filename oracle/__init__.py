@@ -35,6 +35,7 @@ def _lib():
         c_void_p, c_int, c_int64, c_double = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.ora_e2m1.argtypes, lib.ora_e2m1.restype = [ctypes.c_uint], c_double
         lib.ora_e4m3.argtypes, lib.ora_e4m3.restype = [ctypes.c_uint], c_double
+        lib.ora_fp4_scale.argtypes, lib.ora_fp4_scale.restype = [ctypes.c_uint], c_double
         lib.ora_decode_row.argtypes = [c_void_p, c_int, c_int, c_void_p]
         lib.ora_compress.argtypes = [c_void_p, c_int, c_int64, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]
         lib.ora_index_score.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
@@ -122,6 +123,12 @@ def e2m1(code: int) -> float:
 def e4m3(byte: int) -> float:
     """Value of an E4M3 ("FN") byte (OCP 8-bit floating point)."""
     return _lib().ora_e4m3(byte)
+
+
+def fp4_scale(byte: int) -> float:
+    """Value of an FP4 row's scale byte: its E4M3 value, except that the NaN
+    code S.1111.111 saturates to +-448 (a reading: the pages give no rule)."""
+    return _lib().ora_fp4_scale(byte)
 
 
 def decode_rows(rows, D: int) -> np.ndarray:

@@ -81,6 +81,20 @@ double ora_e4m3(unsigned byte)
     return (byte & 0x80u) ? -mag : mag;
 }
 
+/* An FP4 row's scale byte as a value.  E4M3FN's NaN code (S.1111.111) is not a
+ * scale any quantizer writes (the largest finite magnitude is 448 = S.1111.110);
+ * reading taken for it: the scale saturates to +-448, the largest finite value
+ * of the format, so that a corrupted byte cannot turn a whole group, or every
+ * score and attention output that touches it, into NaN.  Every other byte is
+ * its E4M3FN value. */
+double ora_fp4_scale(unsigned byte)
+{
+    double s = ora_e4m3(byte);
+    if (isnan(s))
+        return (byte & 0x80u) ? -448.0 : 448.0;
+    return s;
+}
+
 /* Bytes per stored KV row of width D in format dt. An FP4 row is D/2 code
  * bytes (channel 2i in the low nibble of byte i, channel 2i+1 in the high
  * nibble) followed by D/16 E4M3 scale bytes (scale b covers channels
@@ -103,7 +117,7 @@ void ora_decode_row(const void *row, int dt, int D, double *out)
         for (int c = 0; c < D; c++) {
             uint8_t byte = codes[c / 2];
             unsigned code = (c % 2 == 0) ? (byte & 15u) : (byte >> 4);
-            out[c] = ora_e2m1(code) * ora_e4m3(scales[c / 16]);
+            out[c] = ora_e2m1(code) * ora_fp4_scale(scales[c / 16]);
         }
         return;
     }

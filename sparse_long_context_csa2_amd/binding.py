@@ -64,6 +64,7 @@ _swa = _sig("csa2_swa_attn", ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.c_int
 _quant = _sig("csa2_quantize_fp4", ctypes.c_int, [_vp, ctypes.c_int, _i64, _i32, _vp, _vp, _vp])
 _merge = _sig("csa2_merge_attn", ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _vp, _vp, _vp])
 _layer_ws = _sig("csa2_layer_workspace_size", _sz, [ctypes.POINTER(LayerArgs)])
+_ws_alias = _sig("csa2_workspace_size", _sz, [ctypes.POINTER(LayerArgs)])
 _layer = _sig("csa2_layer", ctypes.c_int, [ctypes.POINTER(LayerArgs), _vp, _sz, _vp])
 _last_error = _sig("csa2_last_error", ctypes.c_char_p, [])
 _version = _sig("csa2_version", ctypes.c_char_p, [])
@@ -71,7 +72,7 @@ _version = _sig("csa2_version", ctypes.c_char_p, [])
 EXPORTS = ["csa2_compress_workspace_size", "csa2_compress", "csa2_index_score_workspace_size", "csa2_index_score",
            "csa2_topk_workspace_size", "csa2_topk", "csa2_sparse_attn_workspace_size", "csa2_sparse_attn",
            "csa2_swa_attn_workspace_size", "csa2_swa_attn", "csa2_merge_attn", "csa2_quantize_fp4",
-           "csa2_layer_workspace_size", "csa2_layer", "csa2_last_error", "csa2_version"]
+           "csa2_layer_workspace_size", "csa2_workspace_size", "csa2_layer", "csa2_last_error", "csa2_version"]
 
 
 class Csa2Error(RuntimeError):
@@ -238,12 +239,29 @@ class Layer:
     """One prepared csa2_layer call: outputs and workspace allocated once, so
     ``run()`` only launches (graph-capturable, no allocation)."""
 
-    def __init__(self, mode, *, q, kv, k, scale, qI=None, w=None, kI=None, q_pos=None, m=1, P=0, pool=None,
+    def __init__(self, mode, *, q, kv, k=None, scale, qI=None, w=None, kI=None, q_pos=None, m=1, P=0, pool=None,
                  idx=None, keep_scores=False, want_lse=True, count=True, out=None):
         mode_i = MODES[mode] if isinstance(mode, str) else mode
-        _dev(q, kv, qI, w, kI, q_pos, pool, idx)
+        _dev(q, kv, qI, w, kI, q_pos, pool, idx, out)
         B, Q, H, D = q.shape
         dev = q.device
+        # the library takes k and P as the row strides of idx and pool: tensors
+        # given by the caller must have exactly those shapes
+        if mode_i == REUSE and idx is not None and k is None:
+            k = idx.shape[-1]
+        if idx is not None and tuple(idx.shape) != (B, Q, k):
+            raise ValueError(f"idx has shape {tuple(idx.shape)}, expected {(B, Q, k)}")
+        if pool is not None and mode_i == FULL and tuple(pool.shape) != (B, Q, P):
+            raise ValueError(f"pool has shape {tuple(pool.shape)}, expected {(B, Q, P)}")
+        if pool is not None and (pool.dim() != 3 or tuple(pool.shape[:2]) != (B, Q)):
+            raise ValueError(f"pool has shape {tuple(pool.shape)}, expected ({B}, {Q}, P)")
+        if out is not None and tuple(out.shape) != tuple(q.shape):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(q.shape)}")
+        for name, t in (("idx", idx), ("pool", pool)):
+            if t is not None and t.dtype != torch.int32:
+                raise TypeError(f"{name} must be int32")
+        if kv.dim() != 3 or kv.shape[0] != B:
+            raise ValueError(f"kv has shape {tuple(kv.shape)}, expected ({B}, N, row)")
         a = LayerArgs()
         a.mode, a.B, a.Q, a.N, a.m = mode_i, B, Q, kv.shape[1], m
         a.H, a.D, a.q_dt, a.kv_dt, a.scale, a.k = H, D, _dt(q), _dt(kv), float(scale), k

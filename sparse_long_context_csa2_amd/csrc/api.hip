@@ -47,6 +47,15 @@ int guarded(F &&f) {
     }
 }
 
+// Queries (B * Q) index the second grid dimension of the indexer, selection
+// and vector-attention launches: checked here, before anything is enqueued.
+constexpr int64_t MAX_QUERIES = 65535;
+void check_queries(int32_t B, int32_t Q) {
+    if ((int64_t)B * Q > MAX_QUERIES)
+        throw Error(CSA2_EUNSUPPORTED, "B * Q = " + std::to_string((int64_t)B * Q) + " query rows; at most " +
+                                           std::to_string(MAX_QUERIES) + " per call");
+}
+
 // ------------------------------------------------------------- indexer
 void check_index_args(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t N, int32_t P) {
     if (dt != CSA2_FP4) need_plain_dt(dt, "indexer dtype");
@@ -54,6 +63,7 @@ void check_index_args(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int6
         throw Error(CSA2_EUNSUPPORTED, "FP4 indexer keys need a matrix-core shape with dI % 64 == 0");
     if (B < 1 || Q < 1 || HI < 1 || dI < 1 || N < 1) throw Error(CSA2_EINVAL, "B, Q, HI, dI and N must be >= 1");
     if (N > INT32_MAX || P < 0) throw Error(CSA2_EINVAL, "N must fit int32 and P must be >= 0");
+    check_queries(B, Q);
     if (!csa2::index_mfma_supported(dt, HI, dI) && !csa2::index_valu_supported(HI, dI))
         throw Error(CSA2_EUNSUPPORTED, "no indexer kernel for HI*dI > 16384 with this shape");
     if (dt == CSA2_BF16 && dI % 8) throw Error(CSA2_EINVAL, "bf16 indexer rows need dI % 8 == 0");
@@ -101,6 +111,7 @@ void check_layer(const csa2_layer_args *a) {
         throw Error(CSA2_EINVAL, "unknown mode");
     if (a->B < 1 || a->Q < 1 || a->N < 1 || a->k < 1 || a->H < 1 || a->D < 1)
         throw Error(CSA2_EINVAL, "B, Q, N, k, H and D must be >= 1");
+    check_queries(a->B, a->Q);
     need_ptr(a->q, "q");
     need_ptr(a->kv, "kv");
     need_ptr(a->out, "out");
@@ -135,6 +146,36 @@ void check_layer(const csa2_layer_args *a) {
         need_ptr(a->pool, "pool");
         check_index_args(a->idx_dt, a->B, a->Q, a->HI, a->dI, a->N, a->P);
     }
+}
+
+// The layer's launches, with scratch carved from ws (at least z.total bytes).
+void run_layer(const csa2_layer_args *a, const LayerSizes &z, void *ws, size_t ws_bytes, void *stream) {
+    hipStream_t s = (hipStream_t)stream;
+    csa2::Carve c(ws, ws_bytes);
+    if (a->mode != CSA2_REUSE) {
+        const int BQ = a->B * a->Q;
+        float *scores = a->scores ? a->scores : c.take<float>((size_t)BQ * z.n);
+        auto *stats = c.take<csa2::TileStat>((size_t)BQ * z.sel.ntiles);
+        auto *sumwq = c.take<double>((size_t)BQ);
+        void *selws = c.base + c.used;
+        c.used += z.selws;
+        const int32_t *cand = a->mode == CSA2_REINDEX ? a->pool : nullptr;
+        csa2::launch_index_score(a->qI, a->idx_dt, a->w, a->kI, a->B, a->Q, a->HI, a->dI, a->N, a->q_pos, a->m,
+                                 cand, cand ? a->P : 0, scores, stats, sumwq, s);
+        const csa2::RescoreArgs rs{a->qI, a->idx_dt, a->w, a->kI, a->Q, a->HI, a->dI, a->N, sumwq};
+        // the top-k's final pick and compaction run in the attention kernel's prologue when both sides allow
+        const bool fuse = csa2::sel_handoff_supported(z.sel) && csa2::attn_handoff_supported(z.att, z.sel.nwords);
+        csa2::SelHandoff h{};
+        csa2::sel_run(z.sel, scores, cand, stats, &rs, a->idx, a->count,
+                      a->mode == CSA2_FULL && a->P > 0 ? a->pool : nullptr, selws, z.selws, s, fuse ? &h : nullptr);
+        if (fuse) {
+            void *attws = c.base + c.used;
+            csa2::attn_run(z.att, a->q, a->kv, a->idx, a->scale, a->out, a->lse, attws, z.attws, s, &h);
+            return;
+        }
+    }
+    void *attws = c.base + c.used;
+    csa2::attn_run(z.att, a->q, a->kv, a->idx, a->scale, a->out, a->lse, attws, z.attws, s);
 }
 
 }  // namespace
@@ -209,6 +250,7 @@ int csa2_topk(const float *scores, int32_t B, int32_t Q, int64_t n, const int32_
     return guarded([&] {
         if (B < 1 || Q < 1 || n < 1 || k < 1) throw Error(CSA2_EINVAL, "B, Q, n and k must be >= 1");
         if (n > INT32_MAX) throw Error(CSA2_EINVAL, "n must fit int32");
+        check_queries(B, Q);
         need_ptr(scores, "scores");
         need_ptr(idx, "idx");
         opt_ptr(cand, "cand");
@@ -231,6 +273,7 @@ int csa2_sparse_attn(const void *q, const void *kv, int q_dt, int kv_dt, int32_t
     return guarded([&] {
         if (B < 1 || Q < 1 || H < 1 || D < 1 || N < 1 || k < 1)
             throw Error(CSA2_EINVAL, "B, Q, H, D, N and k must be >= 1");
+        check_queries(B, Q);
         need_plain_dt(q_dt, "q dtype");
         if (kv_dt != CSA2_F32 && kv_dt != CSA2_BF16 && kv_dt != CSA2_FP4) throw Error(CSA2_EINVAL, "unknown kv format");
         if (kv_dt == CSA2_FP4 && (D % 16 || q_dt != CSA2_BF16))
@@ -278,6 +321,7 @@ int csa2_swa_attn(const void *q, const void *swa_kv, int q_dt, int kv_dt, int32_
     return guarded([&] {
         if (B < 1 || Q < 1 || H < 1 || D < 1 || T < 1 || W < 1)
             throw Error(CSA2_EINVAL, "B, Q, H, D, T and W must be >= 1");
+        check_queries(B, Q);
         need_plain_dt(q_dt, "q dtype");
         if (kv_dt != CSA2_F32 && kv_dt != CSA2_BF16 && kv_dt != CSA2_FP4) throw Error(CSA2_EINVAL, "unknown kv format");
         if (kv_dt == CSA2_FP4 && (D % 16 || q_dt != CSA2_BF16))
@@ -348,40 +392,18 @@ int csa2_quantize_fp4(const void *x, int dt, int64_t n, int32_t D, void *cache, 
 
 size_t csa2_layer_workspace_size(const csa2_layer_args *a) {
     if (!a || a->B < 1 || a->Q < 1 || a->k < 1 || a->H < 1 || a->D < 1) return 0;
+    if ((int64_t)a->B * a->Q > MAX_QUERIES) return 0;
     return layer_sizes(a).total;
 }
+
+size_t csa2_workspace_size(const csa2_layer_args *a) { return csa2_layer_workspace_size(a); }
 
 int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream) {
     return guarded([&] {
         check_layer(a);
         const LayerSizes z = layer_sizes(a);
         need_ws(ws, ws_bytes, z.total);
-        hipStream_t s = (hipStream_t)stream;
-        csa2::Carve c(ws, ws_bytes);
-        if (a->mode != CSA2_REUSE) {
-            const int BQ = a->B * a->Q;
-            float *scores = a->scores ? a->scores : c.take<float>((size_t)BQ * z.n);
-            auto *stats = c.take<csa2::TileStat>((size_t)BQ * z.sel.ntiles);
-            auto *sumwq = c.take<double>((size_t)BQ);
-            void *selws = c.base + c.used;
-            c.used += z.selws;
-            const int32_t *cand = a->mode == CSA2_REINDEX ? a->pool : nullptr;
-            csa2::launch_index_score(a->qI, a->idx_dt, a->w, a->kI, a->B, a->Q, a->HI, a->dI, a->N, a->q_pos, a->m,
-                                     cand, cand ? a->P : 0, scores, stats, sumwq, s);
-            const csa2::RescoreArgs rs{a->qI, a->idx_dt, a->w, a->kI, a->Q, a->HI, a->dI, a->N, sumwq};
-            // the top-k's final pick and compaction run in the attention kernel's prologue when both sides allow
-            const bool fuse = csa2::sel_handoff_supported(z.sel) && csa2::attn_handoff_supported(z.att, z.sel.nwords);
-            csa2::SelHandoff h{};
-            csa2::sel_run(z.sel, scores, cand, stats, &rs, a->idx, a->count,
-                          a->mode == CSA2_FULL && a->P > 0 ? a->pool : nullptr, selws, z.selws, s, fuse ? &h : nullptr);
-            if (fuse) {
-                void *attws = c.base + c.used;
-                csa2::attn_run(z.att, a->q, a->kv, a->idx, a->scale, a->out, a->lse, attws, z.attws, s, &h);
-                return;
-            }
-        }
-        void *attws = c.base + c.used;
-        csa2::attn_run(z.att, a->q, a->kv, a->idx, a->scale, a->out, a->lse, attws, z.attws, s);
+        run_layer(a, z, ws, ws_bytes, stream);
     });
 }
 

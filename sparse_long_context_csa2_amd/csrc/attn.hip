@@ -38,10 +38,12 @@ __device__ __forceinline__ uint32_t e2m1_bits(uint32_t c) {
     const uint32_t mag = e ? (((e + 126u) << 23) | (mb << 22)) : (mb ? 0x3f000000u : 0u);
     return mag | ((c & 8u) << 28);
 }
-// E4M3 ("FN") byte -> float (bias 7; exponent field 0 is m * 2^-9).
+// FP4 row scale byte -> float: its E4M3 ("FN") value (bias 7; exponent field
+// 0 is m * 2^-9), except the NaN code S.1111.111, which saturates to +-448.
 __device__ __forceinline__ float e4m3_val(uint32_t s) {
     const uint32_t e = (s >> 3) & 15u, mt = s & 7u;
-    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0.001953125f;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0.001953125f;
+    if ((s & 0x7fu) == 0x7fu) mag = 448.f;
     return (s & 0x80u) ? -mag : mag;
 }
 __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
@@ -951,7 +953,10 @@ AttnPlan attn_plan(int q_dt, int kv_dt, int B, int Q, int H, int D, int64_t N, i
     return p;
 }
 
-bool attn_supported(const AttnPlan &p) { return p.mfma || (p.D + p.k) <= 16384; }
+bool attn_supported(const AttnPlan &p) {
+    if (p.mfma) return (int64_t)p.B * p.Q * p.nsplit * (p.H / 16) + 8 * (p.H / 16) <= INT32_MAX;  // blocks fit an int
+    return (p.D + p.k) <= 16384;
+}
 
 size_t attn_workspace(const AttnPlan &p) {
     if (!p.mfma || p.nsplit == 1) return 0;

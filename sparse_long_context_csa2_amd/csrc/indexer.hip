@@ -75,8 +75,10 @@ __device__ __forceinline__ u32x4 fp4_keys_to_bf16x8(uint32_t word, uint32_t sbyt
     // scale = pow2 * f: the conversion instruction applies the power of two,
     // an fp32 multiply the mantissa factor f = +-1.mmm (at most 4 significant
     // bits); every product is exact, and so is its bf16 rounding
+    // (the E4M3 NaN code S.1111.111 saturates to +-448)
     const uint32_t e = (sbyte >> 3) & 15u, mt = sbyte & 7u;
     float sc = e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0.001953125f;
+    if ((sbyte & 0x7fu) == 0x7fu) sc = 448.f;
     if (sbyte & 0x80u) sc = -sc;
     const uint32_t sb = __float_as_uint(sc);
     const float pow2 = __uint_as_float(sb & 0x7f800000u);

@@ -1096,6 +1096,7 @@ __global__ __launch_bounds__(RS_NT, 2) void k_sel_rescore(RescoreKArgs a) {
                     const uint32_t sb = krow[a.dI / 2 + c / 2];
                     const uint32_t se = (sb >> 3) & 15u, sm = sb & 7u;
                     double sc = se ? (double)(8u + sm) * __builtin_ldexp(1.0, (int)se - 10) : (double)sm * 0x1p-9;
+                    if ((sb & 0x7fu) == 0x7fu) sc = 448.0;  // the E4M3 NaN code saturates
                     if (sb & 0x80u) sc = -sc;
 #pragma unroll
                     for (int x = 0; x < 8; x++) {

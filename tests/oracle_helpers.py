@@ -33,7 +33,9 @@ def decode_fp4_independent(rows: np.ndarray, D: int) -> np.ndarray:
     nib[..., 0::2] = codes & 15
     nib[..., 1::2] = codes >> 4
     val = e2m1_table()[nib]
-    sc = np.repeat(e4m3_table()[scales], 16, axis=-1)
+    table = e4m3_table()
+    table[0x7F], table[0xFF] = 448.0, -448.0  # the NaN code as a scale saturates (reading)
+    sc = np.repeat(table[scales], 16, axis=-1)
     return val * sc
 
 

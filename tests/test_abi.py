@@ -26,7 +26,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported():
     names = declared_symbols()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -125,3 +125,33 @@ def test_swa_merge_and_quantize_validation():
     assert b._quant(A, b.BF16, 10, 64, None, None, None) == 1              # cache NULL
     assert b._quant(A, b.BF16, 10, 64, A2, MIS, None) == 1                 # dst_row misaligned
     assert "aligned" in b._last_error().decode()
+
+
+def test_query_rows_beyond_the_grid_limit_are_rejected_before_launch():
+    """B * Q indexes a launch's second grid dimension: more than 65535 query
+    rows are refused with EUNSUPPORTED by every entry point that takes them."""
+    ws = 1 << 40
+    assert b._index(A, A, A, 1, 256, 257, 64, 128, 100, None, 1, None, 0, A2, None, A, ws, None) == 2
+    assert "65535" in b._last_error().decode()
+    assert b._topk(A, 65536, 1, 100, None, 5, A2, None, A, ws, None) == 2
+    assert b._attn(A, A, 1, 1, 1, 70000, 64, 512, 10, A, 2048, 1.0, A2, None, A, ws, None) == 2
+    assert b._swa(A, A, b.BF16, b.BF16, 300, 300, 64, 512, 100, A, 128, 0.1, None, None, A2, None, A, ws,
+                  None) == 2
+    a = b.LayerArgs()
+    a.mode, a.B, a.Q, a.N, a.m, a.HI, a.dI, a.idx_dt = b.FULL, 65536, 1, 1000, 4, 64, 128, b.BF16
+    a.k, a.P, a.H, a.D, a.q_dt, a.kv_dt, a.scale = 64, 0, 64, 512, b.BF16, b.BF16, 0.04
+    a.qI, a.w, a.kI, a.idx, a.q, a.kv, a.out = A, A, A, A, A, A, A2
+    assert b._layer(ctypes.byref(a), A, ws, None) == 2
+    assert b._layer_ws(ctypes.byref(a)) == 0
+    a.B = 65535
+    assert b._layer(ctypes.byref(a), A, 0, None) == 3  # within the limit: only the workspace is short
+
+
+def test_workspace_size_alias_and_format_alias():
+    a = b.LayerArgs()
+    a.mode, a.B, a.Q, a.N, a.m, a.HI, a.dI, a.idx_dt = b.FULL, 16, 1, 32768, 4, 64, 128, b.BF16
+    a.k, a.P, a.H, a.D, a.q_dt, a.kv_dt, a.scale = 2048, 0, 64, 512, b.BF16, b.BF16, 0.04
+    assert b._ws_alias(ctypes.byref(a)) == b._layer_ws(ctypes.byref(a)) > 0
+    text = open(HEADER).read()
+    assert "CSA2_FP4E2M1_S16E4M3 = 2" in text and "CSA2_FP4 = 2" in text
+

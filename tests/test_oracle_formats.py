@@ -52,6 +52,38 @@ def test_fp4_rows_match_independent_table_decode():
     assert np.array_equal(got, want)
 
 
+def test_fp4_scale_nan_code_saturates_and_every_other_byte_is_e4m3():
+    """Reading for scale bytes S.1111.111 (E4M3FN's NaN code, never written by
+    a quantizer): the scale saturates to +-448.  Every other byte, including
+    zero, negative zero, subnormals and sign-set bytes, is its E4M3 value."""
+    ref = e4m3_table()
+    for b in range(256):
+        v = oracle.fp4_scale(b)
+        if b in (0x7F, 0xFF):
+            assert v == (448.0 if b == 0x7F else -448.0), (b, v)
+        else:
+            assert v == ref[b] and math.copysign(1, v) == math.copysign(1, ref[b]), (b, v, ref[b])
+    # in a row: channel 0 = code 7 (6.0) under scale 0x7F, channel 16 = code 15 (-6.0) under 0xFF,
+    # channel 32 = code 1 (0.5) under the smallest subnormal 0x01 (2^-9), channel 48 = code 2 (1.0) under 0x80
+    D = 64
+    row = np.zeros(D // 2 + D // 16, dtype=np.uint8)
+    row[0], row[8], row[16], row[24] = 0x07, 0x0F, 0x01, 0x02
+    row[32:36] = [0x7F, 0xFF, 0x01, 0x80]
+    got = oracle.decode_rows(row[None, :], D)[0]
+    want = np.zeros(D)
+    want[0], want[16], want[32], want[48] = 6.0 * 448.0, -6.0 * -448.0, 0.5 * 2.0 ** -9, -0.0
+    assert np.array_equal(got, want)
+    assert math.copysign(1, got[48]) == -1.0
+
+
+def test_fp4_rows_every_scale_byte_match_independent_decode():
+    rng = np.random.default_rng(13)
+    D = 512
+    rows = rng.integers(0, 256, size=(40, D // 2 + D // 16), dtype=np.uint8)
+    rows[:, D // 2:] = np.arange(40 * D // 16).reshape(40, D // 16) % 256
+    assert np.array_equal(oracle.decode_rows(rows, D), decode_fp4_independent(rows, D))
+
+
 def test_bf16_and_f32_rows_decode_exactly():
     rng = np.random.default_rng(5)
     x = synth.normal_bf16(rng, (4, 48))

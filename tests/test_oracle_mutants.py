@@ -32,7 +32,7 @@ MUTANTS = {
     "FP4 nibbles swapped": ("(c % 2 == 0) ? (byte & 15u) : (byte >> 4)", "(c % 2 == 0) ? (byte >> 4) : (byte & 15u)"),
     "E4M3 exponent bias 8": ("ldexp(1.0 + (double)mant / 8.0, (int)e - 7)", "ldexp(1.0 + (double)mant / 8.0, (int)e - 8)"),
     "E2M1 subnormal doubled": ("0.5 * (double)mbit : ldexp", "1.0 * (double)mbit : ldexp"),
-    "FP4 scale group of 32": ("ora_e4m3(scales[c / 16])", "ora_e4m3(scales[c / 32])"),
+    "FP4 scale group of 32": ("ora_fp4_scale(scales[c / 16])", "ora_fp4_scale(scales[c / 32])"),
     "compression projection transposed": ("elem(wz, dt, (int64_t)d * D + c)", "elem(wz, dt, (int64_t)c * D + d)"),
     "compression bias row shifted": ("bias[(int64_t)r * D + c]", "bias[(int64_t)((r + 1) % W) * D + c]"),
     "compression window is current+next group": ("int64_t first_row = halo ? i * m : (i - 1) * m;",
