@@ -250,6 +250,23 @@ CSA2_API size_t csa2_layer_workspace_size(const csa2_layer_args *a);
 CSA2_API size_t csa2_workspace_size(const csa2_layer_args *a);
 CSA2_API int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * csa2_layer_noalloc -- csa2_layer without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, kernels and results as csa2_layer; the scratch comes from a
+ * device array inside the library (one per GPU, CSA2_NOALLOC_SCRATCH_BYTES =
+ * 64 MiB, held until the process ends) instead of the caller's workspace.  A
+ * layer whose csa2_layer_workspace_size exceeds that returns
+ * CSA2_EUNSUPPORTED before anything is enqueued.  The call itself allocates
+ * nothing (the array's device address is looked up once per device, on the
+ * first call with that device current).  Every call on one GPU shares its
+ * array: calls that overlap on one GPU (different streams, or different host
+ * threads) race on it and must be serialised by the caller.
+ * ------------------------------------------------------------------------- */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+CSA2_API int csa2_layer_noalloc(const csa2_layer_args *a, void *stream);
 
 /* ---------------------------------------------------------------------------
  * csa2_swa_attn -- the sliding-window (SWA) branch, optionally merged with the

@@ -66,13 +66,16 @@ _merge = _sig("csa2_merge_attn", ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int
 _layer_ws = _sig("csa2_layer_workspace_size", _sz, [ctypes.POINTER(LayerArgs)])
 _ws_alias = _sig("csa2_workspace_size", _sz, [ctypes.POINTER(LayerArgs)])
 _layer = _sig("csa2_layer", ctypes.c_int, [ctypes.POINTER(LayerArgs), _vp, _sz, _vp])
+_layer_noalloc = _sig("csa2_layer_noalloc", ctypes.c_int, [ctypes.POINTER(LayerArgs), _vp])
+NOALLOC_SCRATCH_BYTES = 64 << 20
 _last_error = _sig("csa2_last_error", ctypes.c_char_p, [])
 _version = _sig("csa2_version", ctypes.c_char_p, [])
 
 EXPORTS = ["csa2_compress_workspace_size", "csa2_compress", "csa2_index_score_workspace_size", "csa2_index_score",
            "csa2_topk_workspace_size", "csa2_topk", "csa2_sparse_attn_workspace_size", "csa2_sparse_attn",
            "csa2_swa_attn_workspace_size", "csa2_swa_attn", "csa2_merge_attn", "csa2_quantize_fp4",
-           "csa2_layer_workspace_size", "csa2_workspace_size", "csa2_layer", "csa2_last_error", "csa2_version"]
+           "csa2_layer_workspace_size", "csa2_workspace_size", "csa2_layer", "csa2_layer_noalloc", "csa2_last_error",
+           "csa2_version"]
 
 
 class Csa2Error(RuntimeError):
@@ -240,7 +243,7 @@ class Layer:
     ``run()`` only launches (graph-capturable, no allocation)."""
 
     def __init__(self, mode, *, q, kv, k=None, scale, qI=None, w=None, kI=None, q_pos=None, m=1, P=0, pool=None,
-                 idx=None, keep_scores=False, want_lse=True, count=True, out=None):
+                 idx=None, keep_scores=False, want_lse=True, count=True, out=None, noalloc=False):
         mode_i = MODES[mode] if isinstance(mode, str) else mode
         _dev(q, kv, qI, w, kI, q_pos, pool, idx, out)
         B, Q, H, D = q.shape
@@ -294,8 +297,9 @@ class Layer:
         a.pool, a.idx, a.count, a.scores = _p(pool), _p(idx), _p(self.count), _p(self.scores)
         a.q, a.kv, a.out, a.lse = _p(q), _p(kv), _p(self.out), _p(self.lse)
         self.args = a
-        self.ws_bytes = _layer_ws(ctypes.byref(a))
-        self.ws = _workspace(self.ws_bytes, dev)
+        self.noalloc = noalloc
+        self.ws_bytes = 0 if noalloc else _layer_ws(ctypes.byref(a))
+        self.ws = None if noalloc else _workspace(self.ws_bytes, dev)
 
     def set_query(self, q):
         """Point the layer at a new query tensor of the same shape (no copy)."""
@@ -304,7 +308,10 @@ class Layer:
         self.args.q = _p(q)
 
     def run(self):
-        _check(_layer(ctypes.byref(self.args), _p(self.ws), self.ws_bytes, _stream()))
+        if self.noalloc:  # csa2_layer_noalloc: the library's own scratch, no workspace
+            _check(_layer_noalloc(ctypes.byref(self.args), _stream()))
+        else:
+            _check(_layer(ctypes.byref(self.args), _p(self.ws), self.ws_bytes, _stream()))
         return self
 
 

@@ -1,6 +1,7 @@
 // C ABI of the CSA2 hot path (include/csa2.h): argument validation before any
 // launch, workspace carving and the Full / Reindex / Reuse mode sequencing.
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -176,6 +177,34 @@ void run_layer(const csa2_layer_args *a, const LayerSizes &z, void *ws, size_t w
     }
     void *attws = c.base + c.used;
     csa2::attn_run(z.att, a->q, a->kv, a->idx, a->scale, a->out, a->lse, attws, z.attws, s);
+}
+
+// ------------------------------------------------- allocation-free layer
+// Scratch of csa2_layer_noalloc: a file-scope device array, one copy per GPU
+// that the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in):
+// its device address is taken once per device with hipGetSymbolAddress, with
+// that device current, and kept here.
+constexpr size_t NOALLOC_SCRATCH_BYTES = CSA2_NOALLOC_SCRATCH_BYTES;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+}  // namespace
+static __device__ __attribute__((aligned(256))) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_dev[NOALLOC_MAX_DEVICES];
+
+void *scratch_ptr() {
+    int dev = 0;
+    CSA2_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) throw Error(CSA2_EUNSUPPORTED, "device ordinal beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        CSA2_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) throw Error(CSA2_EINTERNAL, "scratch address unusable");
+        g_scratch_dev[dev] = p;
+    }
+    return g_scratch_dev[dev];
 }
 
 }  // namespace
@@ -404,6 +433,18 @@ int csa2_layer(const csa2_layer_args *a, void *ws, size_t ws_bytes, void *stream
         const LayerSizes z = layer_sizes(a);
         need_ws(ws, ws_bytes, z.total);
         run_layer(a, z, ws, ws_bytes, stream);
+    });
+}
+
+int csa2_layer_noalloc(const csa2_layer_args *a, void *stream) {
+    return guarded([&] {
+        check_layer(a);
+        const LayerSizes z = layer_sizes(a);
+        if (z.total > NOALLOC_SCRATCH_BYTES)
+            throw Error(CSA2_EUNSUPPORTED, "this layer needs " + std::to_string(z.total) +
+                                               " bytes of scratch; the allocation-free entry point has " +
+                                               std::to_string(NOALLOC_SCRATCH_BYTES));
+        run_layer(a, z, scratch_ptr(), NOALLOC_SCRATCH_BYTES, stream);
     });
 }
 

@@ -26,7 +26,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported():
     names = declared_symbols()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -155,3 +155,16 @@ def test_workspace_size_alias_and_format_alias():
     text = open(HEADER).read()
     assert "CSA2_FP4E2M1_S16E4M3 = 2" in text and "CSA2_FP4 = 2" in text
 
+
+def test_noalloc_layer_rejects_layers_beyond_its_scratch_before_launch():
+    """csa2_layer_noalloc refuses, before touching the device, a layer whose
+    workspace exceeds its fixed 64 MiB scratch, and validates like csa2_layer."""
+    a = b.LayerArgs()
+    a.mode, a.B, a.Q, a.N, a.m, a.HI, a.dI, a.idx_dt = b.FULL, 16, 1, 1 << 20, 1, 64, 128, b.BF16
+    a.k, a.P, a.H, a.D, a.q_dt, a.kv_dt, a.scale = 2048, 16384, 64, 512, b.BF16, b.FP4, 0.04
+    a.qI, a.w, a.kI, a.idx, a.pool, a.q, a.kv, a.out = A, A, A, A, A, A, A, A2
+    assert b._layer_ws(ctypes.byref(a)) > b.NOALLOC_SCRATCH_BYTES
+    assert b._layer_noalloc(ctypes.byref(a), None) == 2
+    assert "scratch" in b._last_error().decode()
+    a.idx = None
+    assert b._layer_noalloc(ctypes.byref(a), None) == 1   # validation first, as csa2_layer
