@@ -8,24 +8,20 @@
 // may be stored as FP4 E2M1 with one E4M3 scale per 16 channels; the decoded
 // value e2m1 * e4m3 has at most 5 significant bits and is exact in bf16.
 //
-// Matrix-core kernel: a block serves all heads of one query over a fixed split
-// of 128 selected entries (the split depends only on k, so a query's result
-// does not depend on the batch), one wave per 16 heads.  The gathered rows are
-// staged once per block in LDS as bf16 (FP4 rows decoded on the way in, to
-// fp16, where they are also exact), S^T = C Q^T runs on the 16x16x32
-// matrix-core instruction of that type with the rows as the A operand, the
-// online softmax keeps one running max per head, and O^T = C^T P^T reuses the
-// same LDS rows (read transposed) with P^T taken straight from the S^T result
-// registers.  Splits are merged by a small combine kernel.
+// Matrix-core kernel (k_attn_split): a block serves one query over a fixed
+// split of 128 selected entries (the split depends only on k, so a query's
+// result does not depend on the batch) for 16 to 64 of its heads.  All rows
+// of the split are gathered at once and staged in LDS as bf16 (FP4 rows
+// decoded on the way in, to fp16, where they are also exact); S^T = C Q^T and
+// O^T = C^T P^T run on the 16x16x32 matrix-core instruction of that type with
+// the block's queries held in registers, a softmax over the split in between.
+// Splits are merged by a small combine kernel.
 #include "internal.h"
 
 namespace csa2 {
 
-constexpr int ATT_SUB = 32;  // entries per tile
-
 // Selected entries per split: fixed, so that a query's result does not depend
-// on the batch it is computed in.  (Longer splits halve the combine traffic but
-// leave each block a longer chain of gathers; measured slower at k = 2048.)
+// on the batch it is computed in.
 constexpr int ATT_SPLIT = 128;
 
 namespace {
@@ -75,686 +71,33 @@ __device__ __forceinline__ int64_t row_bytes(int fmt, int D) {
     return fmt == CSA2_F32 ? 4 * (int64_t)D : (fmt == CSA2_BF16 ? 2 * (int64_t)D : (int64_t)D / 2 + D / 16);
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
-// ------------------------------------------------------------ MFMA kernel
-// Block = one query x one split of the selected entries x HB groups of 16
-// heads; wave w serves heads 16 (HB g + w % HB) .. +15 and, with DS = 2, half of the output channels (the
-// two waves of a head group both compute that group's logits).  Per 32-entry tile: all threads gather the rows into an
-// LDS buffer (bf16 rows as is, FP4 rows decoded to fp16), the next tile's rows
-// are already in flight in registers; each wave computes S^T = C Q^T (rows as
-// the A operand), the online softmax of its 16 heads, and O^T += C^T P^T with
-// the C^T operand read by the LDS transpose load: lane r of each 16-lane group
-// points at 4 consecutive channels of one row, and lane i receives channel i
-// of 4 consecutive rows.
-
+// ------------------------------------------------------ operand helpers
 typedef short __attribute__((ext_vector_type(4))) s16x4;
 typedef float __attribute__((ext_vector_type(2))) f32x2;
 typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2v;  // converted to with round-to-nearest-even
 typedef _Float16 __attribute__((ext_vector_type(2))) f16x2;
 
-// FP4 chunk (32 channels: 16 code bytes) with the two E4M3 scales of its
-// 16-channel halves -> 32 fp16 values.  The conversion instruction applies the
-// scale's power of two; the scale's mantissa (1 + m/8, at most 3 bits) is
-// applied by an fp16 multiply.  Every product has <= 5 significant bits and a
-// magnitude in [2^-10, 3072], so both steps are exact.
-__device__ __forceinline__ void fp4_chunk_to_f16(u32x4 codes, uint32_t sc2, uint32_t *dst16) {
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-        const float s = e4m3_val((sc2 >> (8 * half)) & 0xffu);
-        const uint32_t sb = __float_as_uint(s);
-        float pow2 = __uint_as_float(sb & 0x7f800000u);
-        uint32_t fbits = 0x3c00u | ((sb >> 13) & 0x3ffu) | ((sb >> 16) & 0x8000u);
-        if (s == 0.f) {
-            pow2 = 1.f;
-            fbits = 0u;
-        }
-        const f16x2 f = __builtin_bit_cast(f16x2, fbits | (fbits << 16));
-#pragma unroll
-        for (int wi = 0; wi < 2; wi++) {
-            const uint32_t word = codes[half * 2 + wi];
-            f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 0) * f;
-            f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 1) * f;
-            f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 2) * f;
-            f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 3) * f;
-            uint32_t *o = dst16 + (half * 2 + wi) * 4;
-            o[0] = __builtin_bit_cast(uint32_t, v0);
-            o[1] = __builtin_bit_cast(uint32_t, v1);
-            o[2] = __builtin_bit_cast(uint32_t, v2);
-            o[3] = __builtin_bit_cast(uint32_t, v3);
-        }
+// 8 FP4 channels (one code word) with their E4M3 scale -> 8 fp16 values.  The
+// conversion instruction applies the scale's power of two, an fp16 multiply
+// its mantissa (1 + m/8, at most 3 bits); every product has <= 5 significant
+// bits and a magnitude in [2^-10, 2688], so both steps are exact.
+__device__ __forceinline__ u32x4 fp4_word_to_f16x8(uint32_t word, uint32_t sbyte) {
+    const float s = e4m3_val(sbyte);
+    const uint32_t sb = __float_as_uint(s);
+    float pow2 = __uint_as_float(sb & 0x7f800000u);
+    uint32_t fbits = 0x3c00u | ((sb >> 13) & 0x3ffu) | ((sb >> 16) & 0x8000u);
+    if (s == 0.f) {
+        pow2 = 1.f;
+        fbits = 0u;
     }
-}
-
-template <int D, int FMT>
-struct TileGather {
-    // bf16: a row is D/8 16-byte chunks; FP4: a row is D/32 chunks of 16 code
-    // bytes (32 channels) plus 2 scale bytes each.
-    static constexpr int CPR = FMT == CSA2_FP4 ? D / 32 : D / 8;
-    static constexpr int CHUNKS = ATT_SUB * CPR;
-    static constexpr int ROWB = FMT == CSA2_FP4 ? D / 2 + D / 16 : 2 * D;
-};
-
-// Loads of one tile's rows into registers: every lane loads (entries of -1
-// read row 0 and are flagged in bit 31 of sbuf, then zeroed by gather_store),
-// so that no branch or copy stands between the loads and they all fly at once.
-template <int D, int FMT, int NT>
-__device__ __forceinline__ void gather_issue(const uint8_t *kvb, const int32_t *jt, u32x4 *buf, uint32_t *sbuf) {
-    using G = TileGather<D, FMT>;
-    constexpr int PER = (G::CHUNKS + NT - 1) / NT;
-#pragma unroll
-    for (int u = 0; u < PER; u++) {
-        const int c = threadIdx.x + u * NT;
-        const int cs = c < G::CHUNKS ? c : 0;
-        const int r = cs / G::CPR, cc = cs % G::CPR;
-        const int j = jt[r];
-        const uint8_t *row = kvb + (size_t)(j >= 0 ? j : 0) * G::ROWB;
-        buf[u] = *reinterpret_cast<const u32x4 *>(row + cc * 16);
-        uint32_t sc = 0;
-        if constexpr (FMT == CSA2_FP4) sc = *reinterpret_cast<const uint16_t *>(row + D / 2 + cc * 2);
-        sbuf[u] = sc | (j < 0 ? 0x80000000u : 0u);
-    }
-}
-
-template <int D, int FMT, int NT>
-__device__ __forceinline__ void gather_store(uint16_t *T, const u32x4 *buf, const uint32_t *sbuf) {
-    using G = TileGather<D, FMT>;
-    constexpr int PER = (G::CHUNKS + NT - 1) / NT;
-    constexpr int LS = D + 8;
-#pragma unroll
-    for (int u = 0; u < PER; u++) {
-        const int c = threadIdx.x + u * NT;
-        if (c >= G::CHUNKS) continue;
-        const int r = c / G::CPR, cc = c % G::CPR;
-        const bool skip = sbuf[u] >> 31;  // no entry: the row is zero
-        if constexpr (FMT == CSA2_FP4) {
-            uint32_t o[16];
-            fp4_chunk_to_f16(skip ? u32x4{0u, 0u, 0u, 0u} : buf[u], skip ? 0u : sbuf[u] & 0xffffu, o);
-            uint32_t *dst = reinterpret_cast<uint32_t *>(T + r * LS + cc * 32);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++)
-                reinterpret_cast<u32x4 *>(dst)[q4] = u32x4{o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]};
-        } else {
-            *reinterpret_cast<u32x4 *>(T + r * LS + cc * 8) = skip ? u32x4{0u, 0u, 0u, 0u} : buf[u];
-        }
-    }
-}
-
-// ------------------------------------------------ selection finish (fused)
-// A block's share of the certified top-k, finished from the selection's
-// records in three steps.  The attention itself only needs the selected SET;
-// its blocks take the entries in this order: the IN entries in slot order
-// (positions 0 .. |IN|-1), then the best K - |IN| band entries in rank order
-// (binary64 score descending, slot ascending).  A split's first tile usually
-// holds IN entries only, so its rows are in flight while the band is ranked.
-// The index output is the selected set in slot order, written after the
-// ranking.  Redundant across the query's blocks, but short, and it saves a
-// dependent launch.  `scratch` (bytes available: cap) holds the bitmap and
-// the band until sel_split_idx returns.
-struct BandEntA {
-    uint64_t key;
-    int32_t slot;
-    uint32_t nslot;  // ~slot: ascending slot order as descending unsigned order
-};
-
-struct SplitSel {
-    int32_t in_cnt, nb;  // |IN| and the band size
-    bool in_lds;         // the band is staged in LDS
-};
-
-__device__ __forceinline__ int32_t sel_entry(const SelHandoff &sel, int bq, int32_t slot) {
-    return sel.cand ? sel.cand[(size_t)bq * sel.n + slot] : slot;
-}
-
-// Popcount scan of the bitmap: thread tid owns words [tid * per, ...); returns
-// its first position and the block total.
-template <int NT>
-__device__ __forceinline__ uint32_t bitmap_scan(const uint32_t *bm, int64_t nwords, uint32_t *red, uint32_t &mine,
-                                                uint32_t &tot) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t per = (nwords + NT - 1) / NT;
-    const int64_t w0 = (int64_t)tid * per;
-    mine = 0;
-    for (int64_t w = w0; w < w0 + per && w < nwords; w++) mine += __builtin_popcount(bm[w]);
-    const uint32_t incl = wave_incl_scan_u32(mine);
-    if (lane == 63) red[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-    tot = 0;
-#pragma unroll
-    for (int i = 0; i < NT / 64; i++) {
-        const uint32_t x = red[i];
-        before += i < wave ? x : 0u;
-        tot += x;
-    }
-    return before + incl - mine;
-}
-
-// Step 1: the records into LDS (IN bitmap, band entries with their keys) and
-// the split's IN positions into jsh (-1 elsewhere).  Ends with jsh's IN part
-// visible to the block.
-template <int NT, int SPLIT>
-__device__ SplitSel sel_split_in(const SelHandoff &sel, int bq, int e_begin, int ne, uint32_t *scratch, size_t cap,
-                                 int32_t *jsh, uint32_t *red) {
-    const int tid = threadIdx.x;
-    const int64_t nwords = sel.nwords;
-    const int64_t nw4 = (nwords + 3) & ~int64_t(3);
-    uint32_t *bm = scratch;
-    BandEntA *ent = reinterpret_cast<BandEntA *>(scratch + nw4);
-    const uint32_t *gbm = sel.bitmap + (size_t)bq * nwords;
-    const int32_t *list = sel.band + (size_t)bq * sel.band_cap;
-    const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
-    // One round of loads before anything waits: the first NT band entries
-    // (speculatively, before the count is known; past the capacity they read
-    // the last one), the bitmap (four words per load where the rows are
-    // 16-byte aligned) and the target record, which is used only after them.
-    const int32_t spec_i = tid < sel.band_cap ? tid : (int32_t)sel.band_cap - 1;
-    const int32_t sl0 = list[spec_i];
-    const double sc0 = bs[spec_i];
-    constexpr int U = 4;  // NT * U * 4 words per round
-    const bool vec = (nwords & 3) == 0;
-    const int64_t nq = nwords >> 2;
-    u32x4 v[U];
-    if (vec) {
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t qi = tid + (int64_t)NT * u;
-            v[u] = reinterpret_cast<const u32x4 *>(gbm)[qi < nq ? qi : nq - 1];
-        }
-    }
-    const SelTarget t = sel.sq[bq].t[0];
-    SplitSel st;
-    st.in_cnt = t.in_cnt;
-    st.nb = t.band_cnt;
-    st.in_lds = st.nb <= (int32_t)((cap - (size_t)nw4 * 4) / sizeof(BandEntA));
-    if (vec) {
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t qi = tid + (int64_t)NT * u;
-            if (qi < nq) reinterpret_cast<u32x4 *>(bm)[qi] = v[u];
-        }
-        for (int64_t q0 = (int64_t)NT * U; q0 < nq; q0 += (int64_t)NT * U) {
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int64_t qi = q0 + tid + (int64_t)NT * u;
-                v[u] = reinterpret_cast<const u32x4 *>(gbm)[qi < nq ? qi : nq - 1];
-            }
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int64_t qi = q0 + tid + (int64_t)NT * u;
-                if (qi < nq) reinterpret_cast<u32x4 *>(bm)[qi] = v[u];
-            }
-        }
-    } else {
-        for (int64_t w = tid; w < nwords; w += NT) bm[w] = gbm[w];
-    }
-    for (int e = tid; e < SPLIT; e += NT) jsh[e] = -1;
-    if (st.in_lds) {
-        if (tid < st.nb) {
-            BandEntA e;
-            e.key = dkey(sc0);
-            e.slot = sl0;
-            e.nslot = ~(uint32_t)e.slot;
-            ent[tid] = e;
-        }
-        for (int32_t i = tid + NT; i < st.nb; i += NT) {
-            BandEntA e;
-            e.key = dkey(bs[i]);
-            e.slot = list[i];
-            e.nslot = ~(uint32_t)e.slot;
-            ent[i] = e;
-        }
-    }
-    __syncthreads();
-    uint32_t mine, tot;
-    uint32_t pos = bitmap_scan<NT>(bm, nwords, red, mine, tot);
-    const uint32_t lo = (uint32_t)e_begin, hi = (uint32_t)(e_begin + ne);
-    if (pos < hi && pos + mine > lo) {
-        const int64_t per = (nwords + NT - 1) / NT;
-        const int64_t w0 = (int64_t)tid * per;
-        for (int64_t w = w0; w < w0 + per && w < nwords; w++) {
-            uint32_t bits = bm[w];
-            while (bits) {
-                const int b = __builtin_ctz(bits);
-                bits &= bits - 1;
-                if (pos >= lo && pos < hi) jsh[pos - lo] = sel_entry(sel, bq, (int32_t)(w * 32 + b));
-                pos++;
-            }
-        }
-    }
-    __syncthreads();
-    return st;
-}
-
-// Step 2: rank the band; the best r = K - |IN| entries join the bitmap, and
-// those whose positions |IN| + rank fall in the split go into jsh.  issue()
-// is called once (it starts the first tile's row loads when they are known):
-// on the common path right after the ranking's LDS reads, so that the loads
-// fly during the ranking.  Ends with jsh complete.
-template <int NT, int SPLIT, class Issue>
-__device__ void sel_split_band(const SelHandoff &sel, int bq, int K, const SplitSel &st, int e_begin, int ne,
-                               uint32_t *scratch, size_t cap, int32_t *jsh, Issue &&issue) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t nw4 = (sel.nwords + 3) & ~int64_t(3);
-    uint32_t *bm = scratch;
-    const u32x4 *ent4 = reinterpret_cast<const u32x4 *>(scratch + nw4);
-    const int32_t nb = st.nb, r = K - st.in_cnt;
-    const int32_t *list = sel.band + (size_t)bq * sel.band_cap;
-    const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
-    // entry with slot si and rank rk (< r) is selected
-    auto take = [&](int32_t si, int32_t rk) {
-        atomicOr(&bm[si >> 5], 1u << (si & 31));
-        const int32_t p = st.in_cnt + rk - e_begin;
-        if (p >= 0 && p < ne) jsh[p] = sel_entry(sel, bq, si);
-    };
-    if (r > 0 && nb > 0 && st.in_lds && nb <= NT &&
-        (size_t)(nw4 + 4 * nb) * 4 + (size_t)(NT / 64) * NT * 4 <= cap) {
-        // Lane l of chunk c holds entry i = 64 c + l; wave w takes its share of
-        // the partners j, read from LDS as broadcasts.  j is ahead of i iff
-        // (key_j, ~slot_j) > (key_i, ~slot_i) as 96-bit unsigned numbers, i.e.
-        // iff the subtraction (key_i, ~slot_i) - (key_j, ~slot_j) borrows: three
-        // chained subtractions and an add of the borrow, all on the vector
-        // unit.  The waves' counts meet in LDS and thread i sums them.
-        constexpr int NW = NT / 64;
-        constexpr int MAXC = NT / 64;
-        uint32_t *rkp = scratch + nw4 + 4 * nb;
-        const int nch = (nb + 63) / 64;
-        u32x4 ic[MAXC];
-#pragma unroll
-        for (int c = 0; c < MAXC; c++) {
-            const int i = 64 * c + lane;
-            ic[c] = c < nch ? ent4[i < nb ? i : 0] : u32x4{0u, 0u, 0u, 0u};
-        }
-        const bool act = tid < nb;
-        const u32x4 me = ent4[act ? tid : 0];
-        const int32_t my_e = sel_entry(sel, bq, (int32_t)me[2]);  // before the row loads
-        issue();  // global loads go out after these LDS reads
-        uint32_t rk[MAXC];
-#pragma unroll
-        for (int c = 0; c < MAXC; c++) rk[c] = 0;
-        const int jper = (nb + NW - 1) / NW;
-        const int j0 = __builtin_amdgcn_readfirstlane(wave * jper);
-        const int j1 = __builtin_amdgcn_readfirstlane(min(nb, j0 + jper));
-        // (key lo, key hi, slot, ~slot) of partner j against every chunk
-        auto count = [&](const u32x4 &o) {
-#pragma unroll
-            for (int c = 0; c < MAXC; c++) {
-                if (c < nch) {
-                    uint32_t d;
-                    asm volatile(
-                        "v_sub_co_u32 %0, vcc, %2, %3\n\t"
-                        "v_subb_co_u32 %0, vcc, %4, %5, vcc\n\t"
-                        "v_subb_co_u32 %0, vcc, %6, %7, vcc\n\t"
-                        "v_addc_co_u32 %1, vcc, 0, %1, vcc"
-                        : "=&v"(d), "+v"(rk[c])
-                        : "v"(ic[c][3]), "v"(o[3]), "v"(ic[c][0]), "v"(o[0]), "v"(ic[c][1]), "v"(o[1])
-                        : "vcc");
-                }
-            }
-        };
-        int j = j0;
-        for (; j + 4 <= j1; j += 4) {
-            u32x4 o[4];
-#pragma unroll
-            for (int u = 0; u < 4; u++) o[u] = ent4[j + u];
-#pragma unroll
-            for (int u = 0; u < 4; u++) count(o[u]);
-        }
-        for (; j < j1; j++) count(ent4[j]);
-#pragma unroll
-        for (int c = 0; c < MAXC; c++)
-            if (c < nch) rkp[wave * NT + 64 * c + lane] = rk[c];
-        __syncthreads();
-        if (act) {
-            uint32_t rank = 0;
-#pragma unroll
-            for (int w = 0; w < NW; w++) rank += rkp[w * NT + tid];
-            if (rank < (uint32_t)r) {
-                const int32_t si = (int32_t)me[2];
-                atomicOr(&bm[si >> 5], 1u << (si & 31));
-                const int32_t p = st.in_cnt + (int32_t)rank - e_begin;
-                if (p >= 0 && p < ne) jsh[p] = my_e;
-            }
-        }
-    } else if (r > 0 && nb > 0) {
-        // entry i is ranked by P consecutive lanes, each comparing a 1/P share
-        const int P = nb * 8 <= NT ? 8 : nb * 4 <= NT ? 4 : nb * 2 <= NT ? 2 : 1;
-        const int per = NT / P;
-        for (int32_t i0 = 0; i0 < nb; i0 += per) {
-            const int32_t i = i0 + tid / P;
-            const int ep = tid % P;
-            const bool act = i < nb;
-            const int32_t ii = act ? i : 0;
-            int32_t rank = 0;
-            uint64_t ki;
-            int32_t si;
-            if (st.in_lds) {
-                const u32x4 me = ent4[ii];
-                ki = (uint64_t)me[0] | ((uint64_t)me[1] << 32);
-                si = (int32_t)me[2];
-                for (int32_t j0 = ep; j0 < nb; j0 += 8 * P) {
-                    u32x4 bj[8];
-#pragma unroll
-                    for (int u = 0; u < 8; u++) {
-                        const int32_t j = j0 + u * P;
-                        bj[u] = ent4[j < nb ? j : ii];  // past the end: compare with itself (counts 0)
-                    }
-#pragma unroll
-                    for (int u = 0; u < 8; u++) {
-                        const uint64_t kj = (uint64_t)bj[u][0] | ((uint64_t)bj[u][1] << 32);
-                        rank += (int)((kj > ki) | ((kj == ki) & ((int32_t)bj[u][2] < si)));
-                    }
-                }
-            } else {
-                ki = dkey(bs[ii]);
-                si = list[ii];
-                for (int32_t j = ep; j < nb; j += P) {
-                    const uint64_t kj = dkey(bs[j]);
-                    const int32_t sj = list[j];
-                    rank += (int)((kj > ki) | ((kj == ki) & (sj < si)));
-                }
-            }
-            if (P >= 2) rank = bfly1(rank, OpAdd{});
-            if (P >= 4) rank = bfly2(rank, OpAdd{});
-            if (P >= 8) rank = bfly4(rank, OpAdd{});
-            if (act && ep == 0 && rank < r) take(si, rank);
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // this path's own loads are done before the rows go out
-        issue();
-    } else {
-        issue();
-    }
-    __syncthreads();
-}
-
-// Step 3: the index output, the selected set in slot order (its split's share,
-// -1 past the count), and the count (split 0).  Ends with the scratch free.
-template <int NT>
-__device__ void sel_split_idx(const SelHandoff &sel, int bq, int K, int e_begin, int ne, bool first,
-                              const uint32_t *scratch, uint32_t *red) {
-    const int tid = threadIdx.x;
-    const int64_t nwords = sel.nwords;
-    const uint32_t *bm = scratch;
-    uint32_t mine, tot;
-    uint32_t pos = bitmap_scan<NT>(bm, nwords, red, mine, tot);
-    const int32_t kept = (int32_t)(tot < (uint32_t)K ? tot : (uint32_t)K);
-    const uint32_t lo = (uint32_t)e_begin, hi = (uint32_t)(e_begin + ne);
-    int32_t *orow = sel.idx + (size_t)bq * K + e_begin;
-    // one loop per mapping, so that the identity mapping waits for no load
-    auto scatter = [&](auto map) {
-        const int64_t per = (nwords + NT - 1) / NT;
-        const int64_t w0 = (int64_t)tid * per;
-        for (int64_t w = w0; w < w0 + per && w < nwords; w++) {
-            uint32_t bits = bm[w];
-            while (bits) {
-                const int b = __builtin_ctz(bits);
-                bits &= bits - 1;
-                if (pos >= lo && pos < hi) orow[pos - lo] = map((int32_t)(w * 32 + b));
-                pos++;
-            }
-        }
-    };
-    if (pos < hi && pos + mine > lo) {
-        if (sel.cand) {
-            const int32_t *cq = sel.cand + (size_t)bq * sel.n;
-            scatter([&](int32_t sl) { return cq[sl]; });
-        } else {
-            scatter([](int32_t sl) { return sl; });
-        }
-    }
-    for (int e = (kept > e_begin ? kept - e_begin : 0) + tid; e < ne; e += NT) orow[e] = -1;
-    if (first && tid == 0 && sel.count) sel.count[bq] = kept;
-    __syncthreads();
-}
-
-// Balanced pairwise sum of 1, 2 or 4 partial tiles.
-template <int NPS>
-__device__ __forceinline__ f32x4 tree_sum(const f32x4 *p) {
-    if constexpr (NPS == 1) return p[0];
-    else if constexpr (NPS == 2) return p[0] + p[1];
-    else return (p[0] + p[1]) + (p[2] + p[3]);
-}
-
-
-// Block order: the NG blocks that share one (query, split) -- one per group
-// of HB x 16 heads -- get linear ids congruent mod 8, so that the round-robin
-// dispatch puts them on one XCD and they gather the split's rows through one
-// L2.  Ids past the last (query, split) pair exit at once.
-template <int D, int FMT, int HB, int DS, int SPLIT, bool FROMSEL>
-__global__ __launch_bounds__(64 * HB * DS, 1) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
-                                                          int Q, int H, int64_t N, const int32_t *__restrict__ idx,
-                                                          int k, float scale, int nsplit, int npairs,
-                                                          uint16_t *__restrict__ out, float *__restrict__ lse,
-                                                          uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml,
-                                                          float *__restrict__ part_sc, SelHandoff sel) {
-    constexpr int NT = 64 * HB * DS;
-    constexpr int KS = D / 32 / DS;  // contraction steps of S owned by this wave (its channel part)
-    constexpr int SP = D >= 256 ? 4 : 2;  // channel parts of the S contraction, for every DS
-    static_assert(SP % DS == 0 && (D / 32) % SP == 0, "S parts must split evenly over the waves");
-    constexpr int LP = SP / DS;       // parts contracted by this wave
-    constexpr int PS = KS / LP;       // steps per part
-    constexpr int DT = D / 16 / DS;  // 16-wide d tiles of O owned by this wave
-    constexpr int LS = D + 8;   // LDS row stride in 16-bit elements (16-byte pad)
-    using G = TileGather<D, FMT>;
-    constexpr int PER = (G::CHUNKS + NT - 1) / NT;
-    __shared__ __attribute__((aligned(16))) uint16_t tile[2][ATT_SUB * LS];
-    __shared__ __attribute__((aligned(16))) int32_t jsh[SPLIT];
-    // partial logits of each wave's channel part, summed over the head group's DS waves
-    __shared__ __attribute__((aligned(16))) f32x4 spart[DS > 1 ? 64 * HB * DS * 2 : 1];
-
-    const int NG = H / (16 * HB);
-    const int L = blockIdx.x;
-    const int pair = (L / (8 * NG)) * 8 + (L % 8);
-    const int hgb = (L % (8 * NG)) / 8;
-    if (pair >= npairs) return;
-    const int split = pair % nsplit;
-    const int bq = pair / nsplit;
-    const int b = bq / Q;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int col = lane & 15, kg = lane >> 4;
-    const int hg = hgb * HB + wave % HB;  // this wave's 16 heads
-    const int dpart = wave / HB;          // this wave's channel part: S over it, O for it
-    const int dt0 = dpart * DT;           // first d tile of this wave
-
-    const int e_begin = split * SPLIT;
-    const int e_end = min(k, e_begin + SPLIT);
-    const int ne = e_end - e_begin;
-    const uint8_t *kvb = kv + (size_t)b * N * G::ROWB;
-    // Query heads as the B operand of S^T = C Q^T (fp16 for FP4 rows), in flight from the start.
-    u32x4 qf[KS];
-    const uint16_t *qrow = q + ((size_t)bq * H + hg * 16 + col) * D + 8 * kg + 32 * KS * dpart;
-#pragma unroll
-    for (int s = 0; s < KS; s++) qf[s] = *reinterpret_cast<const u32x4 *>(qrow + 32 * s);
-
-    const int ntiles = (ne + ATT_SUB - 1) / ATT_SUB;
-    u32x4 buf[PER];
-    uint32_t sbuf[PER];
-    if constexpr (FROMSEL) {
-        // the selected set from the certified selection's records (LDS scratch in the tile buffers)
-        __shared__ uint32_t sred[NT / 64];
-        uint32_t *scr = reinterpret_cast<uint32_t *>(tile[0]);
-        const SplitSel st = sel_split_in<NT, SPLIT>(sel, bq, e_begin, ne, scr, sizeof(tile), jsh, sred);
-        // the first tile's rows go out now if its entries are all IN entries
-        const bool early = e_begin + min(ATT_SUB, ne) <= st.in_cnt;
-        // (issued unconditionally: a branch around the loads would make later
-        // waits for other loads wait for these too; reissued below if not early)
-        sel_split_band<NT, SPLIT>(sel, bq, k, st, e_begin, ne, scr, sizeof(tile), jsh,
-                                  [&]() { gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf); });
-        sel_split_idx<NT>(sel, bq, k, e_begin, ne, split == 0, scr, sred);
-        if (!early) gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf);
-    } else {
-        const int32_t *irow = idx + (size_t)bq * k + e_begin;
-        for (int e = threadIdx.x; e < SPLIT; e += NT) {
-            int j = e < ne ? irow[e] : -1;
-            jsh[e] = (j >= 0 && j < N) ? j : -1;  // out-of-range entries are skipped like -1
-        }
-        __syncthreads();  // jsh ready
-        if (ntiles > 0) gather_issue<D, FMT, NT>(kvb, jsh, buf, sbuf);
-    }
-    float qscale = scale;
-    if constexpr (FMT == CSA2_FP4) {
-        // the power-of-two scale covers the whole rows of the 16 heads, so that the
-        // DS waves sharing them contract with the same scaled q
-        float amax = 0.f;
-        const uint16_t *qall = qrow - 32 * KS * dpart;
-#pragma unroll
-        for (int s = 0; s < KS * DS; s++) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(qall + 32 * s);
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(v[e] & 0xffffu)), fabsf(bf16_to_f32(v[e] >> 16))));
-        }
-        amax = wave_max(amax);
-        int ex = 0;
-        if (amax > 32768.f) ex = (int)ceilf(log2f(amax / 32768.f));
-        const float down = ldexpf(1.f, -ex);
-        qscale = ldexpf(scale, ex);
-#pragma unroll
-        for (int s = 0; s < KS; s++)
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                qf[s][e] = pack_f16_rne(bf16_to_f32(qf[s][e] & 0xffffu) * down, bf16_to_f32(qf[s][e] >> 16) * down);
-    }
-
-    f32x4 o[DT];
-#pragma unroll
-    for (int t = 0; t < DT; t++) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = NEG_INF, l_run = 0.f;
-
-    if (ntiles > 0) gather_store<D, FMT, NT>(tile[0], buf, sbuf);
-    __syncthreads();
-    for (int t = 0; t < ntiles; t++) {
-        if (t + 1 < ntiles) gather_issue<D, FMT, NT>(kvb, jsh + (t + 1) * ATT_SUB, buf, sbuf);
-        const uint16_t *T = tile[t & 1];
-        const int32_t *jt = jsh + t * ATT_SUB;
-        // ---- S^T[e][h] for the two 16-entry halves. The contraction is cut into SP
-        // channel parts summed as a balanced tree, the same for every DS: this wave
-        // contracts its SP/DS parts and adds them, the DS waves' sums are then added.
-        f32x4 st[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; h2++) {
-            const uint16_t *arow = T + (h2 * 16 + col) * LS + 8 * kg + 32 * KS * dpart;
-            f32x4 pp[LP];
-#pragma unroll
-            for (int lp = 0; lp < LP; lp++) {
-                pp[lp] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < PS; s++) {
-                    const u32x4 av = *reinterpret_cast<const u32x4 *>(arow + 32 * (lp * PS + s));
-                    pp[lp] = mma<FMT>(av, qf[lp * PS + s], pp[lp]);
-                }
-            }
-            st[h2] = tree_sum<LP>(pp);
-        }
-        if constexpr (DS > 1) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; h2++) spart[(wave * 64 + lane) * 2 + h2] = st[h2];
-            __syncthreads();
-#pragma unroll
-            for (int h2 = 0; h2 < 2; h2++) {
-                f32x4 pp[DS];
-#pragma unroll
-                for (int p2 = 0; p2 < DS; p2++) pp[p2] = spart[(((wave % HB) + p2 * HB) * 64 + lane) * 2 + h2];
-                st[h2] = tree_sum<DS>(pp);
-            }
-        }
-        // ---- online softmax for head col; this lane holds entries 16 h2 + 4 kg + i
-        float a[8];
-        float mt = NEG_INF;
-        // this lane's 8 entries (16 h2 + 4 kg + i): -1 marks an empty one
-        const int4 jv[2] = {*reinterpret_cast<const int4 *>(jt + 4 * kg), *reinterpret_cast<const int4 *>(jt + 16 + 4 * kg)};
-#pragma unroll
-        for (int h2 = 0; h2 < 2; h2++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int jj = i == 0 ? jv[h2].x : i == 1 ? jv[h2].y : i == 2 ? jv[h2].z : jv[h2].w;
-                const float v = jj >= 0 ? st[h2][i] * qscale : NEG_INF;
-                a[h2 * 4 + i] = v;
-                mt = fmaxf(mt, v);
-            }
-        mt = bfly32(bfly16(mt, OpMax{}), OpMax{});
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = m_run == NEG_INF ? 0.f : __expf(m_run - m_new);
-        float psum = 0.f;
-        uint32_t pk[4];
-#pragma unroll
-        for (int x = 0; x < 8; x += 2) {
-            const float p0 = a[x] == NEG_INF ? 0.f : __expf(a[x] - m_new);
-            const float p1 = a[x + 1] == NEG_INF ? 0.f : __expf(a[x + 1] - m_new);
-            psum += p0 + p1;
-            if constexpr (FMT == CSA2_FP4) pk[x / 2] = pack_f16_rne(p0, p1);
-            else pk[x / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2v));
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
-        // ---- O^T[d][h] += C^T[d][e] P^T[e][h]: A operand element x is row
-        // 16 (x/4) + 4 kg + x%4, channel 16 dt + col (two transpose loads).
-        const uint16_t *tr0 = T + (4 * kg + (col >> 2)) * LS + 4 * (col & 3);
-        const uint16_t *tr1 = tr0 + 16 * LS;
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (s16x4 __attribute__((address_space(3))) *)(tr0 + 16 * (dt0 + dt)));
-            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (s16x4 __attribute__((address_space(3))) *)(tr1 + 16 * (dt0 + dt)));
-            const u32x4 av = {__builtin_bit_cast(uint32_t, s16x2{lo4[0], lo4[1]}),
-                              __builtin_bit_cast(uint32_t, s16x2{lo4[2], lo4[3]}),
-                              __builtin_bit_cast(uint32_t, s16x2{hi4[0], hi4[1]}),
-                              __builtin_bit_cast(uint32_t, s16x2{hi4[2], hi4[3]})};
-            o[dt] = o[dt] * alpha;
-            o[dt] = mma<FMT>(av, pb, o[dt]);
-        }
-        if (t + 1 < ntiles) gather_store<D, FMT, NT>(tile[(t + 1) & 1], buf, sbuf);
-        __syncthreads();
-    }
-
-    // ---- write this wave's 16 heads: lane holds O^T[16 dt + 4 kg + r][col]
-    l_run = bfly32(bfly16(l_run, OpAdd{}), OpAdd{});
-    const int h = hg * 16 + col;
-    if (nsplit == 1) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        uint16_t *orow = out + ((size_t)bq * H + h) * D + 16 * dt0 + 4 * kg;
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-            const uint32_t w0 = uint32_t(f32_to_bf16_rne(o[dt][0] * inv)) | (uint32_t(f32_to_bf16_rne(o[dt][1] * inv)) << 16);
-            const uint32_t w1 = uint32_t(f32_to_bf16_rne(o[dt][2] * inv)) | (uint32_t(f32_to_bf16_rne(o[dt][3] * inv)) << 16);
-            *reinterpret_cast<uint2 *>(orow + 16 * dt) = make_uint2(w0, w1);
-        }
-        if (lse && kg == 0 && dt0 == 0) lse[(size_t)bq * H + h] = l_run > 0.f ? m_run + logf(l_run) : NEG_INF;
-    } else {
-        const size_t pi = ((size_t)bq * H + h) * nsplit + split;  // a head's splits are adjacent
-        // the partial row in fp16 under a power-of-two scale per quarter of the
-        // channels (this wave's part spans 4 / DS quarters): its largest
-        // magnitude lands in [2^14, 2^15), so every value keeps fp16's 11
-        // significant bits and none overflows
-        float mx = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) mx = fmaxf(mx, fabsf(o[dt][r]));
-        mx = bfly32(bfly16(mx, OpMax{}), OpMax{});
-        int ex = 0;
-        if (mx > 0.f && mx <= __FLT_MAX__) {
-            frexpf(mx, &ex);
-            ex = min(max(ex - 15, -120), 120);
-        }
-        const float down = ldexpf(1.f, -ex);
-        uint16_t *prow = part_o + pi * D + 16 * dt0 + 4 * kg;
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++)
-            *reinterpret_cast<uint2 *>(prow + 16 * dt) =
-                make_uint2(pack_f16_rne(o[dt][0] * down, o[dt][1] * down), pack_f16_rne(o[dt][2] * down, o[dt][3] * down));
-        if (kg == 0) {
-#pragma unroll
-            for (int qq = 0; qq < 4 / DS; qq++) part_sc[pi * 4 + dpart * (4 / DS) + qq] = ldexpf(1.f, ex);
-        }
-        if (kg == 0 && dt0 == 0) part_ml[pi] = make_float2(m_run, l_run);
-    }
+    const f16x2 f = __builtin_bit_cast(f16x2, fbits | (fbits << 16));
+    const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 0) * f;
+    const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 1) * f;
+    const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 2) * f;
+    const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 3) * f;
+    return u32x4{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1), __builtin_bit_cast(uint32_t, v2),
+                 __builtin_bit_cast(uint32_t, v3)};
 }
 
 // ----------------------------------------------------------- split merge
@@ -775,6 +118,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t *__restrict
     const int64_t row = gid / tpr;  // (bq, h)
     const int c8 = (int)(gid % tpr);
     if (row >= (int64_t)BQ * H) return;
+    const int64_t bqr = row / H;
+    const int hr = (int)(row % H);
     const int quarter = COMB_CPT * c8 / (D / 4);  // the channels' scale slot
     float M = NEG_INF, Ls = 0.f;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -785,7 +130,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t *__restrict
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; u++) {
             // splits past the end read the last one and are dropped
-            const size_t pi = (size_t)row * nsplit + (s0 + u < nsplit ? s0 + u : nsplit - 1);
+            const size_t pi = ((size_t)bqr * nsplit + (s0 + u < nsplit ? s0 + u : nsplit - 1)) * H + hr;
             ml[u] = part_ml[pi];
             sc[u] = part_sc[pi * 4 + quarter];
             ph[u] = reinterpret_cast<const uint4 *>(part_o + pi * D)[c8];
@@ -900,48 +245,391 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
     if (lse && threadIdx.x == 0) lse[(size_t)bq * H + h] = Z > 0.f ? M + logf(Z) : NEG_INF;
 }
 
-// Heads per block: enough blocks to fill the chip (about 256) with as many
-// heads per block as that allows, so that fewer blocks gather the same rows.
-template <int D, int FMT, int HB, int SPLIT>
-void launch_mfma_hb(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                    float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s, const SelHandoff *sel) {
-    // two or more waves per head group (each owns a share of the channels)
-    // while that stays within 512 threads
-    constexpr int DS = HB == 1 ? (D >= 256 ? 4 : 2) : ((HB <= 4 && D >= 128) ? 2 : 1);
-    const int npairs = p.B * p.Q * p.nsplit;
-    const int NG = p.H / (16 * HB);
-    const int blocks = (npairs + 7) / 8 * 8 * NG;
-    if (sel)
-        hipLaunchKernelGGL((k_attn_mfma<D, FMT, HB, DS, SPLIT, true>), dim3(blocks), dim3(64 * HB * DS), 0, s,
-                           static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,
-                           scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, part_sc, *sel);
-    else
-        hipLaunchKernelGGL((k_attn_mfma<D, FMT, HB, DS, SPLIT, false>), dim3(blocks), dim3(64 * HB * DS), 0, s,
-                           static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,
-                           scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, part_sc, SelHandoff{});
-}
+// ------------------------------------------------------- split kernel
+// Block = one query x one split of ATT_SPLIT = 128 selected entries x HB =
+// HPW * HH heads, 4 HH waves.  The LDS read traffic per gathered row is what
+// bounds this step (S and O read every row from LDS), so the block is laid
+// out to read each row as few times as the registers allow:
+//  1. Every row of the split is requested at once (16-byte pieces in
+//     registers, one wave per 1 KiB of a bf16 row), then staged in LDS as the
+//     matrix-core operand type (FP4 rows decoded to fp16 on the way).
+//  2. S^T = C Q^T: wave (rg, hh) takes rows 32 rg .. 32 rg + 31 and heads
+//     hh HPW .. + HPW - 1 over all D channels, its queries held in registers
+//     for the whole contraction; each row fragment read from LDS feeds HPW/16
+//     matrix-core steps.  No partial logits cross waves.
+//  3. Softmax over the split: each head's maximum over the four row groups
+//     meets in LDS; p = exp(a - m) goes to LDS as P[head][row] (the
+//     matrix-core operand type), each row group's sum of p to LDS.
+//  4. O^T = C^T P^T: wave (cq, hh) takes channels cq D/4 .. + D/4 - 1 of the
+//     same heads; the row operand is read transposed from the staged rows,
+//     P^T from LDS; 32 rows per step, in row order.
+//  5. Output (one split: out / l, lse) or the split partial (fp16 under a
+//     power-of-two scale per head and quarter of the channels, m, l) for the
+//     merge kernel.
+// Every head's arithmetic (contraction order over channels and rows, the
+// sums of p over rows grouped by 32, the fixed tree over the four groups) is
+// the same whatever HB, so a query's result does not depend on the batch.
+template <int D, int FMT, int HPW, int HH>
+__global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__restrict__ q,
+                                                           const uint8_t *__restrict__ kv, int Q, int H, int64_t N,
+                                                           const int32_t *__restrict__ idx, int k, float scale,
+                                                           int nsplit, int npairs, uint16_t *__restrict__ out,
+                                                           float *__restrict__ lse, uint16_t *__restrict__ part_o,
+                                                           float2 *__restrict__ part_ml, float *__restrict__ part_sc) {
+    constexpr int NW = 4 * HH, NT = 64 * NW;
+    constexpr int HB = HPW * HH;      // heads of the block
+    constexpr int HT = HPW / 16;      // 16-head tiles of a wave
+    constexpr int KS = D / 32;        // contraction steps of S (32 channels each)
+    constexpr int LS = D + 8;         // LDS row stride in 16-bit elements (16-byte pad)
+    constexpr int ROWS = ATT_SPLIT;   // entries of a split
+    constexpr int PST = ROWS + 8;     // LDS stride of a head's P row
+    constexpr int DQ = D / 4;         // channels of an O wave (one quarter)
+    constexpr int DT = DQ / 16;       // 16-channel tiles of an O wave
+    constexpr int KT = ROWS / 32;     // contraction steps of O (32 rows each)
+    constexpr int RB = FMT == CSA2_FP4 ? D / 2 + D / 16 : 2 * D;  // bytes per stored row
+    static_assert(DQ % 16 == 0 && HPW % 16 == 0, "matrix-core tiles");
+    __shared__ __attribute__((aligned(16))) uint16_t rows_lds[ROWS * LS];
+    __shared__ __attribute__((aligned(16))) uint16_t p_lds[HB * PST];
+    __shared__ float mx_sh[4][HB];
+    __shared__ float l_sh[4][HB];
+    __shared__ float qsc_sh[HB];  // FP4: softmax scale times the head's query prescale
+    __shared__ __attribute__((aligned(16))) int32_t jsh[ROWS];
 
-template <int D, int FMT, int SPLIT>
-void launch_mfma_split(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                       float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s, const SelHandoff *sel) {
-    const int64_t pairs = (int64_t)p.B * p.Q * p.nsplit;
-    const int hgroups = p.H / 16;
-    int hb = hgroups;  // head groups per block
-    while (hb > 1 && pairs * (hgroups / hb) < 256) hb /= 2;
-    switch (hb) {
-        case 1: launch_mfma_hb<D, FMT, 1, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); break;
-        case 2: launch_mfma_hb<D, FMT, 2, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); break;
-        case 4: launch_mfma_hb<D, FMT, 4, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); break;
-        case 8: launch_mfma_hb<D, FMT, 8, SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); break;
-        default: throw Error(CSA2_EUNSUPPORTED, "matrix-core attention needs H in {16, 32, 64, 128}");
+    // Blocks go round-robin over the 8 XCDs (block L to XCD L % 8): XCD x
+    // takes the consecutive (query, split) pairs x P8 .. x P8 + P8 - 1, so that
+    // the blocks of a query share one L2 for its queries and, across head
+    // groups, for its rows.
+    const int NG = H / HB;
+    const int P8 = (npairs + 7) / 8;
+    const int L = blockIdx.x;
+    const int jx = (L / 8) / NG;
+    const int hgb = (L / 8) % NG;
+    const int pair = (L % 8) * P8 + jx;
+    if (jx >= P8 || pair >= npairs) return;
+    const int split = pair % nsplit;
+    const int bq = pair / nsplit;
+    const int b = bq / Q;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, kg = lane >> 4;
+    const int rq = wave & 3;   // row group (S) and channel quarter (O) of this wave
+    const int hh = wave >> 2;  // head half of the block
+    const int hw0 = hh * HPW;  // first head of this wave within the block
+    const int e_begin = split * ROWS;
+    const int ne = min(k, e_begin + ROWS) - e_begin;
+    const uint8_t *kvb = kv + (size_t)b * N * RB;
+
+    // the block's query heads first: they do not depend on the indices
+    constexpr int QS = D + 8;
+    constexpr int QPR = D / 8;                 // 16-byte pieces per head row
+    constexpr int QP = HB * QPR;
+    constexpr int QPT = (QP + NT - 1) / NT;
+    u32x4 qst[QPT];
+    {
+        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q + ((size_t)bq * H + hgb * HB) * D);
+#pragma unroll
+        for (int i = 0; i < QPT; i++) qst[i] = qsrc[QP % NT == 0 ? tid + NT * i : min(tid + NT * i, QP - 1)];
+    }
+    {
+        const int32_t *irow = idx + (size_t)bq * k + e_begin;
+        for (int e = tid; e < ROWS; e += NT) {
+            const int j = e < ne ? irow[e] : -1;
+            jsh[e] = (j >= 0 && j < N) ? j : -1;  // out-of-range entries are skipped like -1
+        }
+    }
+    __syncthreads();
+
+    // ---- 1. gather.  bf16: piece c = 16 bytes (8 channels) of row c / CPR at
+    // column c % CPR, a wave reads one whole 1 KiB row per instruction.  FP4:
+    // piece c = 4 code bytes (8 channels) and their scale byte, a wave reads one
+    // row's 256 code bytes per instruction; decoded to 16 bytes of fp16.
+    // Either way lane l writes 16 bytes at column l of a row: no LDS bank
+    // conflicts.  Entries of -1 read row 0 and are zeroed.
+    constexpr int PPR = D / 8;                 // 8-channel pieces per row
+    constexpr int NPC = ROWS * PPR;            // pieces of the split
+    constexpr int PPT = (NPC + NT - 1) / NT;  // pieces per thread
+    constexpr int GR = PPT > 16 ? 16 : PPT;    // pieces per thread in flight
+    static_assert(PPT % GR == 0, "whole rounds of pieces");
+    uint32_t gw[FMT == CSA2_FP4 ? GR : 1];     // FP4: code word
+    u32x4 gv[FMT == CSA2_FP4 ? 1 : GR];        // bf16: 16 bytes
+    uint32_t gs[GR];                           // FP4 scale byte | no-entry flag in bit 31
+    auto issue = [&](int r0) {
+#pragma unroll
+        for (int u = 0; u < GR; u++) {
+            const int c = tid + (r0 + u) * NT;
+            const int cs = (NPC % NT == 0 || c < NPC) ? c : 0;
+            const int r = cs / PPR, cc = cs % PPR;
+            const int j = jsh[r];
+            const uint8_t *row = kvb + (size_t)(j >= 0 ? j : 0) * RB;
+            uint32_t sc = 0;
+            if constexpr (FMT == CSA2_FP4) {
+                gw[u] = *reinterpret_cast<const uint32_t *>(row + cc * 4);
+                sc = row[D / 2 + cc / 2];
+            } else {
+                gv[u] = *reinterpret_cast<const u32x4 *>(row + cc * 16);
+            }
+            gs[u] = sc | (j < 0 ? 0x80000000u : 0u);
+        }
+    };
+    auto store = [&](int r0) {
+#pragma unroll
+        for (int u = 0; u < GR; u++) {
+            const int c = tid + (r0 + u) * NT;
+            if (NPC % NT != 0 && c >= NPC) continue;
+            const int r = c / PPR, cc = c % PPR;
+            const bool skip = gs[u] >> 31;
+            u32x4 v;
+            if constexpr (FMT == CSA2_FP4) v = fp4_word_to_f16x8(skip ? 0u : gw[u], skip ? 0u : gs[u] & 0xffu);
+            else v = skip ? u32x4{0u, 0u, 0u, 0u} : gv[u];
+            *reinterpret_cast<u32x4 *>(rows_lds + r * LS + cc * 8) = v;
+        }
+    };
+    issue(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- the block's query heads, once per block (each is the B operand of
+    // S^T for four waves): in flight from the start, staged in the row buffer
+    // (padded rows of D + 8) before the rows land; for FP4 rows converted to
+    // fp16 there under a power-of-two scale per head that keeps them below
+    // 32768 (a wave holds whole head rows: piece i of thread t is 16 bytes of
+    // head (t + NT i) / (D / 8))
+    static_assert(HB * QS <= ROWS * LS, "query staging fits the row buffer");
+    static_assert(QPR <= 64 && 64 % QPR == 0, "a head's query row lies within one wave");
+    {
+#pragma unroll
+        for (int i = 0; i < QPT; i++) {
+            const int pc = tid + NT * i;
+            const int hq = pc / QPR, cq = pc % QPR;
+            u32x4 v = qst[i];
+            if constexpr (FMT == CSA2_FP4) {
+                float amax = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(v[e] & 0xffffu)), fabsf(bf16_to_f32(v[e] >> 16))));
+                // the QPR consecutive lanes holding the head's row
+                if constexpr (QPR == 64) {
+                    amax = wave_max(amax);
+                } else {
+#pragma unroll
+                    for (int o = 1; o < QPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+                }
+                int ex = 0;
+                if (amax > 32768.f) ex = (int)ceilf(log2f(amax / 32768.f));
+                const float down = ldexpf(1.f, -ex);
+                if (cq == 0 && (QP % NT == 0 || pc < QP)) qsc_sh[hq] = ldexpf(scale, ex);
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    v[e] = pack_f16_rne(bf16_to_f32(v[e] & 0xffffu) * down, bf16_to_f32(v[e] >> 16) * down);
+            }
+            if (QP % NT == 0 || pc < QP) *reinterpret_cast<u32x4 *>(rows_lds + hq * QS + cq * 8) = v;
+        }
+    }
+    __syncthreads();
+    u32x4 qf[HT][KS];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+        for (int s2 = 0; s2 < KS; s2++)
+            qf[ht][s2] = *reinterpret_cast<const u32x4 *>(rows_lds + (hw0 + 16 * ht + col) * QS + 32 * s2 + 8 * kg);
+    float qscale[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) qscale[ht] = FMT == CSA2_FP4 ? qsc_sh[hw0 + 16 * ht + col] : scale;
+    __syncthreads();  // the row buffer is free again
+
+    store(0);
+#pragma unroll
+    for (int r0 = GR; r0 < PPT; r0 += GR) {
+        issue(r0);
+        store(r0);
+    }
+    __syncthreads();  // rows staged
+
+    // ---- 2. S^T for rows 32 rq + 16 h2 + (lane rows), heads hw0 + 16 ht + col
+    f32x4 sacc[2][HT];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) sacc[h2][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+        const uint16_t *arow = rows_lds + (32 * rq + col) * LS + 8 * kg;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; s2++) {
+            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(arow + 32 * s2);
+            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(arow + 16 * LS + 32 * s2);
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++) {
+                sacc[0][ht] = mma<FMT>(a0, qf[ht][s2], sacc[0][ht]);
+                sacc[1][ht] = mma<FMT>(a1, qf[ht][s2], sacc[1][ht]);
+            }
+        }
+    }
+    // ---- 3. softmax over the split. Lane holds rows 32 rq + 16 h2 + 4 kg + i.
+    const int4 jv0 = *reinterpret_cast<const int4 *>(jsh + 32 * rq + 4 * kg);
+    const int4 jv1 = *reinterpret_cast<const int4 *>(jsh + 32 * rq + 16 + 4 * kg);
+    const int jj[8] = {jv0.x, jv0.y, jv0.z, jv0.w, jv1.x, jv1.y, jv1.z, jv1.w};
+    float mloc[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) {
+        float mt = NEG_INF;
+#pragma unroll
+        for (int x = 0; x < 8; x++) {
+            const float v = jj[x] >= 0 ? sacc[x >> 2][ht][x & 3] * qscale[ht] : NEG_INF;
+            sacc[x >> 2][ht][x & 3] = v;
+            mt = fmaxf(mt, v);
+        }
+        mloc[ht] = bfly32(bfly16(mt, OpMax{}), OpMax{});
+        if (kg == 0) mx_sh[rq][hw0 + 16 * ht + col] = mloc[ht];
+    }
+    __syncthreads();
+    float mh[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) {
+        const int hd = hw0 + 16 * ht + col;
+        mh[ht] = fmaxf(fmaxf(mx_sh[0][hd], mx_sh[1][hd]), fmaxf(mx_sh[2][hd], mx_sh[3][hd]));
+        float ls = 0.f;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+            float pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float a = sacc[h2][ht][i];
+                pv[i] = a == NEG_INF ? 0.f : __expf(a - mh[ht]);
+                ls += pv[i];
+            }
+            uint32_t w0, w1;
+            if constexpr (FMT == CSA2_FP4) {
+                w0 = pack_f16_rne(pv[0], pv[1]);
+                w1 = pack_f16_rne(pv[2], pv[3]);
+            } else {
+                w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{pv[0], pv[1]}), bf16x2v));
+                w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{pv[2], pv[3]}), bf16x2v));
+            }
+            *reinterpret_cast<uint2 *>(p_lds + hd * PST + 32 * rq + 16 * h2 + 4 * kg) = make_uint2(w0, w1);
+        }
+        ls = bfly32(bfly16(ls, OpAdd{}), OpAdd{});
+        if (kg == 0) l_sh[rq][hd] = ls;
+    }
+    __syncthreads();
+
+    // ---- 4. O^T[channel][head] for channels rq DQ + 16 dt + (lane rows), heads hw0 + 16 ht + col
+    f32x4 oacc[DT][HT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) oacc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KT; kt++) {
+        // operand element x <-> row 32 kt + 16 (x / 4) + 4 kg + x % 4, in both operands
+        u32x4 pb[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) {
+            const uint16_t *pp = p_lds + (hw0 + 16 * ht + col) * PST + 32 * kt + 4 * kg;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(pp);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(pp + 16);
+            pb[ht] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+        const uint16_t *tr0 = rows_lds + (32 * kt + 4 * kg + (col >> 2)) * LS + 4 * (col & 3) + rq * DQ;
+        const uint16_t *tr1 = tr0 + 16 * LS;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)(tr0 + 16 * dt));
+            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)(tr1 + 16 * dt));
+            const u32x4 av = {__builtin_bit_cast(uint32_t, s16x2{lo4[0], lo4[1]}),
+                              __builtin_bit_cast(uint32_t, s16x2{lo4[2], lo4[3]}),
+                              __builtin_bit_cast(uint32_t, s16x2{hi4[0], hi4[1]}),
+                              __builtin_bit_cast(uint32_t, s16x2{hi4[2], hi4[3]})};
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++) oacc[dt][ht] = mma<FMT>(av, pb[ht], oacc[dt][ht]);
+        }
+    }
+
+    // ---- 5. output (one split: out / l, lse) or the split partial (fp16
+    // under a power-of-two scale per head and channel quarter, m, l), staged
+    // in the free row buffer as [head][channel] so that the block writes its
+    // HB consecutive rows of D in whole 16-byte pieces per lane
+    __syncthreads();  // every wave is done with the rows
+    constexpr int OS = D + 8;
+    uint16_t *stage = rows_lds;
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) {
+        const int hd = hw0 + 16 * ht + col;
+        const int h = hgb * HB + hd;
+        const float l = (l_sh[0][hd] + l_sh[1][hd]) + (l_sh[2][hd] + l_sh[3][hd]);
+        const float m = mh[ht];
+        uint16_t *srow = stage + hd * OS + rq * DQ + 4 * kg;
+        if (nsplit == 1) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const f32x4 o = oacc[dt][ht];
+                const uint32_t w0 = uint32_t(f32_to_bf16_rne(o[0] * inv)) | (uint32_t(f32_to_bf16_rne(o[1] * inv)) << 16);
+                const uint32_t w1 = uint32_t(f32_to_bf16_rne(o[2] * inv)) | (uint32_t(f32_to_bf16_rne(o[3] * inv)) << 16);
+                *reinterpret_cast<uint2 *>(srow + 16 * dt) = make_uint2(w0, w1);
+            }
+            if (lse && kg == 0 && rq == 0) lse[(size_t)bq * H + h] = l > 0.f ? m + logf(l) : NEG_INF;
+        } else {
+            const size_t pi = ((size_t)bq * nsplit + split) * H + h;
+            float mx = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) mx = fmaxf(mx, fabsf(oacc[dt][ht][r]));
+            mx = bfly32(bfly16(mx, OpMax{}), OpMax{});
+            // ex with mx in [2^(ex+14), 2^(ex+15)), from the exponent field,
+            // clamped to [-120, 120] (subnormal maxima take -120; zero and
+            // non-finite ones 0)
+            const int ef = (int)((__float_as_uint(mx) >> 23) & 0xffu);
+            const int ex = ef == 255 ? 0 : ef == 0 ? (mx > 0.f ? -120 : 0) : min(max(ef - 126 - 15, -120), 120);
+            const float down = __uint_as_float((uint32_t)(127 - ex) << 23);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const f32x4 o = oacc[dt][ht];
+                *reinterpret_cast<uint2 *>(srow + 16 * dt) =
+                    make_uint2(pack_f16_rne(o[0] * down, o[1] * down), pack_f16_rne(o[2] * down, o[3] * down));
+            }
+            if (kg == 0) part_sc[pi * 4 + rq] = __uint_as_float((uint32_t)(127 + ex) << 23);
+            if (kg == 0 && rq == 0) part_ml[pi] = make_float2(m, l);
+        }
+    }
+    __syncthreads();
+    {
+        uint16_t *dst = nsplit == 1 ? out + ((size_t)bq * H + hgb * HB) * D
+                                    : part_o + (((size_t)bq * nsplit + split) * H + hgb * HB) * D;
+        constexpr int OP = HB * D / 8;  // 16-byte pieces of the block's rows
+#pragma unroll
+        for (int i = tid; i < OP; i += NT) {
+            const int r = i / (D / 8), c = i % (D / 8);
+            *reinterpret_cast<u32x4 *>(dst + (size_t)r * D + 8 * c) =
+                *reinterpret_cast<const u32x4 *>(stage + r * OS + 8 * c);
+        }
     }
 }
 
+// Heads per block: as many as keep at least 256 blocks (one per compute unit),
+// from 64 down to 16; the blocks that share a split's rows sit on one XCD.
 template <int D, int FMT>
-void launch_mfma(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                 float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s, const SelHandoff *sel) {
-    launch_mfma_split<D, FMT, ATT_SPLIT>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel);
+void launch_split(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
+                  float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s) {
+    const int npairs = p.B * p.Q * p.nsplit;
+    int hb = p.H < 64 ? p.H : 64;
+    while (hb > 16 && (int64_t)npairs * (p.H / hb) < 256) hb /= 2;
+    const int NG = p.H / hb;
+    const int blocks = 8 * ((npairs + 7) / 8) * NG;
+#define CSA2_SPLIT_LAUNCH(HPW, HH)                                                                                   \
+    hipLaunchKernelGGL((k_attn_split<D, FMT, HPW, HH>), dim3(blocks), dim3(256 * HH), 0, s,                           \
+                       static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,   \
+                       scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, part_sc)
+    switch (hb) {
+        case 64: CSA2_SPLIT_LAUNCH(32, 2); break;
+        case 32: CSA2_SPLIT_LAUNCH(16, 2); break;
+        case 16: CSA2_SPLIT_LAUNCH(16, 1); break;
+        default: throw Error(CSA2_EUNSUPPORTED, "matrix-core attention needs H in {16, 32, 64, 128}");
+    }
+#undef CSA2_SPLIT_LAUNCH
 }
+
+
 
 }  // namespace
 
@@ -967,13 +655,9 @@ size_t attn_workspace(const AttnPlan &p) {
     return c.used;
 }
 
-bool attn_handoff_supported(const AttnPlan &p, int64_t nwords) {
-    // the bitmap must fit the kernel's LDS tile buffers with room for a band
-    return p.mfma && (size_t)((nwords + 3) & ~int64_t(3)) * 4 + 1024 * 16 <= (size_t)2 * ATT_SUB * (p.D + 8) * 2;
-}
 
 void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-              float *lse, void *ws, size_t ws_bytes, hipStream_t s, const SelHandoff *sel) {
+              float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
     const int BQ = p.B * p.Q;
     if (!p.mfma) {
         size_t lds = sizeof(float) * ((size_t)p.D + p.k);
@@ -994,8 +678,8 @@ void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *i
     }
 #define CSA2_ATT_CASE(d)                                                                             \
     case d:                                                                                          \
-        if (p.kv_dt == CSA2_FP4) launch_mfma<d, CSA2_FP4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); \
-        else launch_mfma<d, CSA2_BF16>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel);                   \
+        if (p.kv_dt == CSA2_FP4) launch_split<d, CSA2_FP4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s); \
+        else launch_split<d, CSA2_BF16>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s);                   \
         break;
     switch (p.D) {
         CSA2_ATT_CASE(64)

@@ -86,12 +86,8 @@ struct AttnPlan {
 AttnPlan attn_plan(int q_dt, int kv_dt, int B, int Q, int H, int D, int64_t N, int k);
 bool attn_supported(const AttnPlan &p);
 size_t attn_workspace(const AttnPlan &p);
-// With `sel`, the selected entries come from a certified selection's records
-// (finished in the kernel's prologue, which also writes sel->idx / sel->count)
-// instead of from idx.
 void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-              float *lse, void *ws, size_t ws_bytes, hipStream_t s, const SelHandoff *sel = nullptr);
-bool attn_handoff_supported(const AttnPlan &p, int64_t nwords);
+              float *lse, void *ws, size_t ws_bytes, hipStream_t s);
 
 // ------------------------------------------------------------ compression
 size_t compress_workspace(int dt, int64_t n_out, int D, int m, int halo);
