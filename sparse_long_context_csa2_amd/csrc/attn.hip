@@ -245,6 +245,177 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
     if (lse && threadIdx.x == 0) lse[(size_t)bq * H + h] = Z > 0.f ? M + logf(Z) : NEG_INF;
 }
 
+// ------------------------------------------- selection finish (per block)
+// The certified top-k's last step, finished where the entries are consumed.
+// A query's selected set is its IN entries (certainly kept, in ascending
+// order from the selection kernel) and the best rr = min(K - |IN|, |BAND|)
+// band entries by (binary64 score descending, slot ascending).  The splits
+// take positions 0 .. |IN| - 1 from the IN list and |IN| .. |IN| + rr - 1 from
+// the chosen band entries in slot order; so only the blocks whose split
+// reaches past |IN| (usually one per query) rank the band, and one block per
+// query (the split holding position |IN|) writes the ascending index list:
+// the IN bitmap with the chosen band bits set, compacted.  Nothing crosses
+// blocks: everything comes from the earlier kernels' records.  `scr` is LDS
+// scratch of `scr_words` words (the row buffer, before any row is staged).
+template <int NT>
+__device__ uint32_t att_block_sum(uint32_t v, uint32_t *red) {
+    v = wave_sum_u32(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; i++) t += red[i];
+    return t;
+}
+
+// Band pick: the chosen band entries' bits in `bmb` (n / 32 words of LDS,
+// zeroed here) and, for a block whose split reaches them, their entries in
+// jsh (positions |IN| + rank in slot order).  `scr` (scr_words of LDS) holds
+// the band's keys and slots while they are ranked.
+template <int NT>
+__device__ void att_sel_band(const SelHandoff &sel, int bq, int32_t in_cnt, int32_t nb, int32_t rr, int e_begin,
+                             int ne, bool band_blk, int32_t spec_slot, double spec_score, uint32_t *bmb,
+                             uint32_t *scr, int scr_words, int32_t *jsh, uint32_t *red) {
+    const int tid = threadIdx.x;
+    const int64_t n = sel.n;
+    const int nw = (int)((n + 31) / 32);  // <= 1024 on this path
+    const int32_t *list = sel.band + (size_t)bq * sel.band_cap;
+    const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
+    const int32_t *cq = sel.cand ? sel.cand + (size_t)bq * n : nullptr;
+    for (int w = tid; w < nw; w += NT) bmb[w] = 0u;
+    const int cap = scr_words / 4;
+    u32x4 *ent = reinterpret_cast<u32x4 *>(scr);  // (key lo, key hi, slot, 0)
+    if (nb <= cap) {
+        // the first NT entries arrived with the block's first loads
+        for (int32_t i = tid; i < nb; i += NT) {
+            const int32_t sl = i == tid ? spec_slot : list[i];
+            const uint64_t kk = dkey(i == tid ? spec_score : bs[i]);
+            ent[i] = u32x4{(uint32_t)kk, (uint32_t)(kk >> 32), (uint32_t)sl, 0u};
+        }
+    }
+    __syncthreads();
+    if (nb <= cap) {
+        // entry i is ranked by P consecutive lanes, each counting the entries
+        // ahead of it among every P-th partner (eight partner reads in
+        // flight); (key, slot) is ahead iff key larger, or equal and slot smaller
+        const int P = nb * 16 <= NT ? 16 : nb * 8 <= NT ? 8 : nb * 4 <= NT ? 4 : nb * 2 <= NT ? 2 : 1;
+        const int per = NT / P;
+        for (int32_t i0 = 0; i0 < nb; i0 += per) {
+            const int32_t i = i0 + tid / P;
+            const int part = tid % P;
+            const bool act = i < nb;
+            const u32x4 me = ent[act ? i : 0];
+            const uint64_t ki = (uint64_t)me[0] | ((uint64_t)me[1] << 32);
+            const int32_t si = (int32_t)me[2];
+            int32_t rank = 0;
+            for (int32_t j0 = part; j0 < nb; j0 += 8 * P) {
+                u32x4 o[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const int32_t j = j0 + u * P;
+                    o[u] = ent[j < nb ? j : (act ? i : 0)];  // past the end: itself, which is not ahead
+                }
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const uint64_t kj = (uint64_t)o[u][0] | ((uint64_t)o[u][1] << 32);
+                    rank += (int)((kj > ki) | ((kj == ki) & ((int32_t)o[u][2] < si)));
+                }
+            }
+            for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
+            if (act && part == 0 && rank < rr) atomicOr(&bmb[si >> 5], 1u << (si & 31));
+        }
+    } else {
+        // a band larger than the scratch: the rr-th best key by bisection
+        // over the records, then the tie cut by slot
+        uint64_t lo = 0, hi = ~0ull;  // largest key t with #(key >= t) >= rr
+        while (lo < hi) {
+            const uint64_t mid = lo + (hi - lo) / 2 + 1;
+            uint32_t c = 0;
+            for (int32_t i = tid; i < nb; i += NT) c += dkey(bs[i]) >= mid;
+            if (att_block_sum<NT>(c, red) >= (uint32_t)rr) lo = mid;
+            else hi = mid - 1;
+        }
+        const uint64_t tau = lo;
+        uint32_t gt = 0;
+        for (int32_t i = tid; i < nb; i += NT) gt += dkey(bs[i]) > tau;
+        const uint32_t need = (uint32_t)rr - att_block_sum<NT>(gt, red);
+        int64_t sl0 = 0, sl1 = n - 1;  // smallest slot cut with #(key == tau, slot <= cut) >= need
+        while (sl0 < sl1) {
+            const int64_t mid = sl0 + (sl1 - sl0) / 2;
+            uint32_t c = 0;
+            for (int32_t i = tid; i < nb; i += NT) c += dkey(bs[i]) == tau && list[i] <= mid;
+            if (att_block_sum<NT>(c, red) >= need) sl1 = mid;
+            else sl0 = mid + 1;
+        }
+        for (int32_t i = tid; i < nb; i += NT) {
+            const uint64_t ki = dkey(bs[i]);
+            const int32_t si = list[i];
+            if (ki > tau || (ki == tau && si <= sl0 && need > 0)) atomicOr(&bmb[si >> 5], 1u << (si & 31));
+        }
+    }
+    __syncthreads();
+    if (band_blk) {
+        // positions |IN| + (chosen entries before it in slot order); thread t owns words t * per ..
+        const int per = (nw + NT - 1) / NT;
+        const int w0 = tid * per;
+        uint32_t c = 0;
+        for (int w = w0; w < w0 + per && w < nw; w++) c += (uint32_t)__builtin_popcount(bmb[w]);
+        const uint32_t incl = wave_incl_scan_u32(c);
+        const int wave = tid >> 6, lane = tid & 63;
+        if (lane == 63) red[wave] = incl;
+        __syncthreads();
+        uint32_t pos = (uint32_t)in_cnt + incl - c;
+#pragma unroll
+        for (int i = 0; i < NT / 64; i++) pos += i < wave ? red[i] : 0u;
+        for (int w = w0; w < w0 + per && w < nw; w++)
+            for (uint32_t bb = bmb[w]; bb; bb &= bb - 1) {
+                const int32_t sl = w * 32 + __builtin_ctz(bb);
+                if (pos >= (uint32_t)e_begin && pos < (uint32_t)(e_begin + ne)) jsh[pos - e_begin] = cq ? cq[sl] : sl;
+                pos++;
+            }
+        __syncthreads();
+    }
+}
+
+// The ascending index list of the query: the IN bitmap with the chosen band
+// bits set (words `inw`, thread t holding words t * PW ..), compacted; -1 past
+// the kept count.
+template <int NT, int PW>
+__device__ void att_sel_output(const SelHandoff &sel, int bq, int k, int32_t kept, const uint32_t (&inw)[PW],
+                               uint32_t *red) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t n = sel.n;
+    const int nw = (int)((n + 31) / 32);
+    const int w0 = tid * PW;
+    const int32_t *cq = sel.cand ? sel.cand + (size_t)bq * n : nullptr;
+    uint32_t bits[PW], c = 0;
+#pragma unroll
+    for (int u = 0; u < PW; u++) {
+        bits[u] = w0 + u < nw ? inw[u] : 0u;
+        c += (uint32_t)__builtin_popcount(bits[u]);
+    }
+    const uint32_t incl = wave_incl_scan_u32(c);
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    uint32_t pos = incl - c;
+#pragma unroll
+    for (int i = 0; i < NT / 64; i++) pos += i < wave ? red[i] : 0u;
+    int32_t *orow = sel.idx + (size_t)bq * k;
+#pragma unroll
+    for (int u = 0; u < PW; u++)
+        for (uint32_t bb = bits[u]; bb; bb &= bb - 1) {
+            if (pos < (uint32_t)k) {
+                const int32_t sl = (w0 + u) * 32 + __builtin_ctz(bb);
+                orow[pos] = cq ? cq[sl] : sl;
+            }
+            pos++;
+        }
+    for (int32_t i = kept + tid; i < k; i += NT) orow[i] = -1;
+    if (tid == 0 && sel.count) sel.count[bq] = kept;
+    __syncthreads();
+}
+
 // ------------------------------------------------------- split kernel
 // Block = one query x one split of ATT_SPLIT = 128 selected entries x HB =
 // HPW * HH heads, 4 HH waves.  The LDS read traffic per gathered row is what
@@ -269,13 +440,14 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
 // Every head's arithmetic (contraction order over channels and rows, the
 // sums of p over rows grouped by 32, the fixed tree over the four groups) is
 // the same whatever HB, so a query's result does not depend on the batch.
-template <int D, int FMT, int HPW, int HH>
+template <int D, int FMT, int HPW, int HH, bool SEL>
 __global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__restrict__ q,
                                                            const uint8_t *__restrict__ kv, int Q, int H, int64_t N,
                                                            const int32_t *__restrict__ idx, int k, float scale,
                                                            int nsplit, int npairs, uint16_t *__restrict__ out,
                                                            float *__restrict__ lse, uint16_t *__restrict__ part_o,
-                                                           float2 *__restrict__ part_ml, float *__restrict__ part_sc) {
+                                                           float2 *__restrict__ part_ml, float *__restrict__ part_sc,
+                                                           SelHandoff sel) {
     constexpr int NW = 4 * HH, NT = 64 * NW;
     constexpr int HB = HPW * HH;      // heads of the block
     constexpr int HT = HPW / 16;      // 16-head tiles of a wave
@@ -329,7 +501,46 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__re
 #pragma unroll
         for (int i = 0; i < QPT; i++) qst[i] = qsrc[QP % NT == 0 ? tid + NT * i : min(tid + NT * i, QP - 1)];
     }
-    {
+    // certified selection finished here (SEL): the query's IN count, band size
+    // and chosen band count; the block that writes the index list keeps its
+    // IN bitmap words (loaded with everything else, before any wait)
+    __shared__ uint32_t sred[NT / 64];
+    constexpr int SPW = (1024 + NT - 1) / NT;  // IN bitmap words per thread (n <= 32768)
+    uint32_t inw[SPW];
+    int32_t in_cnt = 0, rr = 0;
+    bool out_blk = false;
+    if constexpr (SEL) {
+        // speculative: the last split usually holds the band's part of the set,
+        // so it loads the first NT band records with the target record
+        const bool spec = split == nsplit - 1;
+        const size_t bo = (size_t)bq * sel.band_cap + (tid < sel.band_cap ? tid : 0);
+        const int32_t spec_slot = spec ? sel.band[bo] : 0;
+        const double spec_score = spec ? sel.band_score[bo] : 0.0;
+        const SelTarget t = sel.sq[bq].t[0];
+        in_cnt = t.in_cnt;
+        const int32_t nb = t.band_cnt;
+        rr = max(0, min(k - in_cnt, nb));
+        out_blk = hgb == 0 && split == min(in_cnt, k - 1) / ROWS;
+        const int nw = (int)sel.nwords;
+        const uint32_t *inbm = sel.bitmap + (size_t)bq * sel.nwords;
+#pragma unroll
+        for (int u = 0; u < SPW; u++) inw[u] = (out_blk && tid * SPW + u < nw) ? inbm[tid * SPW + u] : 0u;
+        const int32_t *il = sel.in_list + (size_t)bq * sel.in_cap;
+        for (int e = tid; e < ROWS; e += NT) {
+            const int p = e_begin + e;
+            jsh[e] = (e < ne && p < in_cnt) ? il[p] : -1;
+        }
+        const bool band_blk = rr > 0 && e_begin + ne > in_cnt;
+        if (band_blk || (out_blk && rr > 0)) {
+            const bool have = spec && tid < sel.band_cap;
+            att_sel_band<NT>(sel, bq, in_cnt, nb, rr, e_begin, ne, band_blk,
+                             have ? spec_slot : sel.band[bo], have ? spec_score : sel.band_score[bo],
+                             reinterpret_cast<uint32_t *>(p_lds), reinterpret_cast<uint32_t *>(rows_lds),
+                             ROWS * LS / 2, jsh, sred);
+        }
+        else if (out_blk)
+            for (int w = tid; w < nw; w += NT) reinterpret_cast<uint32_t *>(p_lds)[w] = 0u;
+    } else {
         const int32_t *irow = idx + (size_t)bq * k + e_begin;
         for (int e = tid; e < ROWS; e += NT) {
             const int j = e < ne ? irow[e] : -1;
@@ -383,6 +594,16 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__re
             *reinterpret_cast<u32x4 *>(rows_lds + r * LS + cc * 8) = v;
         }
     };
+    if constexpr (SEL) {
+        // the chosen band bits join the output block's IN words in registers
+        // (P's LDS is reused by the softmax); the list is written at the end
+        if (out_blk) {
+            const int nw = (int)sel.nwords;
+#pragma unroll
+            for (int u = 0; u < SPW; u++)
+                if (tid * SPW + u < nw) inw[u] |= reinterpret_cast<const uint32_t *>(p_lds)[tid * SPW + u];
+        }
+    }
     issue(0);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -604,22 +825,37 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__re
                 *reinterpret_cast<const u32x4 *>(stage + r * OS + 8 * c);
         }
     }
+    // the query's ascending index list (SEL: the block holding position |IN|),
+    // last, so that its stores do not stand in the loads' way
+    if constexpr (SEL) {
+        if (out_blk) att_sel_output<NT, SPW>(sel, bq, k, in_cnt + rr, inw, sred);
+    }
 }
 
 // Heads per block: as many as keep at least 256 blocks (one per compute unit),
 // from 64 down to 16; the blocks that share a split's rows sit on one XCD.
 template <int D, int FMT>
 void launch_split(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-                  float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s) {
+                  float *lse, uint16_t *part_o, float2 *part_ml, float *part_sc, hipStream_t s,
+                  const SelHandoff *sel) {
     const int npairs = p.B * p.Q * p.nsplit;
     int hb = p.H < 64 ? p.H : 64;
     while (hb > 16 && (int64_t)npairs * (p.H / hb) < 256) hb /= 2;
     const int NG = p.H / hb;
     const int blocks = 8 * ((npairs + 7) / 8) * NG;
 #define CSA2_SPLIT_LAUNCH(HPW, HH)                                                                                   \
-    hipLaunchKernelGGL((k_attn_split<D, FMT, HPW, HH>), dim3(blocks), dim3(256 * HH), 0, s,                           \
-                       static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N, idx, p.k,   \
-                       scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o, part_ml, part_sc)
+    do {                                                                                                             \
+        if (sel)                                                                                                     \
+            hipLaunchKernelGGL((k_attn_split<D, FMT, HPW, HH, true>), dim3(blocks), dim3(256 * HH), 0, s,             \
+                               static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N,     \
+                               idx, p.k, scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o,         \
+                               part_ml, part_sc, *sel);                                                              \
+        else                                                                                                         \
+            hipLaunchKernelGGL((k_attn_split<D, FMT, HPW, HH, false>), dim3(blocks), dim3(256 * HH), 0, s,            \
+                               static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kv), p.Q, p.H, p.N,     \
+                               idx, p.k, scale, p.nsplit, npairs, static_cast<uint16_t *>(out), lse, part_o,         \
+                               part_ml, part_sc, SelHandoff{});                                                      \
+    } while (0)
     switch (hb) {
         case 64: CSA2_SPLIT_LAUNCH(32, 2); break;
         case 32: CSA2_SPLIT_LAUNCH(16, 2); break;
@@ -641,6 +877,12 @@ AttnPlan attn_plan(int q_dt, int kv_dt, int B, int Q, int H, int D, int64_t N, i
     return p;
 }
 
+bool attn_handoff_supported(const AttnPlan &p, const SelPlan &sp) {
+    // the matrix-core kernel finishes the selection in its prologue when the
+    // IN bitmap is at most 1024 words (the one-block selection path)
+    return p.mfma && sp.certified && sp.nwords <= 1024;
+}
+
 bool attn_supported(const AttnPlan &p) {
     if (p.mfma) return (int64_t)p.B * p.Q * p.nsplit * (p.H / 16) + 8 * (p.H / 16) <= INT32_MAX;  // blocks fit an int
     return (p.D + p.k) <= 16384;
@@ -657,7 +899,7 @@ size_t attn_workspace(const AttnPlan &p) {
 
 
 void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-              float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
+              float *lse, void *ws, size_t ws_bytes, hipStream_t s, const SelHandoff *sel) {
     const int BQ = p.B * p.Q;
     if (!p.mfma) {
         size_t lds = sizeof(float) * ((size_t)p.D + p.k);
@@ -678,8 +920,8 @@ void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *i
     }
 #define CSA2_ATT_CASE(d)                                                                             \
     case d:                                                                                          \
-        if (p.kv_dt == CSA2_FP4) launch_split<d, CSA2_FP4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s); \
-        else launch_split<d, CSA2_BF16>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s);                   \
+        if (p.kv_dt == CSA2_FP4) launch_split<d, CSA2_FP4>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel); \
+        else launch_split<d, CSA2_BF16>(p, q, kv, idx, scale, out, lse, part_o, part_ml, part_sc, s, sel);                   \
         break;
     switch (p.D) {
         CSA2_ATT_CASE(64)

@@ -32,10 +32,12 @@ struct SelQuery {
 };
 // What a certified selection leaves for its top-k target when the final pick
 // and compaction are left to the consumer (the attention kernel): the IN
-// bitmap, the band list with its binary64 scores, and where the ascending
-// index list and its count go.
+// entries in ascending order, the IN bitmap, the band list with its binary64
+// scores, and where the ascending index list and its count go.
 struct SelHandoff {
     const SelQuery *sq;
+    const int32_t *in_list;  // [BQ][in_cap] IN entries of target 0, ascending
+    int64_t in_cap;
     const uint32_t *bitmap;  // [BQ][nwords] IN bits of target 0
     int64_t nwords;
     const int32_t *band;     // [BQ][band_cap] band slots of target 0
@@ -86,8 +88,12 @@ struct AttnPlan {
 AttnPlan attn_plan(int q_dt, int kv_dt, int B, int Q, int H, int D, int64_t N, int k);
 bool attn_supported(const AttnPlan &p);
 size_t attn_workspace(const AttnPlan &p);
+// With `sel`, the selected entries come from a certified selection's records
+// (the top-k target finished in the kernel: each block derives its own split,
+// and one block per query writes sel->idx / sel->count) instead of from idx.
 void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
-              float *lse, void *ws, size_t ws_bytes, hipStream_t s);
+              float *lse, void *ws, size_t ws_bytes, hipStream_t s, const SelHandoff *sel = nullptr);
+bool attn_handoff_supported(const AttnPlan &p, const SelPlan &sp);
 
 // ------------------------------------------------------------ compression
 size_t compress_workspace(int dt, int64_t n_out, int D, int m, int halo);

@@ -752,6 +752,7 @@ struct OneArgs {
     int64_t nwords;
     int32_t *band;
     int64_t band_cap;
+    int32_t *in_list;  // certified, nullable: target 0's IN entries in ascending order, [BQ][K0]
 };
 
 // Smallest key in [lk, hk] whose bin is >= target (hk + 1 if none): a 64-way
@@ -958,6 +959,21 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
         if constexpr (CERT) {
             uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
             for (int64_t wd = tid; wd < nwords; wd += ONE_NT) gbm[wd] = bm[wd];
+            if (tg == 0 && a.in_list) {
+                // the IN entries in slot order: thread tid's word at the prefix of the popcounts
+                const uint32_t c = (uint32_t)__builtin_popcount(win);
+                const uint32_t inc = wave_incl_scan_u32(c);
+                if (lane == 63) red[wave] = inc;
+                __syncthreads();
+                uint32_t pos = inc - c;
+#pragma unroll
+                for (int i = 0; i < ONE_NT / 64; i++) pos += i < wave ? red[i] : 0u;
+                int32_t *il = a.in_list + (size_t)bq * K;
+                for (uint32_t m = win; m; m &= m - 1) {
+                    const int sl = s0 + __builtin_ctz(m);
+                    il[pos++] = cp ? cp[sl] : sl;
+                }
+            }
             if (tid == 0) {
                 SelTarget t;
                 t.lo = tlo;
@@ -1463,6 +1479,8 @@ SelPlan sel_plan(int BQ, int64_t n, int K0, int K1, bool certified) {
 
 static bool small_path(const SelPlan &p) { return p.n <= ONE_N; }
 
+bool sel_handoff_supported(const SelPlan &p) { return p.certified && small_path(p); }
+
 size_t sel_workspace(const SelPlan &p, bool own_stats) {
     Carve c(nullptr, 0);
     if (own_stats && !small_path(p)) c.take<TileStat>((size_t)p.BQ * p.ntiles);
@@ -1472,10 +1490,11 @@ size_t sel_workspace(const SelPlan &p, bool own_stats) {
     c.take<uint32_t>((size_t)p.ntgt * p.BQ * p.nwords);
     c.take<int32_t>((size_t)p.ntgt * p.BQ * p.band_cap);
     if (p.certified) c.take<double>((size_t)p.ntgt * p.BQ * p.band_cap);
+    if (sel_handoff_supported(p)) c.take<int32_t>((size_t)p.BQ * p.K0);  // IN list of the top-k target
     return c.used;
 }
 
-bool sel_handoff_supported(const SelPlan &p) { return p.certified && p.nwords <= 8192; }
+
 
 void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats_in,
              const RescoreArgs *rs, int32_t *out0, int32_t *count0, int32_t *out1, void *ws, size_t ws_bytes,
@@ -1489,7 +1508,9 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     uint32_t *bitmap = c.take<uint32_t>((size_t)p.ntgt * p.BQ * p.nwords);
     int32_t *band = c.take<int32_t>((size_t)p.ntgt * p.BQ * p.band_cap);
     double *band_score = p.certified ? c.take<double>((size_t)p.ntgt * p.BQ * p.band_cap) : nullptr;
+    int32_t *in_list = sel_handoff_supported(p) ? c.take<int32_t>((size_t)p.BQ * p.K0) : nullptr;
     if (c.used > ws_bytes) throw Error(CSA2_EWORKSPACE, "selection workspace too small");
+    if (handoff && !sel_handoff_supported(p)) throw Error(CSA2_EINTERNAL, "selection hand-off not supported");
     if (p.certified && (!rs || !rs->sumwq)) throw Error(CSA2_EINTERNAL, "certified selection needs query norms");
 
     if (small_path(p)) {
@@ -1515,6 +1536,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         a.nwords = p.nwords;
         a.band = band;
         a.band_cap = p.band_cap;
+        a.in_list = handoff ? in_list : nullptr;
         if (p.certified) hipLaunchKernelGGL(k_sel_one<true>, dim3(p.BQ), dim3(ONE_NT), 0, s, a);
         else hipLaunchKernelGGL(k_sel_one<false>, dim3(p.BQ), dim3(ONE_NT), 0, s, a);
         check_launch("selection (one block per query)");
@@ -1578,8 +1600,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     }
     int tg0 = 0;
     if (handoff) {
-        if (!sel_handoff_supported(p)) throw Error(CSA2_EINTERNAL, "selection hand-off not supported for this size");
-        *handoff = SelHandoff{sq, bitmap, p.nwords, band, band_score, p.band_cap, cand, p.n, out0, count0};
+        *handoff = SelHandoff{sq, in_list, p.K0, bitmap, p.nwords, band, band_score, p.band_cap, cand, p.n, out0, count0};
         if (p.ntgt == 1) return;
         tg0 = 1;  // the pool is finished here
     }
