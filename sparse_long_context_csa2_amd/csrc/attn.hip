@@ -284,7 +284,7 @@ __device__ void att_sel_band(const SelHandoff &sel, int bq, int32_t in_cnt, int3
     const double *bs = sel.band_score + (size_t)bq * sel.band_cap;
     const int32_t *cq = sel.cand ? sel.cand + (size_t)bq * n : nullptr;
     for (int w = tid; w < nw; w += NT) bmb[w] = 0u;
-    const int cap = scr_words / 4;
+    const int cap = (scr_words - nw) / 4;  // entries; nw words after them for a tie group's bitmap
     u32x4 *ent = reinterpret_cast<u32x4 *>(scr);  // (key lo, key hi, slot, 0)
     if (nb <= cap) {
         // the first NT entries arrived with the block's first loads
@@ -296,34 +296,79 @@ __device__ void att_sel_band(const SelHandoff &sel, int bq, int32_t in_cnt, int3
     }
     __syncthreads();
     if (nb <= cap) {
-        // entry i is ranked by P consecutive lanes, each counting the entries
-        // ahead of it among every P-th partner (eight partner reads in
-        // flight); (key, slot) is ahead iff key larger, or equal and slot smaller
-        const int P = nb * 16 <= NT ? 16 : nb * 8 <= NT ? 8 : nb * 4 <= NT ? 4 : nb * 2 <= NT ? 2 : 1;
-        const int per = NT / P;
-        for (int32_t i0 = 0; i0 < nb; i0 += per) {
-            const int32_t i = i0 + tid / P;
-            const int part = tid % P;
+        // (key, slot) is ahead of entry i iff its key is larger, or equal
+        // with a smaller slot.  First every entry counts the larger keys: a
+        // wave takes 64 entries (one a lane) and 32 partners, loads the
+        // partners' keys into 32 lanes and broadcasts each through scalar
+        // registers, so a partner costs a compare and an add with carry,
+        // unrolled, with no LDS latency.  The (entry chunk, partner chunk)
+        // pairs are spread over the waves; keys past the end read as 0,
+        // below every key of a finite score.  Entries with fewer than rr
+        // larger keys are chosen: exactly rr of them unless the group of
+        // equal keys at the cut straddles it.  That group is the chosen
+        // entries with the most larger keys, G; then its first rr - G
+        // members in slot order stay, found by a scan of its bitmap.
+        constexpr int W = NT / 64, S = 32;
+        __shared__ uint32_t n_chosen, g_cut;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+        const int C = (nb + 63) / 64, PC = (nb + S - 1) / S;
+        if (tid == 0) n_chosen = 0, g_cut = 0;
+        for (int task = wave; task < C * PC; task += W) {
+            const int32_t i = (task / PC) * 64 + lane;
+            const int32_t jl = (task % PC) * S + (lane & (S - 1));
             const bool act = i < nb;
             const u32x4 me = ent[act ? i : 0];
+            const u32x4 o = ent[jl < nb ? jl : 0];
+            const uint32_t plo = jl < nb ? o[0] : 0u, phi = jl < nb ? o[1] : 0u;
             const uint64_t ki = (uint64_t)me[0] | ((uint64_t)me[1] << 32);
-            const int32_t si = (int32_t)me[2];
-            int32_t rank = 0;
-            for (int32_t j0 = part; j0 < nb; j0 += 8 * P) {
-                u32x4 o[8];
+            uint32_t gt = 0;
 #pragma unroll
-                for (int u = 0; u < 8; u++) {
-                    const int32_t j = j0 + u * P;
-                    o[u] = ent[j < nb ? j : (act ? i : 0)];  // past the end: itself, which is not ahead
-                }
-#pragma unroll
-                for (int u = 0; u < 8; u++) {
-                    const uint64_t kj = (uint64_t)o[u][0] | ((uint64_t)o[u][1] << 32);
-                    rank += (int)((kj > ki) | ((kj == ki) & ((int32_t)o[u][2] < si)));
+            for (int t = 0; t < S; t++) {
+                const uint64_t kj = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)plo, t) |
+                                    ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)phi, t) << 32);
+                gt += kj > ki;
+            }
+            if (act) atomicAdd(reinterpret_cast<uint32_t *>(scr) + 4 * i + 3, gt);
+        }
+        __syncthreads();
+        for (int32_t i0 = 0; i0 < nb; i0 += NT) {  // count and G: one LDS atomic per wave
+            const int32_t i = i0 + tid;
+            const u32x4 me = ent[i < nb ? i : 0];
+            const bool ch = i < nb && me[3] < (uint32_t)rr;
+            if (ch) atomicOr(&bmb[me[2] >> 5], 1u << (me[2] & 31));
+            const uint32_t cnt = (uint32_t)__builtin_popcountll(__ballot(ch));
+            const uint32_t gm = wave_max_u32(ch ? me[3] : 0u);
+            if (lane == 0 && cnt) {
+                atomicAdd(&n_chosen, cnt);
+                atomicMax(&g_cut, gm);
+            }
+        }
+        __syncthreads();
+        if (n_chosen != (uint32_t)rr) {
+            uint32_t *gb = scr + 4 * cap;  // the straddling group's bitmap (nw words)
+            const uint32_t G = g_cut, need = (uint32_t)rr - G;
+            for (int w = tid; w < nw; w += NT) gb[w] = 0u;
+            __syncthreads();
+            for (int32_t i = tid; i < nb; i += NT) {
+                const u32x4 me = ent[i];
+                if (me[3] == G) {
+                    atomicOr(&gb[me[2] >> 5], 1u << (me[2] & 31));
+                    atomicAnd(&bmb[me[2] >> 5], ~(1u << (me[2] & 31)));
                 }
             }
-            for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
-            if (act && part == 0 && rank < rr) atomicOr(&bmb[si >> 5], 1u << (si & 31));
+            __syncthreads();
+            const int per = (nw + NT - 1) / NT, w0 = tid * per;
+            uint32_t c = 0;
+            for (int w = w0; w < w0 + per && w < nw; w++) c += (uint32_t)__builtin_popcount(gb[w]);
+            const uint32_t incl = wave_incl_scan_u32(c);
+            if (lane == 63) red[wave] = incl;
+            __syncthreads();
+            uint32_t pos = incl - c;
+#pragma unroll
+            for (int q = 0; q < W; q++) pos += q < wave ? red[q] : 0u;
+            for (int w = w0; w < w0 + per && w < nw; w++)
+                for (uint32_t bb = gb[w]; bb && pos < need; bb &= bb - 1, pos++)
+                    atomicOr(&bmb[w], 1u << __builtin_ctz(bb));
         }
     } else {
         // a band larger than the scratch: the rr-th best key by bisection
@@ -490,17 +535,22 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__re
     const int ne = min(k, e_begin + ROWS) - e_begin;
     const uint8_t *kvb = kv + (size_t)b * N * RB;
 
-    // the block's query heads first: they do not depend on the indices
+    // the block's query heads first: they do not depend on the indices.  Not
+    // so in the last split with a selection to finish, which usually ranks
+    // the band: its LDS work would wait behind these loads, so there they
+    // are issued after the ranking, still ahead of the rows.
     constexpr int QS = D + 8;
     constexpr int QPR = D / 8;                 // 16-byte pieces per head row
     constexpr int QP = HB * QPR;
     constexpr int QPT = (QP + NT - 1) / NT;
     u32x4 qst[QPT];
-    {
+    const bool q_early = !SEL || split != nsplit - 1;
+    auto load_q = [&]() {
         const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q + ((size_t)bq * H + hgb * HB) * D);
 #pragma unroll
         for (int i = 0; i < QPT; i++) qst[i] = qsrc[QP % NT == 0 ? tid + NT * i : min(tid + NT * i, QP - 1)];
-    }
+    };
+    if (q_early) load_q();
     // certified selection finished here (SEL): the query's IN count, band size
     // and chosen band count; the block that writes the index list keeps its
     // IN bitmap words (loaded with everything else, before any wait)
@@ -604,6 +654,7 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__re
                 if (tid * SPW + u < nw) inw[u] |= reinterpret_cast<const uint32_t *>(p_lds)[tid * SPW + u];
         }
     }
+    if (!q_early) load_q();
     issue(0);
     __builtin_amdgcn_sched_barrier(0);
 

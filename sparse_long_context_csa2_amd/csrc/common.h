@@ -125,6 +125,9 @@ struct OpMax {
 struct OpMin {
     __device__ float operator()(float a, float b) const { return fminf(a, b); }
 };
+struct OpMaxU {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
 
 // Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
 // 16-lane row, then the row totals are carried forward with the row
@@ -144,6 +147,7 @@ __device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpAdd
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
 __device__ __forceinline__ float wave_min(float v) { return wave_reduce(v, OpMin{}); }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_reduce(v, OpAdd{}); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_reduce(v, OpMaxU{}); }
 
 // Order-preserving key of a binary64 value (-0 is folded onto +0 so that it
 // ties with +0, as numeric comparison does).
