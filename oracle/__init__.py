@@ -46,8 +46,10 @@ def _lib():
         lib.ora_window_idx.argtypes = [c_void_p, c_int64, c_int, c_void_p]
         lib.ora_quantize_fp4.argtypes = [c_void_p, c_int, c_int64, c_int, c_void_p]
         lib.ora_merge_attn.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p]
+        lib.ora_round_bf16.argtypes, lib.ora_round_bf16.restype = [c_double], c_double
+        lib.ora_round_bf16_array.argtypes = [c_void_p, c_int64, c_void_p]
         for f in ("ora_decode_row", "ora_compress", "ora_index_score", "ora_topk", "ora_sparse_attn",
-                  "ora_window_idx", "ora_merge_attn", "ora_quantize_fp4"):
+                  "ora_window_idx", "ora_merge_attn", "ora_quantize_fp4", "ora_round_bf16_array"):
             getattr(lib, f).restype = None
         _LIB = lib
     return _LIB
@@ -206,13 +208,22 @@ def index_score(qI, w, kI, q_pos=None, m: int = 1, cand=None) -> np.ndarray:
     """
     qa, dt = _raw(qI)
     ka, kdt = _raw(kI)
+    if dt == FP4:
+        # FP4 indexer queries (same passage): FP4 rows of dI/2 + dI/16 bytes per
+        # head, decoded exactly (at most 6 significant bits, within binary32's
+        # range) like the keys, which must then be FP4 rows too
+        if kdt != FP4 or ka.shape[-1] != qa.shape[-1] or (qa.shape[-1] * 16) % 9:
+            raise TypeError("FP4 queries need FP4 keys of the same row width")
+        dI = qa.shape[-1] * 16 // 9
+        qa = decode_rows(qa, dI).astype(np.float32)
+        dt = F32
     if kdt == FP4:
         # FP4 indexer keys (same page, the passage on V4's FP4 indexer q/K): the
         # decoded values (at most 6 significant bits) are exact in fp32, and so
         # are the bf16 or fp32 queries; the formula is then the fp32 one
         dI = qa.shape[-1]
         ka = decode_rows(ka, dI).astype(np.float32)
-        if dt == BF16:
+        if qa.dtype == np.uint16:
             qa = (qa.astype(np.uint32) << 16).view(np.float32)
         dt = kdt = F32
     if kdt != dt:
@@ -233,13 +244,34 @@ def index_score(qI, w, kI, q_pos=None, m: int = 1, cand=None) -> np.ndarray:
 
 # --------------------------------------------------------------- selection
 
-def topk(scores, k: int, cand=None):
+def round_bf16(x) -> np.ndarray:
+    """binary64 values rounded once to bfloat16 (nearest, ties to even), as float64.
+
+    "读完这篇，你就搞懂 DeepSeek v4 了", the FP4 quantization-aware training
+    passage: the indexer's score is quantized only down to BF16 for the top-k
+    ranking (reading and method in the C file)."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty_like(a)
+    _lib().ora_round_bf16_array(_ptr(a), int(a.size), _ptr(out))
+    return out
+
+
+SCORE_KEYS = ("f64", "bf16")
+
+
+def topk(scores, k: int, cand=None, key: str = "f64"):
     """Top-k per query: (idx int32 [..., k] ascending and -1 padded, count int32 [...]).
 
     Order by (score descending, entry index ascending); the k most relevant
     entries are kept ("闪电索引机制（对应步骤二）"), lowest index winning ties.
+    key = "bf16": the ranked score is the binary64 score rounded to bfloat16
+    (round_bf16), so scores that round alike tie and the lower index wins.
     """
+    if key not in SCORE_KEYS:
+        raise ValueError(key)
     s = np.ascontiguousarray(np.asarray(scores, dtype=np.float64))
+    if key == "bf16":
+        s = round_bf16(s)
     lead = s.shape[:-1]
     n = s.shape[-1]
     BQ = int(np.prod(lead)) if lead else 1
@@ -326,7 +358,7 @@ def swa_attn(q, swa_kv, q_pos, W: int, scale: float):
 # ------------------------------------------------------------------- modes
 
 def layer(mode: str, *, k: int, scale: float, q, kv, qI=None, w=None, kI=None, q_pos=None, m: int = 1,
-          P: int = 0, pool=None, idx=None):
+          P: int = 0, pool=None, idx=None, score_key: str = "f64"):
     """One CSA2 layer in the given mode; returns a dict of outputs.
 
     Modes, per the V4.1 Flash transcript (prism.simon-ai.net) and "Recall之王
@@ -336,20 +368,22 @@ def layer(mode: str, *, k: int, scale: float, q, kv, qI=None, w=None, kI=None, q
       REINDEX -- reuse the shared KV and indexer keys, score only the pool
                  with this layer's own queries, keep top-k of the pool, attend.
       REUSE   -- reuse KV and the previous top-k indices; attention only.
+    score_key = "bf16" ranks (top-k and pool) by the scores rounded to bfloat16
+    (see topk).
     """
     res = {}
     if mode == "FULL":
         s = index_score(qI, w, kI, q_pos=q_pos, m=m)
         res["scores"] = s
-        res["idx"], res["count"] = topk(s, k)
+        res["idx"], res["count"] = topk(s, k, key=score_key)
         if P > 0:
-            res["pool"], res["pool_count"] = topk(s, P)
+            res["pool"], res["pool_count"] = topk(s, P, key=score_key)
     elif mode == "REINDEX":
         if pool is None:
             raise ValueError("REINDEX needs the pool")
         s = index_score(qI, w, kI, q_pos=q_pos, m=m, cand=pool)
         res["scores"] = s
-        res["idx"], res["count"] = topk(s, k, cand=pool)
+        res["idx"], res["count"] = topk(s, k, cand=pool, key=score_key)
     elif mode == "REUSE":
         if idx is None:
             raise ValueError("REUSE needs the previous indices")

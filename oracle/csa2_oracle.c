@@ -235,6 +235,46 @@ void ora_index_score(const void *qI, const float *w, const void *kI, int dt, int
     }
 }
 
+/* ------------------------------------------------------- bf16 score keys */
+
+/*
+ * "读完这篇，你就搞懂 DeepSeek v4 了", the passage on V4's FP4 quantization-aware
+ * training: the lightning indexer's score is quantized only down to BF16,
+ * because the top-k ranking is sensitive to it.  Reading taken: the value
+ * that top-k ranks is the binary64 score of the formula rounded once to
+ * bfloat16 (8 exponent bits like binary32, 8 significant bits), to nearest
+ * with ties to the even significand, directly from binary64 (never through
+ * binary32, which could round twice); magnitudes that round past the largest
+ * finite bfloat16 become infinite with their sign; zero, infinities and NaN
+ * are kept.  Equal rounded scores are then ordered by entry index, as any tie.
+ *
+ * Method: the spacing of bfloat16 values around |x| is 2^(e-7) for the
+ * binade [2^e, 2^(e+1)), and 2^-133 below 2^-126 (subnormals); |x| divided
+ * by that spacing (exact: a power of two) is rounded to the nearest integer,
+ * ties to even, by nearbyint in the default rounding mode, and scaled back.
+ */
+double ora_round_bf16(double x)
+{
+    if (x == 0.0 || isnan(x) || isinf(x))
+        return x;
+    int e2;
+    frexp(fabs(x), &e2); /* |x| in [2^(e2-1), 2^e2) */
+    int lead = e2 - 1;
+    if (lead < -126)
+        lead = -126;
+    double spacing = ldexp(1.0, lead - 7);
+    double r = nearbyint(fabs(x) / spacing) * spacing;
+    if (r >= ldexp(1.0, 128))
+        r = INFINITY;
+    return x < 0.0 ? -r : r;
+}
+
+void ora_round_bf16_array(const double *x, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = ora_round_bf16(x[i]);
+}
+
 /* ------------------------------------------------------------- selection */
 
 typedef struct {

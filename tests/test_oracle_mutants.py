@@ -15,7 +15,7 @@ import oracle
 from oracle import build as obuild
 
 PIN_MODULES = ["test_oracle_formats", "test_oracle_indexer", "test_oracle_topk", "test_oracle_attn",
-               "test_oracle_compress", "test_oracle_modes"]
+               "test_oracle_compress", "test_oracle_modes", "test_oracle_scorekeys"]
 
 MUTANTS = {
     "indexer drops the ReLU": ("double r = dot > 0.0 ? dot : 0.0;", "double r = dot;"),
@@ -38,6 +38,12 @@ MUTANTS = {
     "compression window is current+next group": ("int64_t first_row = halo ? i * m : (i - 1) * m;",
                                                  "int64_t first_row = halo ? i * m : i * m;"),
     "compression pools the logits": ("acc = acc + p * elem(x, dt, t * D + c);", "acc = acc + p * logit[r];"),
+    "bf16 key rounded through binary32": ("double r = nearbyint(fabs(x) / spacing) * spacing;",
+                                          "double r = nearbyint((double)(float)fabs(x) / spacing) * spacing;"),
+    "bf16 key ties away from zero": ("double r = nearbyint(fabs(x) / spacing) * spacing;",
+                                     "double r = round(fabs(x) / spacing) * spacing;"),
+    "bf16 key keeps 8 stored bits": ("double spacing = ldexp(1.0, lead - 7);", "double spacing = ldexp(1.0, lead - 8);"),
+    "bf16 key subnormal spacing halved": ("    if (lead < -126)\n        lead = -126;", "    if (lead < -127)\n        lead = -127;"),
 }
 
 
@@ -75,8 +81,9 @@ def test_pins_catch_mutant(name):
     with tempfile.TemporaryDirectory() as tmp:
         so = _build_mutant(mutated, tmp, "mutant")
         lib = ctypes.CDLL(so)
-        for attr in ("ora_e2m1", "ora_e4m3", "ora_decode_row", "ora_compress", "ora_index_score", "ora_topk",
-                     "ora_sparse_attn"):
+        for attr in ("ora_e2m1", "ora_e4m3", "ora_fp4_scale", "ora_decode_row", "ora_compress", "ora_index_score",
+                     "ora_topk", "ora_sparse_attn", "ora_window_idx", "ora_merge_attn", "ora_quantize_fp4",
+                     "ora_round_bf16", "ora_round_bf16_array"):
             f_new, f_old = getattr(lib, attr), getattr(saved, attr)
             f_new.argtypes, f_new.restype = f_old.argtypes, f_old.restype
         oracle._LIB = lib
