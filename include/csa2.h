@@ -66,8 +66,24 @@ typedef enum {
  *   zero, subnormals and sign-set bytes are their E4M3 values; the E4M3 NaN
  *   code S.1111.111 (never written by csa2_quantize_fp4) saturates to +-448.
  *   Main KV, and indexer keys (csa2_index_score).
- *   CSA2_FP4E2M1_S16E4M3 is the same format under its descriptive name. */
-typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_FP4 = 2, CSA2_FP4E2M1_S16E4M3 = 2 } csa2_dtype;
+ *   CSA2_FP4E2M1_S16E4M3 is the same format under its descriptive name.
+ * CSA2_FP4QK (indexer only): FP4 indexer queries and keys -- qI holds one FP4
+ *   row of dI channels per head and kI one per entry, both in the CSA2_FP4
+ *   layout.  "读完这篇，你就搞懂 DeepSeek v4 了", the passage on V4's FP4
+ *   quantization-aware training: the lightning indexer's q and K are FP4. */
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_FP4 = 2, CSA2_FP4E2M1_S16E4M3 = 2, CSA2_FP4QK = 3 } csa2_dtype;
+
+/* The value the layer's top-k ranks (csa2_layer_args.score_fmt).
+ *   CSA2_SCORE_F64  -- the binary64 score of the indexer formula (default).
+ *   CSA2_SCORE_BF16 -- that score rounded once to bfloat16 (nearest, ties to
+ *                      the even significand, straight from binary64; past the
+ *                      largest finite value it becomes infinite).  Same
+ *                      passage: the indexer's score is quantized only down to
+ *                      BF16, since top-k ranks it.  Equal rounded scores are
+ *                      ordered by entry index like any tie, so the choice
+ *                      differs from CSA2_SCORE_F64's where scores that round
+ *                      alike straddle the cut. */
+typedef enum { CSA2_SCORE_F64 = 0, CSA2_SCORE_BF16 = 1 } csa2_score_fmt;
 
 /* Layer modes (V4.1 Flash video transcript on prism.simon-ai.net, the passage
  * introducing CSA2's three modes; "Recall之王 祭出Reuse", same section):
@@ -137,10 +153,13 @@ CSA2_API int csa2_quantize_fp4(const void *x, int dt, int64_t n, int32_t D, void
  *
  * qI [B,Q,HI,dI] and kI [B,N,dI] in dt (CSA2_F32 or CSA2_BF16); w [B,Q,HI] fp32.
  * dt = CSA2_FP4: FP4 indexer keys -- kI holds FP4 rows of dI/2 + dI/16 bytes
- *   (layout as CSA2_FP4, e.g. written by csa2_quantize_fp4) and qI is bf16
- *   (an FP4 query is passed decoded, exactly, in bf16).  Needs dI % 64 == 0
- *   and a matrix-core shape.  Same page, the passage on V4's FP4 indexer q/K
- *   (the scores stay at higher precision; here fp32 with the bound below).
+ *   (layout as CSA2_FP4, e.g. written by csa2_quantize_fp4) and qI is bf16.
+ * dt = CSA2_FP4QK: FP4 queries too -- qI holds [B,Q,HI] FP4 rows of the same
+ *   width, decoded exactly (into bf16, in the workspace) before scoring.
+ *   Both FP4 forms need dI % 64 == 0 and a matrix-core shape.  Same page,
+ *   the passage on V4's FP4 indexer q/K (the score is held at higher
+ *   precision: here fp32 with the bound below; csa2_layer can rank it
+ *   rounded to bf16, see csa2_score_fmt).
  * q_pos [B,Q] absolute token positions, or NULL: with q_pos, entry j is visible
  *   to the query only if (j+1)*m <= q_pos+1 (complete groups); without it all
  *   N entries are visible.
@@ -216,7 +235,10 @@ CSA2_API int csa2_sparse_attn(const void *q, const void *kv, int q_dt, int kv_dt
  * The selection (idx, pool, count) equals the top-k of the binary64 scores of
  * the formula in csa2_index_score, taken in sequential order, exactly: entries
  * whose fp32 score is within the error bound of the k-th are rescored in
- * binary64 on the GPU before the cut.
+ * binary64 on the GPU before the cut.  With score_fmt = CSA2_SCORE_BF16 the
+ * ranked value is that binary64 score rounded to bfloat16 (the bound then
+ * also covers the rounding, and rescored entries are rounded before the cut),
+ * again exactly.
  * ------------------------------------------------------------------------- */
 typedef struct {
     int32_t mode;         /* csa2_mode */
@@ -224,8 +246,9 @@ typedef struct {
     int64_t N;            /* compressed entries per sequence */
     int32_t m;            /* group size (for q_pos visibility) */
     int32_t HI, dI;       /* indexer heads and dim */
-    int32_t idx_dt;       /* dtype of qI and kI (CSA2_F32 or CSA2_BF16), or CSA2_FP4: FP4 kI, bf16 qI
-                             (as csa2_index_score; dI % 64 == 0, dI <= 256) */
+    int32_t idx_dt;       /* dtype of qI and kI (CSA2_F32 or CSA2_BF16), or CSA2_FP4: FP4 kI, bf16 qI,
+                             or CSA2_FP4QK: FP4 qI and kI (as csa2_index_score; dI % 64 == 0,
+                             dI <= 256) */
     int32_t k;            /* top-k (>= 1) */
     int32_t P;            /* FULL: pool size (0 = no pool); REINDEX: pool slots */
     int32_t H, D;         /* attention heads and dim (kv row width D) */
@@ -243,6 +266,7 @@ typedef struct {
     const void *kv;       /* [B,N,row] (shared across layers of a group) */
     void *out;            /* [B,Q,H,D] in q_dt */
     float *lse;           /* [B,Q,H] or NULL */
+    int32_t score_fmt;    /* csa2_score_fmt: the value top-k ranks (FULL, REINDEX); 0 = binary64 */
 } csa2_layer_args;
 
 CSA2_API size_t csa2_layer_workspace_size(const csa2_layer_args *a);

@@ -16,7 +16,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
-F32, BF16, FP4 = 0, 1, 2
+F32, BF16, FP4, FP4QK = 0, 1, 2, 3
+SCORE_FMTS = {"f64": 0, "bf16": 1}
 FULL, REINDEX, REUSE = 0, 1, 2
 MODES = {"FULL": FULL, "REINDEX": REINDEX, "REUSE": REUSE}
 STATUS = {0: "CSA2_OK", 1: "CSA2_EINVAL", 2: "CSA2_EUNSUPPORTED", 3: "CSA2_EWORKSPACE", 4: "CSA2_EHIP",
@@ -37,7 +38,7 @@ class LayerArgs(ctypes.Structure):
         ("idx_dt", _i32), ("k", _i32), ("P", _i32), ("H", _i32), ("D", _i32), ("q_dt", _i32), ("kv_dt", _i32),
         ("scale", _f32),
         ("q_pos", _vp), ("qI", _vp), ("w", _vp), ("kI", _vp), ("pool", _vp), ("idx", _vp), ("count", _vp),
-        ("scores", _vp), ("q", _vp), ("kv", _vp), ("out", _vp), ("lse", _vp),
+        ("scores", _vp), ("q", _vp), ("kv", _vp), ("out", _vp), ("lse", _vp), ("score_fmt", _i32),
     ]
 
 
@@ -150,13 +151,24 @@ def compress(x, n_out, m, halo, wz, bias, out=None, ws=None):
     return out
 
 
+def _index_shape(qI, kI):
+    """(B, Q, HI, dI, dtype code) of indexer inputs: FP4 keys (uint8 rows) with
+    bf16 queries, FP4 queries and keys (both uint8 rows), or plain tensors."""
+    if qI.dtype == torch.uint8:
+        if kI.dtype != torch.uint8 or qI.shape[-1] != kI.shape[-1] or (qI.shape[-1] * 16) % 9:
+            raise TypeError("FP4 queries need FP4 keys of the same row width")
+        B, Q, HI, rb = qI.shape
+        return B, Q, HI, rb * 16 // 9, FP4QK
+    B, Q, HI, dI = qI.shape
+    return B, Q, HI, dI, (FP4 if kI.dtype == torch.uint8 else _dt(qI))
+
+
 def index_score(qI, w, kI, q_pos=None, m=1, cand=None, want_err=True, scores=None, ws=None):
     _dev(qI, w, kI, q_pos, cand)
-    B, Q, HI, dI = qI.shape
+    B, Q, HI, dI, dt = _index_shape(qI, kI)
     N = kI.shape[1]
     P = cand.shape[-1] if cand is not None else 0
     n = P if cand is not None else N
-    dt = FP4 if kI.dtype == torch.uint8 else _dt(qI)  # FP4 indexer keys with bf16 queries
     if scores is None:
         scores = torch.empty(B, Q, n, dtype=torch.float32, device=qI.device)
     err = torch.empty(B, Q, dtype=torch.float32, device=qI.device) if want_err else None
@@ -243,7 +255,7 @@ class Layer:
     ``run()`` only launches (graph-capturable, no allocation)."""
 
     def __init__(self, mode, *, q, kv, k=None, scale, qI=None, w=None, kI=None, q_pos=None, m=1, P=0, pool=None,
-                 idx=None, keep_scores=False, want_lse=True, count=True, out=None, noalloc=False):
+                 idx=None, keep_scores=False, want_lse=True, count=True, out=None, noalloc=False, score_fmt="f64"):
         mode_i = MODES[mode] if isinstance(mode, str) else mode
         _dev(q, kv, qI, w, kI, q_pos, pool, idx, out)
         B, Q, H, D = q.shape
@@ -270,8 +282,8 @@ class Layer:
         a.H, a.D, a.q_dt, a.kv_dt, a.scale, a.k = H, D, _dt(q), _dt(kv), float(scale), k
         self.tensors = {"q": q, "kv": kv}
         if mode_i != REUSE:
-            a.HI, a.dI = qI.shape[2], qI.shape[3]
-            a.idx_dt = FP4 if kI.dtype == torch.uint8 else _dt(qI)
+            _, _, a.HI, a.dI, a.idx_dt = _index_shape(qI, kI)
+            a.score_fmt = SCORE_FMTS[score_fmt]
             self.tensors.update(qI=qI, w=w, kI=kI, q_pos=q_pos)
             if mode_i == FULL:
                 a.P = P

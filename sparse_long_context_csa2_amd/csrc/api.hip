@@ -58,7 +58,22 @@ void check_queries(int32_t B, int32_t Q) {
 }
 
 // ------------------------------------------------------------- indexer
-void check_index_args(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t N, int32_t P) {
+// FP4 queries are decoded into bf16 in the workspace first; the kernels then
+// see FP4 keys with bf16 queries.
+int kernel_idx_dt(int dt) { return dt == CSA2_FP4QK ? CSA2_FP4 : dt; }
+size_t qdec_bytes(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI) {
+    return dt == CSA2_FP4QK ? (size_t)B * Q * HI * dI * 2 : 0;
+}
+const void *decode_queries(const void *qI, int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, csa2::Carve &c,
+                           hipStream_t s) {
+    if (dt != CSA2_FP4QK) return qI;
+    uint16_t *qd = c.take<uint16_t>((size_t)B * Q * HI * dI);
+    csa2::launch_fp4_rows_to_bf16(qI, (int64_t)B * Q * HI, dI, qd, s);
+    return qd;
+}
+
+void check_index_args(int dt0, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t N, int32_t P) {
+    const int dt = kernel_idx_dt(dt0);
     if (dt != CSA2_FP4) need_plain_dt(dt, "indexer dtype");
     if (dt == CSA2_FP4 && !csa2::index_mfma_supported(dt, HI, dI))
         throw Error(CSA2_EUNSUPPORTED, "FP4 indexer keys need a matrix-core shape with dI % 64 == 0");
@@ -70,9 +85,10 @@ void check_index_args(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int6
     if (dt == CSA2_BF16 && dI % 8) throw Error(CSA2_EINVAL, "bf16 indexer rows need dI % 8 == 0");
 }
 
-size_t index_ws(int32_t B, int32_t Q, int64_t n) {
+size_t index_ws(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t n) {
     csa2::Carve c(nullptr, 0);
     c.take<csa2::TileStat>((size_t)B * Q * ((n + csa2::TILE - 1) / csa2::TILE));
+    if (dt == CSA2_FP4QK) c.take<uint16_t>(qdec_bytes(dt, B, Q, HI, dI) / 2);
     return c.used;
 }
 
@@ -95,11 +111,13 @@ LayerSizes layer_sizes(const csa2_layer_args *a) {
     }
     z.n = a->mode == CSA2_FULL ? a->N : a->P;
     z.sel = csa2::sel_plan(BQ, z.n, a->k, a->mode == CSA2_FULL ? a->P : 0, true);
+    z.sel.bf16key = a->score_fmt == CSA2_SCORE_BF16;
     csa2::Carve c(nullptr, 0);
     z.scores = a->scores ? 0 : (c.take<float>((size_t)BQ * z.n), (size_t)BQ * z.n * 4);
     size_t before = c.used;
     c.take<csa2::TileStat>((size_t)BQ * z.sel.ntiles);
     c.take<double>((size_t)BQ);  // sum_h |w_h| ||q_h||
+    if (a->idx_dt == CSA2_FP4QK) c.take<uint16_t>(qdec_bytes(a->idx_dt, a->B, a->Q, a->HI, a->dI) / 2);
     z.stats = c.used - before;
     z.selws = csa2::sel_workspace(z.sel, false);
     z.total = c.used + z.selws + z.attws;
@@ -128,13 +146,16 @@ void check_layer(const csa2_layer_args *a) {
     if (!csa2::attn_supported(csa2::attn_plan(a->q_dt, a->kv_dt, a->B, a->Q, a->H, a->D, a->N, a->k)))
         throw Error(CSA2_EUNSUPPORTED, "no attention kernel for this shape (vector path needs D + k <= 16384)");
     if (a->mode == CSA2_REUSE) return;
+    if (a->score_fmt != CSA2_SCORE_F64 && a->score_fmt != CSA2_SCORE_BF16) throw Error(CSA2_EINVAL, "unknown score_fmt");
     need_ptr(a->qI, "qI");
+    if (a->idx_dt == CSA2_FP4QK && (reinterpret_cast<uintptr_t>(a->qI) & 3))
+        throw Error(CSA2_EINVAL, "FP4 query rows must be 4-byte aligned");
     need_ptr(a->w, "w");
     need_ptr(a->kI, "kI");
     opt_ptr(a->scores, "scores");
     opt_ptr(a->q_pos, "q_pos");
     if (a->q_pos && a->m < 1) throw Error(CSA2_EINVAL, "m must be >= 1 with q_pos");
-    if (!csa2::rescore_supported(a->idx_dt, a->dI))
+    if (!csa2::rescore_supported(kernel_idx_dt(a->idx_dt), a->dI))
         throw Error(CSA2_EUNSUPPORTED, "certified selection needs indexer rows of whole 16-byte vectors "
                                        "(dI % 4 == 0 for fp32, dI % 8 == 0 for bf16, dI % 64 == 0 and "
                                        "dI <= 256 for FP4 keys)");
@@ -158,12 +179,14 @@ void run_layer(const csa2_layer_args *a, const LayerSizes &z, void *ws, size_t w
         float *scores = a->scores ? a->scores : c.take<float>((size_t)BQ * z.n);
         auto *stats = c.take<csa2::TileStat>((size_t)BQ * z.sel.ntiles);
         auto *sumwq = c.take<double>((size_t)BQ);
+        const void *qI = decode_queries(a->qI, a->idx_dt, a->B, a->Q, a->HI, a->dI, c, s);
+        const int dt = kernel_idx_dt(a->idx_dt);
         void *selws = c.base + c.used;
         c.used += z.selws;
         const int32_t *cand = a->mode == CSA2_REINDEX ? a->pool : nullptr;
-        csa2::launch_index_score(a->qI, a->idx_dt, a->w, a->kI, a->B, a->Q, a->HI, a->dI, a->N, a->q_pos, a->m,
+        csa2::launch_index_score(qI, dt, a->w, a->kI, a->B, a->Q, a->HI, a->dI, a->N, a->q_pos, a->m,
                                  cand, cand ? a->P : 0, scores, stats, sumwq, s);
-        const csa2::RescoreArgs rs{a->qI, a->idx_dt, a->w, a->kI, a->Q, a->HI, a->dI, a->N, sumwq};
+        const csa2::RescoreArgs rs{qI, dt, a->w, a->kI, a->Q, a->HI, a->dI, a->N, sumwq};
         // the top-k's final pick and compaction run in the attention kernel when both sides allow
         const bool fuse = csa2::sel_handoff_supported(z.sel) && csa2::attn_handoff_supported(z.att, z.sel);
         csa2::SelHandoff h{};
@@ -236,11 +259,8 @@ int csa2_compress(const void *x, int dt, int64_t n_out, int32_t D, int32_t m, in
 }
 
 size_t csa2_index_score_workspace_size(int dt, int32_t B, int32_t Q, int32_t HI, int32_t dI, int64_t N, int32_t P) {
-    (void)dt;
-    (void)HI;
-    (void)dI;
-    if (B < 1 || Q < 1) return 0;
-    return index_ws(B, Q, P > 0 ? P : N);
+    if (B < 1 || Q < 1 || HI < 1 || dI < 1) return 0;
+    return index_ws(dt, B, Q, HI, dI, P > 0 ? P : N);
 }
 
 int csa2_index_score(const void *qI, const float *w, const void *kI, int dt, int32_t B, int32_t Q, int32_t HI,
@@ -257,15 +277,19 @@ int csa2_index_score(const void *qI, const float *w, const void *kI, int dt, int
         opt_ptr(cand, "cand");
         if (cand && P < 1) throw Error(CSA2_EINVAL, "cand needs P >= 1");
         if (q_pos && m < 1) throw Error(CSA2_EINVAL, "m must be >= 1 with q_pos");
+        if (dt == CSA2_FP4QK && (reinterpret_cast<uintptr_t>(qI) & 3))
+            throw Error(CSA2_EINVAL, "FP4 query rows must be 4-byte aligned");
         const int64_t n = cand ? P : N;
-        need_ws(ws, ws_bytes, index_ws(B, Q, n));
+        need_ws(ws, ws_bytes, index_ws(dt, B, Q, HI, dI, n));
         hipStream_t s = (hipStream_t)stream;
         csa2::Carve c(ws, ws_bytes);
         const int ntiles = (int)((n + csa2::TILE - 1) / csa2::TILE);
         auto *stats = c.take<csa2::TileStat>((size_t)B * Q * ntiles);
-        csa2::launch_index_score(qI, dt, w, kI, B, Q, HI, dI, N, q_pos, m, cand, cand ? P : 0, scores, stats, nullptr,
+        const void *qk = decode_queries(qI, dt, B, Q, HI, dI, c, s);
+        const int kdt = kernel_idx_dt(dt);
+        csa2::launch_index_score(qk, kdt, w, kI, B, Q, HI, dI, N, q_pos, m, cand, cand ? P : 0, scores, stats, nullptr,
                                  s);
-        if (err) csa2::launch_err_bound(qI, dt, w, B * Q, HI, dI, stats, ntiles, err, nullptr, s);
+        if (err) csa2::launch_err_bound(qk, kdt, w, B * Q, HI, dI, stats, ntiles, err, nullptr, s);
     });
 }
 

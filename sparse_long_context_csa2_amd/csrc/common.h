@@ -191,6 +191,40 @@ __host__ __device__ inline double score_bound(double kmax, double sumwq, int HI,
     return ldexp(1.0, -22) * double(dI + HI + 2) * kmax * sumwq * (1.0 + ldexp(1.0, -20)) + ldexp(1.0, -100);
 }
 
+// Scores ranked rounded to bfloat16 ("读完这篇，你就搞懂 DeepSeek v4 了", the
+// passage on FP4 quantization-aware training: the indexer's score is
+// quantized only down to BF16).  The rounded key r of an exact score x obeys
+// |r - x| <= 2^-8 |x| + 2^-134 (half a spacing: 2^(e-8) in the binade
+// [2^e, 2^(e+1)), 2^-134 among the subnormals) until x rounds past the
+// largest finite value.  With |fp32 score - x| <= E and |fp32 score| <= M,
+// the selection's bound for the keys is E plus this slack (slightly
+// enlarged for the binary64 arithmetic); infinite when a key could overflow.
+__host__ __device__ inline double bf16_key_bound(double E, double M) {
+    const double x = M + E;
+    if (!(x < 0x1.fe0p127)) return __builtin_inf();
+    return E + (ldexp(1.0, -8) * x + ldexp(1.0, -134)) * (1.0 + ldexp(1.0, -40));
+}
+
+// A binary64 value rounded once to bfloat16, nearest with ties to even, as a
+// binary64: in the normal range by rounding the 52-bit fraction to its top 7
+// bits on the bit pattern (a carry may step the exponent; past 2^128 the
+// result is infinite), below 2^-126 on a fixed spacing of 2^-133.  Zero,
+// infinities and NaN pass through.
+__device__ inline double bf16_round_key(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint64_t mag = u & 0x7fffffffffffffffull, sign = u & 0x8000000000000000ull;
+    const int ex = (int)(mag >> 52) - 1023;
+    if (mag == 0 || ex == 1024) return x;
+    if (ex >= -126) {
+        const uint64_t keep = (mag >> 45) & 1u;
+        uint64_t r = (mag + 0x00000fffffffffffull + keep) & ~0x00001fffffffffffull;
+        if ((int)(r >> 52) - 1023 >= 128) r = 0x7ff0000000000000ull;
+        return __longlong_as_double((long long)(r | sign));
+    }
+    const double r = rint(__longlong_as_double((long long)mag) * 0x1p133) * 0x1p-133;
+    return __longlong_as_double((long long)((uint64_t)__double_as_longlong(r) | sign));
+}
+
 // sum_h |w_h| ||q_h|| in binary64 with a fixed reduction order: groups of 16
 // threads take heads g, g + NT/16, ...; the 16 threads of a group split the
 // head's row into 16 runs (one 16-byte load each when the row allows), square

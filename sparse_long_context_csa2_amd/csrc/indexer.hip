@@ -588,6 +588,23 @@ void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, i
                        static_cast<const uint16_t *>(kI), Q, N, q_pos, m, cand, P, scores, stats, ntiles, sumwq);
 }
 
+// FP4 indexer queries ("读完这篇，你就搞懂 DeepSeek v4 了", the passage on V4's
+// FP4 quantization-aware training: the indexer's q is FP4 as well as its K):
+// each query row is decoded once, exactly, into bf16 (piece t = 8 channels:
+// 4 code bytes and their scale byte to 16 bytes), so that the scoring and
+// the certified selection run on the bf16-query, FP4-key path unchanged.
+__global__ __launch_bounds__(256) void k_fp4_rows_to_bf16(const uint8_t *__restrict__ rows, int64_t npieces, int D,
+                                                          uint16_t *__restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= npieces) return;
+    const int ppr = D / 8;
+    const int64_t r = t / ppr;
+    const int c = (int)(t - r * ppr);
+    const uint8_t *row = rows + r * (D / 2 + D / 16);
+    const uint32_t word = *reinterpret_cast<const uint32_t *>(row + 4 * c);
+    *reinterpret_cast<u32x4 *>(out + r * D + 8 * c) = fp4_keys_to_bf16x8<64>(word, row[D / 2 + c / 2]);
+}
+
 }  // namespace
 
 bool index_mfma_supported(int dt, int HI, int dI) {
@@ -629,6 +646,13 @@ void launch_index_score(const void *qI, int dt, const float *w, const void *kI, 
                            scores, stats, ntiles, sumwq);
     }
     check_launch("index score");
+}
+
+void launch_fp4_rows_to_bf16(const void *rows, int64_t nrows, int D, uint16_t *out, hipStream_t s) {
+    const int64_t np = nrows * (D / 8);
+    hipLaunchKernelGGL(k_fp4_rows_to_bf16, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint8_t *>(rows), np, D, out);
+    check_launch("FP4 query decode");
 }
 
 void launch_err_bound(const void *qI, int dt, const float *w, int BQ, int HI, int dI, const TileStat *stats,

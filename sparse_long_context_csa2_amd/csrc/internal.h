@@ -11,6 +11,8 @@ bool index_valu_supported(int HI, int dI);
 void launch_index_score(const void *qI, int dt, const float *w, const void *kI, int B, int Q, int HI, int dI,
                         int64_t N, const int64_t *q_pos, int m, const int32_t *cand, int P, float *scores,
                         TileStat *stats, double *sumwq, hipStream_t s);
+// FP4 rows (D channels, D % 64 == 0, 4-byte aligned) decoded exactly to bf16 [nrows][D].
+void launch_fp4_rows_to_bf16(const void *rows, int64_t nrows, int D, uint16_t *out, hipStream_t s);
 void launch_err_bound(const void *qI, int dt, const float *w, int BQ, int HI, int dI, const TileStat *stats,
                       int ntiles, float *err32, double *err64, hipStream_t s);
 
@@ -55,6 +57,7 @@ struct SelPlan {
     int ntgt, ntiles, nchunks;
     int64_t nwords, band_cap;
     bool certified;
+    bool bf16key = false;  // certified: rank the binary64 scores rounded to bfloat16
 };
 struct RescoreArgs {
     const void *qI;

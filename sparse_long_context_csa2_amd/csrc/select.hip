@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void k_sel_stats(const float *__restrict__ sco
 __global__ __launch_bounds__(256) void k_sel_range(const TileStat *__restrict__ stats, int ntiles,
                                                    SelQuery *__restrict__ sq, uint32_t *__restrict__ qhist,
                                                    const double *__restrict__ sumwq, int HI, int dI,
-                                                   double *__restrict__ err64) {
+                                                   double *__restrict__ err64, int bf16key) {
     __shared__ float r_min[4], r_max[4], r_k[4];
     __shared__ uint32_t r_n[4];
     const int bq = blockIdx.x, wave = threadIdx.x >> 6;
@@ -174,8 +174,10 @@ __global__ __launch_bounds__(256) void k_sel_range(const TileStat *__restrict__ 
         if (err64) {
             // the score error bound from the largest key norm and the query's sum of w |q|
             const float k2 = fmaxf(fmaxf(r_k[0], r_k[1]), fmaxf(r_k[2], r_k[3]));
-            err64[bq] = score_bound(sqrt((double)k2 * (1.0 + ldexp(1.0, -10))),
-                                    sumwq[bq] * (1.0 + ldexp(1.0, -30)), HI, dI);
+            double E = score_bound(sqrt((double)k2 * (1.0 + ldexp(1.0, -10))), sumwq[bq] * (1.0 + ldexp(1.0, -30)),
+                                   HI, dI);
+            if (bf16key && nv > 0) E = bf16_key_bound(E, fmax(fabs((double)lo), fabs((double)hi)));
+            err64[bq] = E;
         }
     }
 }
@@ -753,6 +755,7 @@ struct OneArgs {
     int32_t *band;
     int64_t band_cap;
     int32_t *in_list;  // certified, nullable: target 0's IN entries in ascending order, [BQ][K0]
+    int bf16key;       // certified: the ranked value is the score rounded to bfloat16
 };
 
 // Smallest key in [lk, hk] whose bin is >= target (hk + 1 if none): a 64-way
@@ -914,9 +917,11 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
                 if (wave == 0) kk = edge_key(lk, hk, bstar, lo, inv);
                 else if (bstar + 1 < NB) kk = edge_key(lk, hk, bstar + 1, lo, inv) - 1;
                 double E = 0.0;
-                if constexpr (CERT)
+                if constexpr (CERT) {
                     E = score_bound(sqrt((double)km * (1.0 + ldexp(1.0, -10))), sumwq * (1.0 + ldexp(1.0, -30)),
                                     a.HI, a.dI);
+                    if (a.bf16key) E = bf16_key_bound(E, fmax(fabs((double)lo), fabs((double)hi)));
+                }
                 if (lane == 0) thr_sh[wave] = wave == 0 ? thr_lo(fkey_inv(kk), E) : thr_hi(fkey_inv(kk), E);
             }
             __syncthreads();
@@ -1023,6 +1028,7 @@ struct RescoreKArgs {
     const int32_t *band;
     double *band_score;
     int64_t band_cap;
+    int bf16key;  // store the scores rounded to bfloat16 (the ranked value)
 };
 
 // Running binary64 dot over one 16-byte vector of each row.
@@ -1205,6 +1211,7 @@ __global__ __launch_bounds__(RS_NT, 2) void k_sel_rescore(RescoreKArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
         const int32_t e = e0 + ew + lane;
+        if (a.bf16key) sc = bf16_round_key(sc);
         if (lane < RS_EPW && e < total) {
             if (e < nb0) a.band_score[row0 + e] = sc;
             else a.band_score[row1 + (e - nb0)] = sc;
@@ -1284,6 +1291,7 @@ __global__ __launch_bounds__(RS_NT) void k_sel_rescore_wide(RescoreKArgs a) {
                     for (int i = 0; i < 16; i++)
                         if (c0 + i < hn) sc = sc + tv[i];
                 }
+                if (a.bf16key && h0 + 64 >= a.HI) sc = bf16_round_key(sc);  // the last head pass
                 a.band_score[(tg == 0 ? row0 : row1) + pos] = sc;
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1537,6 +1545,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         a.band = band;
         a.band_cap = p.band_cap;
         a.in_list = handoff ? in_list : nullptr;
+        a.bf16key = p.certified && p.bf16key ? 1 : 0;
         if (p.certified) hipLaunchKernelGGL(k_sel_one<true>, dim3(p.BQ), dim3(ONE_NT), 0, s, a);
         else hipLaunchKernelGGL(k_sel_one<false>, dim3(p.BQ), dim3(ONE_NT), 0, s, a);
         check_launch("selection (one block per query)");
@@ -1549,7 +1558,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         }
         hipLaunchKernelGGL(k_sel_range, dim3(p.BQ), dim3(256), 0, s, stats, p.ntiles, sq, qhist,
                            p.certified ? rs->sumwq : nullptr, p.certified ? rs->HI : 0, p.certified ? rs->dI : 0,
-                           p.certified ? ebuf : nullptr);
+                           p.certified ? ebuf : nullptr, p.certified && p.bf16key ? 1 : 0);
         check_launch("selection range");
         hipLaunchKernelGGL(k_sel_hist, dim3((p.nchunks + HIST_CPB - 1) / HIST_CPB, p.BQ), dim3(256), 0, s, scores,
                            cand, p.n, sq, qhist);
@@ -1579,6 +1588,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         r.band = band;
         r.band_score = band_score;
         r.band_cap = p.band_cap;
+        r.bf16key = p.bf16key ? 1 : 0;
         const int rowb = rs->dI * (rs->dt == CSA2_F32 ? 4 : 2);
         if (rowb <= RS_ROWB) {
             // about 256 entries per query per round at 32,768 slots, more for longer

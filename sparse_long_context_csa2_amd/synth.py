@@ -100,13 +100,14 @@ class Decode:
     H: int
     D: int
     k: int
-    idx_dtype: str = "bf16"  # "bf16", "f32", or "fp4" (FP4 indexer keys, bf16 queries)
+    idx_dtype: str = "bf16"  # "bf16", "f32", "fp4" (FP4 indexer keys, bf16 queries) or "fp4qk" (both FP4)
     kv_fmt: str = "bf16"     # "bf16", "f32" or "fp4"
     m: int = 4
     P: int = 0
     seed: int = 0
     layers: list = field(default_factory=lambda: ["FULL"])
     k_reindex: int = 0  # top-k of the Reindex layers (0: the same k as the Full layer)
+    score_fmt: str = "f64"  # the ranked score: "f64" (binary64) or "bf16" (rounded to bfloat16)
 
     def layer_k(self, mode: str) -> int:
         return self.k_reindex if mode == "REINDEX" and self.k_reindex > 0 else self.k
@@ -122,7 +123,7 @@ def make_decode(spec: Decode) -> dict:
     rng = np.random.default_rng(spec.seed)
     idx_draw = normal_f32 if spec.idx_dtype == "f32" else normal_bf16
     out = {"spec": spec}
-    if spec.idx_dtype == "fp4":
+    if spec.idx_dtype in ("fp4", "fp4qk"):
         out["kI"] = fp4_rows(rng, (spec.B, spec.N), spec.dI)
     else:
         out["kI"] = idx_draw(rng, (spec.B, spec.N, spec.dI))
@@ -137,7 +138,10 @@ def make_decode(spec: Decode) -> dict:
     for mode in spec.layers:
         lay = {"mode": mode}
         if mode in ("FULL", "REINDEX"):
-            lay["qI"] = idx_draw(rng, (spec.B, spec.Q, spec.HI, spec.dI))
+            if spec.idx_dtype == "fp4qk":
+                lay["qI"] = fp4_rows(rng, (spec.B, spec.Q, spec.HI), spec.dI)
+            else:
+                lay["qI"] = idx_draw(rng, (spec.B, spec.Q, spec.HI, spec.dI))
             lay["w"] = uniform_f32(rng, (spec.B, spec.Q, spec.HI))
         lay["q"] = q_draw(rng, (spec.B, spec.Q, spec.H, spec.D))
         out["layers"].append(lay)

@@ -55,8 +55,9 @@ def run_group(b, d, q_pos=None):
         kw = dict(q=dev(lay["q"]), kv=kv, k=k, scale=spec.scale)
         rkw = dict(q=lay["q"], kv=d["kv"], k=k, scale=spec.scale)
         if mode in ("FULL", "REINDEX"):
-            kw.update(qI=dev(lay["qI"]), w=dev(lay["w"]), kI=kI, q_pos=dev(q_pos), m=spec.m)
-            rkw.update(qI=lay["qI"], w=lay["w"], kI=d["kI"], q_pos=q_pos, m=spec.m)
+            kw.update(qI=dev(lay["qI"]), w=dev(lay["w"]), kI=kI, q_pos=dev(q_pos), m=spec.m,
+                      score_fmt=spec.score_fmt)
+            rkw.update(qI=lay["qI"], w=lay["w"], kI=d["kI"], q_pos=q_pos, m=spec.m, score_key=spec.score_fmt)
         if mode == "FULL":
             kw["P"] = rkw["P"] = spec.P
         elif mode == "REINDEX":

@@ -58,7 +58,13 @@ def test_topk_rejects_bad_arguments_without_launching():
 def test_index_score_rejects_and_reports_unsupported():
     ws = 1 << 30
     # unknown dtype
-    assert b._index(A, A, A, 3, 1, 1, 4, 64, 100, None, 1, None, 0, A2, None, A, ws, None) == 1
+    assert b._index(A, A, A, 4, 1, 1, 4, 64, 100, None, 1, None, 0, A2, None, A, ws, None) == 1
+    # FP4 queries and keys: the matrix-core shape rule of FP4 keys, 4-byte aligned query rows, and
+    # the decoded queries' room in the workspace
+    assert b._index(A, A, A, b.FP4QK, 1, 1, 4, 64, 100, None, 1, None, 0, A2, None, A, ws, None) == 2
+    assert b._index(MIS, A, A, b.FP4QK, 1, 1, 64, 128, 100, None, 1, None, 0, A2, None, A, ws, None) == 1
+    qk = b._index_ws(b.FP4QK, 2, 3, 64, 128, 1000, 0)
+    assert qk >= b._index_ws(b.FP4, 2, 3, 64, 128, 1000, 0) + 2 * 3 * 64 * 128 * 2
     # FP4 keys without a matrix-core shape (HI = 4), and with dI % 64 != 0
     assert b._index(A, A, A, 2, 1, 1, 4, 64, 100, None, 1, None, 0, A2, None, A, ws, None) == 2
     assert b._index(A, A, A, 2, 1, 1, 64, 32, 100, None, 1, None, 0, A2, None, A, ws, None) == 2
@@ -99,6 +105,12 @@ def test_layer_mode_pointer_mismatch():
     need = b._layer_ws(ctypes.byref(a))
     assert need > 0
     assert b._layer(ctypes.byref(a), A, need - 256, None) == 3   # workspace one block short
+    a.score_fmt = 7
+    assert b._layer(ctypes.byref(a), A, 1 << 40, None) == 1      # unknown score format
+    a.score_fmt, a.idx_dt, a.qI = b.SCORE_FMTS["bf16"], b.FP4QK, MIS
+    assert b._layer(ctypes.byref(a), A, 1 << 40, None) == 1      # FP4 query rows misaligned
+    a.qI = A
+    assert b._layer_ws(ctypes.byref(a)) >= need + 64 * 128 * 2  # room for the decoded queries
 
 
 def test_swa_merge_and_quantize_validation():
