@@ -23,6 +23,8 @@ namespace csa2 {
 // Selected entries per split: fixed, so that a query's result does not depend
 // on the batch it is computed in.
 constexpr int ATT_SPLIT = 128;
+// Query tokens per sequence from which a call counts as a prefill chunk.
+constexpr int ATT_TILES_MIN_Q = 64;
 
 namespace {
 
@@ -883,6 +885,271 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__re
     }
 }
 
+// ------------------------------------------------------- prefill kernel
+// Block = one query token x HB = HPW * HH heads, over all k of its selected
+// entries in tiles of 64 rows: a prefill chunk has thousands of queries, so
+// whole queries fill the chip and no split partials go through memory.  The
+// rows of tile t + 1 are copied straight from HBM into the second LDS buffer
+// (16-byte global->LDS loads, one 1 KiB row per wave instruction, no
+// registers) while tile t is computed from the first, and the softmax runs
+// online: each tile's maximum per head joins the running one, which rescales
+// the running sum and the O^T accumulators before the tile's P C is added.
+// Phases per tile, as in the split kernel: S^T = C Q^T (wave (rq, hh): rows
+// 16 rq .. 16 rq + 15, heads hh HPW ..), p = exp(a - m) to LDS, O^T = C^T P^T
+// (wave (rq, hh): channels rq D/4 ..).  bf16 rows of D = 512 only (a row is one
+// wave-wide load).  A query's result does not depend on B, Q or the batch.
+constexpr int TROWS = 64;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at dst + 16 l (dst is the same for the whole wave).  A device function of
+// its own, so that the host side of the kernel never sees the builtin.
+__device__ __forceinline__ void copy16_to_lds(const uint16_t *src, uint16_t *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+template <int D, int HPW, int HH>
+__global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__restrict__ q,
+                                                           const uint16_t *__restrict__ kv, int Q, int H, int64_t N,
+                                                           const int32_t *__restrict__ idx, int k, float scale,
+                                                           int nq, uint16_t *__restrict__ out, float *__restrict__ lse) {
+    constexpr int NW = 4 * HH, NT = 64 * NW;
+    constexpr int HB = HPW * HH;
+    constexpr int HT = HPW / 16;
+    constexpr int KS = D / 32;
+    constexpr int LS = D + 8;          // LDS row stride (16-bit elements)
+    constexpr int DQ = D / 4;
+    constexpr int DT = DQ / 16;
+    constexpr int KT = TROWS / 32;     // O contraction steps per tile
+    constexpr int PST = TROWS + 8;     // P row stride
+    constexpr int QS = D + 8;
+    static_assert(D == 512, "one bf16 row is one 64-lane load of 16 bytes");
+    static_assert(HB * QS <= 2 * TROWS * LS, "query staging fits the row buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t rows_lds[2][TROWS * LS];
+    __shared__ __attribute__((aligned(16))) uint16_t p_lds[HB * PST];
+    __shared__ float mx_sh[4][HB];
+    __shared__ float l_sh[4][HB];
+    __shared__ __attribute__((aligned(16))) int32_t jsh[2][TROWS];
+
+    // block L on XCD L % 8: consecutive queries (which share most of their
+    // rows) on one XCD, the head groups of a query beside them
+    const int NG = H / HB;
+    const int P8 = (nq + 7) / 8;
+    const int L = blockIdx.x;
+    const int jx = (L / 8) / NG;
+    const int hgb = (L / 8) % NG;
+    const int bq = (L % 8) * P8 + jx;
+    if (jx >= P8 || bq >= nq) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, kg = lane >> 4;
+    const int rq = wave & 3, hh = wave >> 2, hw0 = hh * HPW;
+    const int ntl = (k + TROWS - 1) / TROWS;
+    const int32_t *irow = idx + (size_t)bq * k;
+    const uint16_t *kvb = kv + (size_t)(bq / Q) * N * D;
+
+    // ---- query heads: registers -> LDS [head][QS] -> this wave's fragments
+    constexpr int QP = HB * D / 8, QPT = (QP + NT - 1) / NT;
+    {
+        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q + ((size_t)bq * H + hgb * HB) * D);
+        u32x4 qst[QPT];
+#pragma unroll
+        for (int i = 0; i < QPT; i++) qst[i] = qsrc[QP % NT == 0 ? tid + NT * i : min(tid + NT * i, QP - 1)];
+        uint16_t *qs = &rows_lds[0][0];
+#pragma unroll
+        for (int i = 0; i < QPT; i++) {
+            const int pc = tid + NT * i;
+            if (QP % NT == 0 || pc < QP) *reinterpret_cast<u32x4 *>(qs + (pc / (D / 8)) * QS + (pc % (D / 8)) * 8) = qst[i];
+        }
+    }
+    for (int e = tid; e < TROWS; e += NT) {
+        const int j = e < k ? irow[e] : -1;
+        jsh[0][e] = (j >= 0 && j < N) ? j : -1;
+    }
+    __syncthreads();
+    u32x4 qf[HT][KS];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+        for (int s2 = 0; s2 < KS; s2++)
+            qf[ht][s2] = *reinterpret_cast<const u32x4 *>(&rows_lds[0][0] + (hw0 + 16 * ht + col) * QS + 32 * s2 + 8 * kg);
+    __syncthreads();  // the row buffers are free
+
+    // rows of tile t into buffer b: wave w copies rows w, w + NW, ...; an entry
+    // of -1 copies row 0 (masked later)
+    auto issue = [&](int b, const int32_t *js) {
+#pragma unroll
+        for (int r = wave; r < TROWS; r += NW) {
+            const int j = __builtin_amdgcn_readfirstlane(js[r]);
+            const uint16_t *src = kvb + (size_t)(j >= 0 ? j : 0) * D + 8 * lane;
+            copy16_to_lds(src, &rows_lds[b][r * LS]);
+        }
+    };
+    issue(0, jsh[0]);
+    int jn = -1;  // next tile's entry of this thread (tid < TROWS)
+    if (tid < TROWS && TROWS + tid < k) {
+        const int j = irow[TROWS + tid];
+        jn = (j >= 0 && j < N) ? j : -1;
+    }
+
+    f32x4 oacc[DT][HT];
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) oacc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[HT], l_run[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) {
+        m_run[ht] = NEG_INF;
+        l_run[ht] = 0.f;
+    }
+
+    for (int t = 0; t < ntl; t++) {
+        const int cur = t & 1;
+        // this tile's rows (and the next tile's entries) have landed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (tid < TROWS) jsh[cur ^ 1][tid] = jn;
+        __syncthreads();
+        if (t + 1 < ntl) {
+            issue(cur ^ 1, jsh[cur ^ 1]);
+            jn = -1;
+            const int e = (t + 2) * TROWS + tid;
+            if (tid < TROWS && e < k) {
+                const int j = irow[e];
+                jn = (j >= 0 && j < N) ? j : -1;
+            }
+        }
+        const uint16_t *rows = rows_lds[cur];
+
+        // S^T for rows 16 rq + 4 kg + i, heads hw0 + 16 ht + col
+        f32x4 sacc[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) sacc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            const uint16_t *arow = rows + (16 * rq + col) * LS + 8 * kg;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; s2++) {
+                const u32x4 a0 = *reinterpret_cast<const u32x4 *>(arow + 32 * s2);
+#pragma unroll
+                for (int ht = 0; ht < HT; ht++) sacc[ht] = mma<CSA2_BF16>(a0, qf[ht][s2], sacc[ht]);
+            }
+        }
+        const int4 jv = *reinterpret_cast<const int4 *>(&jsh[cur][16 * rq + 4 * kg]);
+        const int jj[4] = {jv.x, jv.y, jv.z, jv.w};
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) {
+            float mt = NEG_INF;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float v = jj[i] >= 0 ? sacc[ht][i] * scale : NEG_INF;
+                sacc[ht][i] = v;
+                mt = fmaxf(mt, v);
+            }
+            mt = bfly32(bfly16(mt, OpMax{}), OpMax{});
+            if (kg == 0) mx_sh[rq][hw0 + 16 * ht + col] = mt;
+        }
+        __syncthreads();
+        float alpha[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) {
+            const int hd = hw0 + 16 * ht + col;
+            const float mt = fmaxf(fmaxf(mx_sh[0][hd], mx_sh[1][hd]), fmaxf(mx_sh[2][hd], mx_sh[3][hd]));
+            const float mh = fmaxf(m_run[ht], mt);
+            alpha[ht] = mh == NEG_INF ? 1.f : (m_run[ht] == NEG_INF ? 0.f : __expf(m_run[ht] - mh));
+            m_run[ht] = mh;
+            float pv[4], ls = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float a = sacc[ht][i];
+                pv[i] = a == NEG_INF ? 0.f : __expf(a - mh);
+                ls += pv[i];
+            }
+            const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{pv[0], pv[1]}), bf16x2v));
+            const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{pv[2], pv[3]}), bf16x2v));
+            *reinterpret_cast<uint2 *>(p_lds + hd * PST + 16 * rq + 4 * kg) = make_uint2(w0, w1);
+            ls = bfly32(bfly16(ls, OpAdd{}), OpAdd{});
+            if (kg == 0) l_sh[rq][hd] = ls;
+        }
+        __syncthreads();
+        // O^T[channel][head] += C^T P^T for channels rq DQ + 16 dt + (lane rows)
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) {
+            const int hd = hw0 + 16 * ht + col;
+            l_run[ht] = l_run[ht] * alpha[ht] + ((l_sh[0][hd] + l_sh[1][hd]) + (l_sh[2][hd] + l_sh[3][hd]));
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) oacc[dt][ht][r] *= alpha[ht];
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; kt++) {
+            u32x4 pb[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++) {
+                const uint16_t *pp = p_lds + (hw0 + 16 * ht + col) * PST + 32 * kt + 4 * kg;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(pp);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(pp + 16);
+                pb[ht] = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+            const uint16_t *tr0 = rows + (32 * kt + 4 * kg + (col >> 2)) * LS + 4 * (col & 3) + rq * DQ;
+            const uint16_t *tr1 = tr0 + 16 * LS;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 __attribute__((address_space(3))) *)(tr0 + 16 * dt));
+                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 __attribute__((address_space(3))) *)(tr1 + 16 * dt));
+                const u32x4 av = {__builtin_bit_cast(uint32_t, s16x2{lo4[0], lo4[1]}),
+                                  __builtin_bit_cast(uint32_t, s16x2{lo4[2], lo4[3]}),
+                                  __builtin_bit_cast(uint32_t, s16x2{hi4[0], hi4[1]}),
+                                  __builtin_bit_cast(uint32_t, s16x2{hi4[2], hi4[3]})};
+#pragma unroll
+                for (int ht = 0; ht < HT; ht++) oacc[dt][ht] = mma<CSA2_BF16>(av, pb[ht], oacc[dt][ht]);
+            }
+        }
+    }
+
+    // ---- output: out / l in bf16, staged as [head][channel] in the free row
+    // buffer, written as whole rows; lse = m + ln l
+    __syncthreads();
+    constexpr int OS = D + 8;
+    uint16_t *stage = &rows_lds[0][0];
+#pragma unroll
+    for (int ht = 0; ht < HT; ht++) {
+        const int hd = hw0 + 16 * ht + col;
+        const float l = l_run[ht];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t *srow = stage + hd * OS + rq * DQ + 4 * kg;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const f32x4 o = oacc[dt][ht];
+            const uint32_t w0 = uint32_t(f32_to_bf16_rne(o[0] * inv)) | (uint32_t(f32_to_bf16_rne(o[1] * inv)) << 16);
+            const uint32_t w1 = uint32_t(f32_to_bf16_rne(o[2] * inv)) | (uint32_t(f32_to_bf16_rne(o[3] * inv)) << 16);
+            *reinterpret_cast<uint2 *>(srow + 16 * dt) = make_uint2(w0, w1);
+        }
+        if (lse && kg == 0 && rq == 0) lse[(size_t)bq * H + hgb * HB + hd] = l > 0.f ? m_run[ht] + logf(l) : NEG_INF;
+    }
+    __syncthreads();
+    {
+        uint16_t *dst = out + ((size_t)bq * H + hgb * HB) * D;
+        constexpr int OP = HB * D / 8;
+#pragma unroll
+        for (int i = tid; i < OP; i += NT) {
+            const int r = i / (D / 8), c = i % (D / 8);
+            *reinterpret_cast<u32x4 *>(dst + (size_t)r * D + 8 * c) = *reinterpret_cast<const u32x4 *>(stage + r * OS + 8 * c);
+        }
+    }
+}
+
+void launch_tiles(const AttnPlan &p, const void *q, const void *kv, const int32_t *idx, float scale, void *out,
+                  float *lse, hipStream_t s) {
+    const int nq = p.B * p.Q;
+    constexpr int HB = 64;
+    const int NG = p.H / HB;
+    const int blocks = 8 * ((nq + 7) / 8) * NG;
+    hipLaunchKernelGGL((k_attn_tiles<512, 32, 2>), dim3(blocks), dim3(512), 0, s, static_cast<const uint16_t *>(q),
+                       static_cast<const uint16_t *>(kv), p.Q, p.H, p.N, idx, p.k, scale, nq,
+                       static_cast<uint16_t *>(out), lse);
+}
+
 // Heads per block: as many as keep at least 256 blocks (one per compute unit),
 // from 64 down to 16; the blocks that share a split's rows sit on one XCD.
 template <int D, int FMT>
@@ -921,17 +1188,21 @@ void launch_split(const AttnPlan &p, const void *q, const void *kv, const int32_
 }  // namespace
 
 AttnPlan attn_plan(int q_dt, int kv_dt, int B, int Q, int H, int D, int64_t N, int k) {
-    AttnPlan p{q_dt, kv_dt, B, Q, H, D, N, k, false, 1};
+    AttnPlan p{q_dt, kv_dt, B, Q, H, D, N, k, false, 1, false};
     p.mfma = q_dt == CSA2_BF16 && (kv_dt == CSA2_BF16 || kv_dt == CSA2_FP4) &&
              (H == 16 || H == 32 || H == 64 || H == 128) && (D == 64 || D == 128 || D == 256 || D == 512);
     p.nsplit = p.mfma ? (k + ATT_SPLIT - 1) / ATT_SPLIT : 1;
+    // a prefill chunk (many query tokens per sequence) of bf16 rows of 512:
+    // whole queries per block, no split partials
+    p.tiles = p.mfma && kv_dt == CSA2_BF16 && D == 512 && H % 64 == 0 && Q >= ATT_TILES_MIN_Q && k > ATT_SPLIT;
+    if (p.tiles) p.nsplit = 1;
     return p;
 }
 
 bool attn_handoff_supported(const AttnPlan &p, const SelPlan &sp) {
     // the matrix-core kernel finishes the selection in its prologue when the
     // IN bitmap is at most 1024 words (the one-block selection path)
-    return p.mfma && sp.certified && sp.nwords <= 1024;
+    return p.mfma && !p.tiles && sp.certified && sp.nwords <= 1024;
 }
 
 bool attn_supported(const AttnPlan &p) {
@@ -940,7 +1211,7 @@ bool attn_supported(const AttnPlan &p) {
 }
 
 size_t attn_workspace(const AttnPlan &p) {
-    if (!p.mfma || p.nsplit == 1) return 0;
+    if (!p.mfma || p.tiles || p.nsplit == 1) return 0;
     Carve c(nullptr, 0);
     c.take<uint16_t>((size_t)p.B * p.Q * p.nsplit * p.H * p.D);
     c.take<float2>((size_t)p.B * p.Q * p.nsplit * p.H);
@@ -957,6 +1228,12 @@ void attn_run(const AttnPlan &p, const void *q, const void *kv, const int32_t *i
         hipLaunchKernelGGL(k_attn_valu, dim3(p.H, BQ), dim3(256), lds, s, q, p.q_dt,
                            static_cast<const uint8_t *>(kv), p.kv_dt, p.Q, p.H, p.D, p.N, idx, p.k, scale, out, lse);
         check_launch("attention (vector)");
+        return;
+    }
+    if (p.tiles) {
+        if (sel) throw Error(CSA2_EINTERNAL, "the prefill attention takes finished indices");
+        launch_tiles(p, q, kv, idx, scale, out, lse, s);
+        check_launch("attention (prefill tiles)");
         return;
     }
     uint16_t *part_o = nullptr;

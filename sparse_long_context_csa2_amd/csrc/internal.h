@@ -87,6 +87,7 @@ struct AttnPlan {
     int k;
     bool mfma;
     int nsplit;
+    bool tiles;  // prefill chunk: whole queries per block over 64-row tiles
 };
 AttnPlan attn_plan(int q_dt, int kv_dt, int B, int Q, int H, int D, int64_t N, int k);
 bool attn_supported(const AttnPlan &p);
