@@ -8,9 +8,11 @@
 //     l_r[c] = x_t . wz[:, c] + bias[r][c],   out_i[c] = sum_r softmax_r(l[c]) x_t[c]
 // Positions before token 0 are dropped.
 //
-// Two kernels: the projection Z = X wz for every token row (a tiled fp32 GEMM
-// from LDS), then the windowed per-channel softmax pooling, one thread per
-// (entry, channel), reading Z and X once per window position.
+// bf16 rows of 128 or 512 channels: one matrix-core kernel that projects and
+// pools (below).  Otherwise two kernels: the projection Z = X wz for every
+// token row (a tiled fp32 GEMM from LDS), then the windowed per-channel
+// softmax pooling, one thread per (entry, channel), reading Z and X once per
+// window position.
 #include "internal.h"
 
 namespace csa2 {
@@ -95,13 +97,124 @@ __global__ __launch_bounds__(256) void k_compress_pool(const void *__restrict__ 
     else static_cast<uint16_t *>(out)[(size_t)i * D + c] = f32_to_bf16_rne(v);
 }
 
+// ---------------------------------------------------- bf16: matrix cores
+// For bf16 rows the projection runs on the matrix cores and the pooling is
+// fused behind it, so Z never goes through memory.  Block = EPB = 64 / m
+// consecutive entries x 64 channels; it needs the token rows of their
+// windows, first(e0) .. first(e0) + (EPB + 1) m - 1 (at most 80), and
+// computes Z for 80 rows from there: wave w takes channels c0 + 16 w ..
+// + 15, its W^T fragments for all D held in registers (from a transposed copy
+// of W), the 5 row tiles' X fragments read per 32-deep step.  Each Z element
+// is one matrix-core dot product over d in a fixed order, whatever the
+// block, so an entry comes out bitwise the same from a chunk with a halo as
+// from the whole context.  Z goes to LDS; then each thread pools entries
+// for its channels as the fp32 kernel does.
+constexpr int CZ_ROWS = 80;  // 5 tiles of 16 rows: EPB m + m <= 64 + 16
+
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t *__restrict__ w, int D,
+                                                        uint16_t *__restrict__ wt) {
+    __shared__ uint16_t t[32][33];
+    const int bx = blockIdx.x * 32, by = blockIdx.y * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int r = ty; r < 32; r += 8)
+        if (by + r < D && bx + tx < D) t[r][tx] = w[(size_t)(by + r) * D + bx + tx];
+    __syncthreads();
+    for (int r = ty; r < 32; r += 8)
+        if (bx + r < D && by + tx < D) wt[(size_t)(bx + r) * D + by + tx] = t[tx][r];
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_compress_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wt,
+                                                       const float *__restrict__ bias, int64_t rows, int64_t n_out,
+                                                       int m, int halo, uint16_t *__restrict__ out) {
+    constexpr int KS = D / 32;
+    constexpr int RT = CZ_ROWS / 16;
+    constexpr int ZS = 64 + 1;
+    __shared__ float zs[CZ_ROWS * ZS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, kg = lane >> 4;
+    const int epb = 64 / m;
+    const int64_t e0 = (int64_t)blockIdx.y * epb;
+    const int c0 = blockIdx.x * 64;
+    const int64_t r0 = halo ? e0 * m : (e0 - 1) * m;  // token row of window position 0 of entry e0
+    // W^T fragments of this wave's 16 channels: B[d][c] = W[d][c] = Wt[c][d]
+    u32x4 bw[KS];
+    {
+        const uint16_t *wr = wt + (size_t)(c0 + 16 * wave + col) * D + 8 * kg;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; s2++) bw[s2] = *reinterpret_cast<const u32x4 *>(wr + 32 * s2);
+    }
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const uint16_t *xr[RT];
+    bool ok[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) {
+        const int64_t r = r0 + 16 * rt + col;
+        ok[rt] = r >= 0 && r < rows;
+        xr[rt] = x + (size_t)(ok[rt] ? r : 0) * D + 8 * kg;
+    }
+    // X fragments two steps ahead of the matrix cores (three register sets,
+    // named statically: the loop is fully unrolled, so bw stays in registers)
+    u32x4 a[3][RT];
+    auto load_a = [&](int set, int s2) {
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++) a[set][rt] = ok[rt] ? *reinterpret_cast<const u32x4 *>(xr[rt] + 32 * s2) : zero;
+    };
+    load_a(0, 0);
+    load_a(1, 1);
+#pragma unroll
+    for (int s2 = 0; s2 < KS; s2++) {
+        if (s2 + 2 < KS) load_a((s2 + 2) % 3, s2 + 2);
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s2 % 3][rt]),
+                                                             __builtin_bit_cast(bf16x8, bw[s2]), acc[rt], 0, 0, 0);
+    }
+    // Z[row 16 rt + 4 kg + i][channel 16 wave + col] -> LDS
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) zs[(16 * rt + 4 * kg + i) * ZS + 16 * wave + col] = acc[rt][i];
+    __syncthreads();
+    // pooling: thread -> channel c0 + (tid % 64), entries e0 + tid / 64 + 4 j
+    const int cl = threadIdx.x & 63, c = c0 + cl;
+    for (int el = threadIdx.x >> 6; el < epb; el += 4) {
+        const int64_t i = e0 + el;
+        if (i >= n_out) break;
+        const int lr0 = el * m;  // local row of window position 0 (rows from r0)
+        float l[32];
+        float mx = -__builtin_inff();
+        for (int r = 0; r < 2 * m; r++) {
+            const int64_t t = r0 + lr0 + r;
+            l[r] = -__builtin_inff();
+            if (t < 0) continue;
+            l[r] = zs[(lr0 + r) * ZS + cl] + bias[(size_t)r * D + c];
+            mx = fmaxf(mx, l[r]);
+        }
+        float den = 0.f, a = 0.f;
+        for (int r = 0; r < 2 * m; r++) {
+            const int64_t t = r0 + lr0 + r;
+            if (t < 0) continue;
+            const float p = expf(l[r] - mx);
+            den += p;
+            a = fmaf(p, bf16_to_f32(x[(size_t)t * D + c]), a);
+        }
+        out[(size_t)i * D + c] = f32_to_bf16_rne(a / den);
+    }
+}
+
 }  // namespace
 
+static bool compress_mfma(int dt, int D) { return dt == CSA2_BF16 && (D == 128 || D == 512); }
+
 size_t compress_workspace(int dt, int64_t n_out, int D, int m, int halo) {
-    (void)dt;
     const int64_t rows = halo ? (n_out + 1) * m : n_out * m;
     Carve c(nullptr, 0);
-    c.take<float>((size_t)rows * D);
+    if (compress_mfma(dt, D)) c.take<uint16_t>((size_t)D * D);  // W^T
+    else c.take<float>((size_t)rows * D);
     return c.used;
 }
 
@@ -109,6 +222,23 @@ void compress_run(const void *x, int dt, int64_t n_out, int D, int m, int halo, 
                   void *out, void *ws, size_t ws_bytes, hipStream_t s) {
     const int64_t rows = halo ? (n_out + 1) * m : n_out * m;
     Carve c(ws, ws_bytes);
+    if (compress_mfma(dt, D)) {
+        uint16_t *wt = c.take<uint16_t>((size_t)D * D);
+        if (c.used > ws_bytes) throw Error(CSA2_EWORKSPACE, "compression workspace too small");
+        hipLaunchKernelGGL(k_transpose_bf16, dim3((D + 31) / 32, (D + 31) / 32), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(wz), D, wt);
+        check_launch("compression weights transpose");
+        const int epb = 64 / m;
+        const dim3 g(D / 64, (unsigned)((n_out + epb - 1) / epb));
+        if (D == 512)
+            hipLaunchKernelGGL(k_compress_mfma<512>, g, dim3(256), 0, s, static_cast<const uint16_t *>(x), wt, bias,
+                               rows, n_out, m, halo, static_cast<uint16_t *>(out));
+        else
+            hipLaunchKernelGGL(k_compress_mfma<128>, g, dim3(256), 0, s, static_cast<const uint16_t *>(x), wt, bias,
+                               rows, n_out, m, halo, static_cast<uint16_t *>(out));
+        check_launch("compression (matrix cores)");
+        return;
+    }
     float *Z = c.take<float>((size_t)rows * D);
     if (c.used > ws_bytes) throw Error(CSA2_EWORKSPACE, "compression workspace too small");
     dim3 g1((D + 63) / 64, (unsigned)((rows + 63) / 64));

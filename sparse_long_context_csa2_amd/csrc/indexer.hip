@@ -553,6 +553,176 @@ __global__ __launch_bounds__(256) void k_err_bound(const void *__restrict__ qI, 
 constexpr bool stream_fits(int HI, int DI) { return HI * DI / 128 + DI / 2 <= 128; }
 constexpr int64_t STREAM_MIN_TILES = 1024;  // below this, one tile per block fills the chip better
 
+// ------------------------------------------------------------ prefill path
+// A prefill chunk scores thousands of query tokens against the same keys, so
+// the score is one dense contraction [queries x heads] x [keys] and the keys
+// are what to reuse.  Block = one 256-key tile x PF_QT query tokens of one
+// sequence: each wave loads the bf16 B fragments of its 64 keys once (and
+// their squared norms), then takes the block's queries in turn, each
+// query's heads (A fragments) read from LDS, where the next query is staged
+// (global -> registers -> the other LDS buffer) while this one is scored.  The
+// contraction, the ReLU-weighted head sum and its order are those of
+// k_index_mfma, so the scores are the same bits.  Per query and tile the
+// waves' statistics meet in LDS and are written at the end; tile 0's blocks
+// also write each query's sum_h |w_h| ||q_h||.
+constexpr int PF_QT = 32;      // query tokens per block
+constexpr int PF_MIN_Q = 64;   // query tokens per sequence from which the chunk path is taken
+
+template <int HI, int DI>
+__global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t *__restrict__ qI, const float *__restrict__ w,
+                                                          const uint16_t *__restrict__ kI, int Q, int64_t N,
+                                                          const int64_t *__restrict__ q_pos, int m,
+                                                          float *__restrict__ scores, TileStat *__restrict__ stats,
+                                                          int ntiles, double *__restrict__ sumwq) {
+    constexpr int HT = HI / 16, KS = DI / 32, G = 4;
+    constexpr int QE = HI * DI;                 // bf16 elements of one query token's heads
+    constexpr int QPT = QE / 8 / 256;           // 16-byte pieces per thread
+    static_assert(QE % (8 * 256) == 0, "a query's heads split evenly over the block");
+    constexpr int QRS = DI + 8;                 // LDS row stride of a head (16-byte pad: no bank conflicts)
+    __shared__ __attribute__((aligned(16))) uint16_t qs[2][HI * QRS];
+    __shared__ float wsh[2][HI];
+    __shared__ f32x4 stp[PF_QT][4];             // per query and wave: smin, smax, kmax2, count
+    const int tile = blockIdx.x;
+    const int qtiles = (Q + PF_QT - 1) / PF_QT;
+    const int b = blockIdx.y / qtiles;
+    const int q0 = (blockIdx.y % qtiles) * PF_QT;
+    const int nq = min(PF_QT, Q - q0);
+    const int bq0 = b * Q + q0;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, kg = lane >> 4;
+    const int64_t slot0 = (int64_t)tile * TILE + wave * 64;
+
+    // this wave's keys: B fragments and squared norms (rows past N read as 0)
+    u32x4 kb[G][KS];
+    float kn[G];
+    {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            const int64_t j = slot0 + g * 16 + col;
+            const uint16_t *kr = kI + ((size_t)b * N + (j < N ? j : 0)) * DI + 8 * kg;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; s2++) kb[g][s2] = j < N ? *reinterpret_cast<const u32x4 *>(kr + 32 * s2) : zero;
+        }
+    }
+    // query 0 of the block into buffer 0
+    auto load_q = [&](int qi, u32x4 (&reg)[QPT], float &wreg) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(qI + (size_t)(bq0 + qi) * QE);
+#pragma unroll
+        for (int i = 0; i < QPT; i++) reg[i] = src[threadIdx.x + 256 * i];
+        wreg = threadIdx.x < HI ? w[(size_t)(bq0 + qi) * HI + threadIdx.x] : 0.f;
+    };
+    auto put_q = [&](int buf, const u32x4 (&reg)[QPT], float wreg) {
+#pragma unroll
+        for (int i = 0; i < QPT; i++) {
+            const int pc = threadIdx.x + 256 * i;  // 16-byte piece: head pc / (DI / 8), channels 8 (pc % (DI / 8)) ..
+            *reinterpret_cast<u32x4 *>(qs[buf] + (pc / (DI / 8)) * QRS + 8 * (pc % (DI / 8))) = reg[i];
+        }
+        if (threadIdx.x < HI) wsh[buf][threadIdx.x] = wreg;
+    };
+    // queries in flight two ahead: query qi + 1 waits in registers (set
+    // (qi + 1) & 1) while qi is scored, and qi + 2 is requested into the set
+    // qi just left; both sets are named statically (the loop is unrolled by 2)
+    u32x4 qr[2][QPT];
+    float wr[2] = {0.f, 0.f};
+    load_q(0, qr[0], wr[0]);
+    if (nq > 1) load_q(1, qr[1], wr[1]);
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        float ss = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; s2++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                bf16x2 v = __builtin_bit_cast(bf16x2, kb[g][s2][e]);
+                ss = __builtin_amdgcn_fdot2_f32_bf16(v, v, ss, false);
+            }
+        kn[g] = bfly32(bfly16(ss, OpAdd{}), OpAdd{});
+    }
+    put_q(0, qr[0], wr[0]);
+
+    auto score_query = [&](int qi) {
+        const int buf = qi & 1;
+        const int bq = bq0 + qi;
+        const int64_t nvis = visible_entries(q_pos, bq, m, N);
+        u32x4 qa[HT][KS];
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+            for (int s2 = 0; s2 < KS; s2++)
+                qa[ht][s2] = *reinterpret_cast<const u32x4 *>(qs[buf] + (ht * 16 + col) * QRS + 32 * s2 + 8 * kg);
+        float wv[HT][4];
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) wv[ht][r] = wsh[buf][ht * 16 + 4 * kg + r];
+        float smin = POS_INF, smax = NEG_INF, kmax2 = 0.f, cnt = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            f32x4 acc[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < KS; s2++)
+#pragma unroll
+                for (int ht = 0; ht < HT; ht++)
+                    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ht][s2]),
+                                                                      __builtin_bit_cast(bf16x8, kb[g][s2]), acc[ht], 0,
+                                                                      0, 0);
+            float part = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ht++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
+            part = bfly32(bfly16(part, OpAdd{}), OpAdd{});
+            const int64_t slot = slot0 + g * 16 + col;
+            const bool valid = slot < nvis;
+            if (kg == 0 && slot < N) scores[(int64_t)bq * N + slot] = valid ? part : NEG_INF;
+            if (valid) {
+                smin = fminf(smin, part);
+                smax = fmaxf(smax, part);
+                kmax2 = fmaxf(kmax2, kn[g]);
+                cnt += 1.f;
+            }
+        }
+        // the wave's statistics: every kg group holds the same values
+        smin = bfly8(bfly4(bfly2(bfly1(smin, OpMin{}), OpMin{}), OpMin{}), OpMin{});
+        smax = bfly8(bfly4(bfly2(bfly1(smax, OpMax{}), OpMax{}), OpMax{}), OpMax{});
+        kmax2 = bfly8(bfly4(bfly2(bfly1(kmax2, OpMax{}), OpMax{}), OpMax{}), OpMax{});
+        cnt = bfly8(bfly4(bfly2(bfly1(cnt, OpAdd{}), OpAdd{}), OpAdd{}), OpAdd{});
+        if (lane == 0) stp[qi][wave] = f32x4{smin, smax, kmax2, cnt};
+    };
+    for (int q2 = 0; q2 < nq; q2 += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int qi = q2 + h;
+            if (qi < nq) {
+                __syncthreads();  // query qi staged in buffer qi & 1; the other buffer free
+                if (qi + 2 < nq) load_q(qi + 2, qr[h], wr[h]);
+                score_query(qi);
+                if (qi + 1 < nq) put_q(h ^ 1, qr[h ^ 1], wr[h ^ 1]);
+            }
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nq) {
+        const int qi = threadIdx.x;
+        TileStat t;
+        t.smin = fminf(fminf(stp[qi][0][0], stp[qi][1][0]), fminf(stp[qi][2][0], stp[qi][3][0]));
+        t.smax = fmaxf(fmaxf(stp[qi][0][1], stp[qi][1][1]), fmaxf(stp[qi][2][1], stp[qi][3][1]));
+        t.kmax2 = fmaxf(fmaxf(stp[qi][0][2], stp[qi][1][2]), fmaxf(stp[qi][2][2], stp[qi][3][2]));
+        t.nvalid = (uint32_t)(stp[qi][0][3] + stp[qi][1][3] + stp[qi][2][3] + stp[qi][3][3]);
+        stats[(size_t)(bq0 + qi) * ntiles + tile] = t;
+    }
+    if (sumwq && tile == 0) {
+        __shared__ double dred[256 / 16];
+        for (int qi = 0; qi < nq; qi++) {
+            const double v = block_sumwq<256>(qI, CSA2_BF16, w, HI, DI, bq0 + qi, dred);
+            if (threadIdx.x == 0) sumwq[bq0 + qi] = v;
+        }
+    }
+}
+
 template <int HI, int DI>
 void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, int64_t N, const int64_t *q_pos,
                  int m, const int32_t *cand, int P, float *scores, TileStat *stats, int ntiles, double *sumwq,
@@ -574,6 +744,14 @@ void launch_mfma(const void *qI, const float *w, const void *kI, int B, int Q, i
                                sumwq);
         }
         return;
+    }
+    if constexpr (HI == 64 && DI == 128) {
+        if (!cand && Q >= PF_MIN_Q) {
+            dim3 grid(ntiles, B * ((Q + PF_QT - 1) / PF_QT));
+            hipLaunchKernelGGL((k_index_prefill<HI, DI>), grid, dim3(256), 0, s, static_cast<const uint16_t *>(qI), w,
+                               static_cast<const uint16_t *>(kI), Q, N, q_pos, m, scores, stats, ntiles, sumwq);
+            return;
+        }
     }
     if constexpr (stream_fits(HI, DI)) {
         if (!cand && (int64_t)B * Q * ntiles >= STREAM_MIN_TILES) {

@@ -39,7 +39,8 @@ def test_workspace_sizes_grow_with_problem():
     assert b._index_ws(b.BF16, 16, 1, 64, 128, 32768, 0) > 0
     assert b._attn_ws(b.BF16, b.BF16, 16, 1, 64, 512, 2048) > 0       # split over blocks of 128 entries
     assert b._attn_ws(b.BF16, b.BF16, 16, 1, 64, 512, 128) == 0       # one split: no partials
-    assert b._compress_ws(b.BF16, 1024, 512, 4, 1) >= 4100 * 512 * 4
+    assert b._compress_ws(b.F32, 1024, 512, 4, 1) >= 4100 * 512 * 4        # fp32 rows: Z through memory
+    assert b._compress_ws(b.BF16, 1024, 512, 4, 1) == 512 * 512 * 2         # bf16 rows: only W^T
 
 
 def _rc(fn, *args):

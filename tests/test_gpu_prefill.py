@@ -74,3 +74,37 @@ def test_prefill_attention_batch_invariance(b):
     o1, l1 = b.sparse_attn(dev(q[1:2]), dev(kv[1:2]), dev(idx[1:2]), 0.05)
     torch.cuda.synchronize()
     assert torch.equal(host(out[1]), host(o1[0])) and torch.equal(host(lse[1]), host(l1[0]))
+
+
+def test_prefill_index_scores_within_bound(b):
+    """The chunk indexer (64 or more query tokens per sequence, 64 heads x 128
+    bf16): query tiles of 32 with a ragged last one (70 = 32 + 32 + 6), a
+    ragged last key tile, causal visibility per query token."""
+    from gpu_helpers import assert_scores_within_bound
+    rng = np.random.default_rng(77)
+    B, Q, N, HI, dI, m = 2, 70, 3000, 64, 128, 4
+    T = N * m
+    kI = synth.normal_bf16(rng, (B, N, dI))
+    qI = synth.normal_bf16(rng, (B, Q, HI, dI))
+    w = synth.uniform_f32(rng, (B, Q, HI))
+    q_pos = torch.arange(T - 300 - Q, T - 300, dtype=torch.int64).view(1, Q).repeat(B, 1)
+    q_pos[1] -= 2000                                   # the second sequence further back
+    ref = oracle.index_score(qI, w, kI, q_pos=q_pos, m=m)
+    s, e = b.index_score(dev(qI), dev(w), dev(kI), q_pos=dev(q_pos), m=m)
+    torch.cuda.synchronize()
+    worst = assert_scores_within_bound(s, e, ref)
+    print(f"prefill indexer: max |s - ref| / E = {worst:.3e}")
+
+
+@pytest.mark.parametrize("score_fmt", ["f64", "bf16"])
+def test_prefill_full_layer_with_pool(b, score_fmt):
+    """A Full layer (with a pool) over a causal chunk of 96 query tokens per
+    sequence: idx, pool and count bit-exact, outputs within tolerance."""
+    from gpu_helpers import run_group
+    spec = synth.Decode(B=2, Q=96, N=2500, HI=64, dI=128, H=64, D=512, k=400, P=800, seed=91,
+                        layers=["FULL", "REINDEX", "REUSE"], score_fmt=score_fmt)
+    d = synth.make_decode(spec)
+    T = spec.N * spec.m
+    q_pos = torch.arange(T - spec.Q, T, dtype=torch.int64).view(1, spec.Q).repeat(spec.B, 1)
+    q_pos[0] -= 777
+    run_group(b, d, q_pos=q_pos)
