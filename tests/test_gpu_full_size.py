@@ -45,7 +45,7 @@ def test_decode_128k_benchmark_inputs(b):
     """The benchmark's own GPU-drawn inputs and prepared Layer, checked whole."""
     sys.path.insert(0, ROOT)
     import bench
-    W = bench.WORKLOAD
+    W = bench.C2
     s = bench.make_sets(torch, 1)[0]
     scale = W["D"] ** -0.5
     L = b.Layer("FULL", q=s["q"], kv=s["kv"], k=W["k"], scale=scale, qI=s["qI"], w=s["w"], kI=s["kI"])
