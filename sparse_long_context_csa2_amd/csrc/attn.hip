@@ -1070,14 +1070,22 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
         }
         __syncthreads();
         // O^T[channel][head] += C^T P^T for channels rq DQ + 16 dt + (lane rows)
+        // (the accumulators are rescaled only when some head's maximum moved:
+        // after the first tiles that is rare, and multiplying by 1 is exact)
+        bool moved = false;
 #pragma unroll
         for (int ht = 0; ht < HT; ht++) {
             const int hd = hw0 + 16 * ht + col;
             l_run[ht] = l_run[ht] * alpha[ht] + ((l_sh[0][hd] + l_sh[1][hd]) + (l_sh[2][hd] + l_sh[3][hd]));
+            moved |= alpha[ht] != 1.f;
+        }
+        if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
-            for (int dt = 0; dt < DT; dt++)
+            for (int ht = 0; ht < HT; ht++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) oacc[dt][ht][r] *= alpha[ht];
+                for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) oacc[dt][ht][r] *= alpha[ht];
         }
 #pragma unroll
         for (int kt = 0; kt < KT; kt++) {

@@ -657,6 +657,11 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t *__rest
 #pragma unroll
             for (int r = 0; r < 4; r++) wv[ht][r] = wsh[buf][ht * 16 + 4 * kg + r];
         float smin = POS_INF, smax = NEG_INF, kmax2 = 0.f, cnt = 0.f;
+        // this lane's slots are slot0 + col + 16 g: visible below rem_vis, stored below rem_n
+        const int64_t own = slot0 + col;
+        const int rem_vis = (int)max<int64_t>(min<int64_t>(nvis - own, 1 << 20), -1);
+        const int rem_n = (int)max<int64_t>(min<int64_t>(N - own, 1 << 20), -1);
+        float *srow = scores + (size_t)bq * N + own;
 #pragma unroll
         for (int g = 0; g < G; g++) {
             f32x4 acc[HT];
@@ -675,9 +680,8 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t *__rest
 #pragma unroll
                 for (int r = 0; r < 4; r++) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
             part = bfly32(bfly16(part, OpAdd{}), OpAdd{});
-            const int64_t slot = slot0 + g * 16 + col;
-            const bool valid = slot < nvis;
-            if (kg == 0 && slot < N) scores[(int64_t)bq * N + slot] = valid ? part : NEG_INF;
+            const bool valid = g * 16 < rem_vis;
+            if (kg == 0 && g * 16 < rem_n) srow[g * 16] = valid ? part : NEG_INF;
             if (valid) {
                 smin = fminf(smin, part);
                 smax = fmaxf(smax, part);
