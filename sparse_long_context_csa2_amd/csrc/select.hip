@@ -22,9 +22,12 @@
 //              exact top-K and every OUT entry is not.
 //  3 classify: write the IN bitmap, count IN, append BAND slots to a list.
 //  4 rescore:  (certified only) binary64 score of every BAND entry in the
-//              sequential operation order of the definition (one wave per
-//              entry; the products of bf16/fp32 inputs are exact in binary64,
-//              so a fused multiply-add equals the rounded product + add).
+//              sequential operation order of the definition (lane h: head h's
+//              dot product; the products of bf16/fp32 inputs are exact in
+//              binary64, so a fused multiply-add equals the rounded product +
+//              add).  Up to 32,768 slots and 64 queries, steps 1-4 are one
+//              kernel: R replicas of each query's block repeat steps 1-3 and
+//              split the band between them.
 //  5 band+compact: rank the BAND entries by (exact score, slot) and keep the
 //              first K - |IN|; then compact the bitmap in slot order into the
 //              ascending index list.
@@ -735,6 +738,175 @@ constexpr int ONE_SPT = (int)(ONE_N / ONE_NT);
 constexpr int ONE_OUT = 8192;  // output entries staged in LDS
 static_assert(ONE_SPT == 32, "a thread's slots form one bitmap word");
 
+// ----------------------------------------------------------------- rescore
+// One wave per BAND entry (both targets' lists back to back), no staging:
+// lane h loads query head h's row and the key row (the same address in every
+// lane) with 16-byte loads into registers, and computes head h's dot product
+// in the definition's order d = 0, 1, ... (products of bf16/fp32 inputs are
+// exact in binary64, so fma = rounded product + add); t_h = w_h * ReLU(d_h)
+// is rounded on its own, and lane 0 sums t_0, t_1, ... from +0.0 out of LDS.
+// Idle blocks exit at once.
+constexpr int RS_NT = 256;
+constexpr int RS_VB = 16;      // 16-byte vectors per row batch
+
+struct RescoreKArgs {
+    const void *qI;
+    int dt;
+    int kfp4;  // key rows in FP4 (queries bf16)
+    const float *w;
+    const void *kI;
+    int Q, HI, dI;
+    int64_t N;
+    const int32_t *cand;
+    int64_t n;
+    int ntgt;
+    const SelQuery *sq;
+    const int32_t *band;
+    double *band_score;
+    int64_t band_cap;
+    int bf16key;  // store the scores rounded to bfloat16 (the ranked value)
+};
+
+// Running binary64 dot over one 16-byte vector of each row.
+template <bool F32>
+__device__ __forceinline__ double dot_vec(double acc, u32x4 q, u32x4 k) {
+#pragma clang fp contract(off)
+    if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc = __builtin_fma((double)__uint_as_float(q[e]), (double)__uint_as_float(k[e]), acc);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            acc = __builtin_fma((double)__uint_as_float(q[e] << 16), (double)__uint_as_float(k[e] << 16), acc);
+            acc = __builtin_fma((double)__uint_as_float(q[e] & 0xffff0000u), (double)__uint_as_float(k[e] & 0xffff0000u),
+                                acc);
+        }
+    }
+    return acc;
+}
+
+constexpr int RS_EPW = 2;                       // entries per wave
+constexpr int RS_EPB = RS_EPW * (RS_NT / 64);  // entries per block
+constexpr int RS_ROWB = 512;                    // longest key row staged (bytes)
+constexpr int RS_MAXD = RS_ROWB / 2;            // longest staged row in elements
+constexpr int RS_QS = RS_ROWB / 16 + 1;        // LDS stride of a staged query row in 16-byte vectors (padded)
+
+
+// Piece c of key row `row` as fp32 values, exactly: 16 bytes of bf16 or fp32
+// values, or (FP4 rows) 8 channels from 4 code bytes and their E4M3 scale
+// byte (a code times a scale has at most 7 significant bits, within fp32's
+// range).  The dot products widen them to binary64.
+template <bool F32>
+__device__ __forceinline__ void rs_stage_piece(const void *kI, int kfp4, size_t row, int dI, int c, float *dst) {
+    constexpr int ESZ = F32 ? 4 : 2;
+    constexpr int EPV = 16 / ESZ;  // elements per 16-byte vector
+    if (!F32 && kfp4) {
+        const uint8_t *krow = static_cast<const uint8_t *>(kI) + row * (size_t)(dI / 2 + dI / 16);
+        const uint32_t cw = *reinterpret_cast<const uint32_t *>(krow + 4 * c);
+        const uint32_t sb = krow[dI / 2 + c / 2];
+        const uint32_t se = (sb >> 3) & 15u, sm = sb & 7u;
+        double sc = se ? (double)(8u + sm) * __builtin_ldexp(1.0, (int)se - 10) : (double)sm * 0x1p-9;
+        if ((sb & 0x7fu) == 0x7fu) sc = 448.0;  // the E4M3 NaN code saturates
+        if (sb & 0x80u) sc = -sc;
+#pragma unroll
+        for (int x = 0; x < 8; x++) {
+            const uint32_t cd = (cw >> (4 * x)) & 15u;
+            const uint32_t ce = (cd >> 1) & 3u, mb = cd & 1u;
+            const double mag = ce ? (1.0 + 0.5 * mb) * __builtin_ldexp(1.0, (int)ce - 1) : 0.5 * mb;
+            dst[x] = (float)(((cd & 8u) ? -mag : mag) * sc);
+        }
+    } else {
+        const u32x4 kv = reinterpret_cast<const u32x4 *>(static_cast<const char *>(kI) + row * dI * ESZ)[c];
+#pragma unroll
+        for (int x = 0; x < EPV; x++) {
+            const uint32_t kw = kv[F32 ? x : x >> 1];
+            dst[x] = __uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
+        }
+    }
+}
+
+// Binary64 scores of the staged entries ew .. ew + RS_EPW - 1 of query bq
+// (their key rows in krow as fp32, the first 64 heads' query rows in
+// qsh; heads past 64 read from memory): lane h runs head h's dot products
+// of the RS_EPW entries as independent chains in the definition's order
+// d = 0, 1, ..., t_h = w_h * ReLU(d_h) goes through the wave's LDS rows tl,
+// and lane e < RS_EPW sums entry e's terms in head order from +0.0.
+// Returns lane e's score (not rounded to a key), 0 in the other lanes.
+template <bool F32>
+__device__ double rs_wave_scores(const void *qI, const float *w, int bq, int HI, int dI,
+                                 const u32x4 (*qsh)[RS_QS], const float (*krow_lds)[RS_MAXD], int ew,
+                                 double (*tl)[64]) {
+#pragma clang fp contract(off)
+    constexpr int ESZ = F32 ? 4 : 2;
+    constexpr int EPV = 16 / ESZ;
+    constexpr int KF = EPV / 4;  // fp32 key vectors per 16-byte query vector
+    const int lane = threadIdx.x & 63;
+    const int nvec = dI * ESZ / 16;
+    double sc = 0.0;  // lane e < RS_EPW: running score of entry ew + e
+    for (int h0 = 0; h0 < HI; h0 += 64) {
+        const int h = h0 + lane;
+        const int hc = h < HI ? h : HI - 1;  // idle lanes recompute the last head, unused
+        const u32x4 *qrow = reinterpret_cast<const u32x4 *>(static_cast<const char *>(qI) +
+                                                            ((size_t)bq * HI + hc) * dI * ESZ);
+        const double wh = (double)w[(size_t)bq * HI + hc];
+        double dot[RS_EPW];
+#pragma unroll
+        for (int e = 0; e < RS_EPW; e++) dot[e] = 0.0;
+        // vector u's query values and the entries' key values, one vector
+        // ahead of the multiply-adds (two register sets, so that the LDS
+        // reads of the next vector are in flight while this one is used)
+        u32x4 qa, qb;
+        f32x4 ka[RS_EPW][KF], kb[RS_EPW][KF];
+        auto load = [&](int u, u32x4 &qq, f32x4 (&kk)[RS_EPW][KF]) {
+            qq = h0 == 0 ? qsh[lane][u] : qrow[u];
+#pragma unroll
+            for (int e = 0; e < RS_EPW; e++)
+#pragma unroll
+                for (int x = 0; x < KF; x++) kk[e][x] = *reinterpret_cast<const f32x4 *>(&krow_lds[ew + e][u * EPV + 4 * x]);
+        };
+        auto step = [&](const u32x4 &qq, const f32x4 (&kk)[RS_EPW][KF]) {
+#pragma unroll
+            for (int i = 0; i < EPV; i++) {
+                const uint32_t qw = qq[F32 ? i : i >> 1];
+                const double qd = (double)__uint_as_float(F32 ? qw : ((i & 1) ? (qw & 0xffff0000u) : (qw << 16)));
+#pragma unroll
+                for (int e = 0; e < RS_EPW; e++) dot[e] = __builtin_fma(qd, (double)kk[e][i >> 2][i & 3], dot[e]);
+            }
+        };
+        load(0, qa, ka);
+        for (int u = 0; u < nvec; u += 2) {
+            if (u + 1 < nvec) load(u + 1, qb, kb);
+            step(qa, ka);
+            if (u + 1 >= nvec) break;
+            if (u + 2 < nvec) load(u + 2, qa, ka);
+            step(qb, kb);
+        }
+#pragma unroll
+        for (int e = 0; e < RS_EPW; e++) tl[e][lane] = h < HI ? wh * (dot[e] > 0.0 ? dot[e] : 0.0) : 0.0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < RS_EPW) {
+            // head terms t_h0, t_h0+1, ... added in order (read 16 at a time);
+            // lanes past the last head hold +0.0, and sc + 0.0 == sc (sc is
+            // never -0.0: it starts at +0.0 and a round-to-nearest sum is
+            // -0.0 only if both addends are)
+            const int hn = HI - h0 < 64 ? HI - h0 : 64;
+            for (int c0 = 0; c0 < hn; c0 += 16) {
+                double tv[16];
+#pragma unroll
+                for (int i = 0; i < 16; i++) tv[i] = tl[lane][c0 + i];
+#pragma unroll
+                for (int i = 0; i < 16; i++) sc = sc + tv[i];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    return lane < RS_EPW ? sc : 0.0;
+}
+
 struct OneArgs {
     const float *scores;
     const int32_t *cand;
@@ -756,7 +928,100 @@ struct OneArgs {
     int64_t band_cap;
     int32_t *in_list;  // certified, nullable: target 0's IN entries in ascending order, [BQ][K0]
     int bf16key;       // certified: the ranked value is the score rounded to bfloat16
+    // certified, nullable qI: the band's binary64 scores computed here, the
+    // band split over the gridDim.y replicas of each query's block (else the
+    // rescoring kernel computes them)
+    const void *qI;
+    int rs_f32, kfp4;
+    const float *w;
+    const void *kI;
+    int Q;
+    int64_t N;
+    double *band_score;
 };
+
+constexpr int OR_CH = RS_EPW * (ONE_NT / 64);  // band entries a replica rescores per round
+constexpr int OR_QPT = 64 * (RS_ROWB / 16) / ONE_NT;  // query-row vectors per thread (heads 0 .. 63)
+
+// Exclusive prefix sum over the block's threads in thread order, and the
+// block's total; red holds NT / 64 words and is free again on return.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t c, uint32_t *red, uint32_t &total) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t inc = wave_incl_scan_u32(c);
+    if (lane == 63) red[wave] = inc;
+    __syncthreads();
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; i++) {
+        const uint32_t r = red[i];
+        pre += i < wave ? r : 0u;
+        tot += r;
+    }
+    __syncthreads();
+    total = tot;
+    return pre + inc - c;
+}
+
+// The band rescoring inside the one-block selection.  Every replica of a
+// query's block classified the same slots, so each holds the same band lists
+// (target 0's, then target 1's, each in slot order); entry e is rescored by
+// replica e mod R, in rounds of OR_CH of its entries.  Each thread places its
+// own band slots that fall in the round, the round's key rows are staged in
+// LDS as binary64, and each wave computes RS_EPW entries' scores in the
+// definition's order (rs_wave_scores), as the rescoring kernel does.  The
+// first 64 heads' query rows are in qsh already.
+template <bool F32>
+__device__ void one_rescore(const OneArgs &a, int bq, int rep, int nrep, int s0, uint32_t kw0, uint32_t kw1,
+                            int32_t kp0, int32_t kp1, int32_t nb0, int32_t nb1, int32_t *slots,
+                            float (*krow)[RS_MAXD], u32x4 (*qsh)[RS_QS], double (*tl)[RS_EPW][64]) {
+    constexpr int ESZ = F32 ? 4 : 2;
+    constexpr int EPV = 16 / ESZ;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = bq / a.Q;
+    const int nvec = a.dI * ESZ / 16;
+    const int32_t total = nb0 + nb1;
+    const int32_t mine = total > rep ? (total - rep + nrep - 1) / nrep : 0;  // entries rep, rep + R, ...
+    if (mine == 0) return;
+    const size_t row0 = (size_t)bq * a.band_cap, row1 = ((size_t)gridDim.x + bq) * a.band_cap;
+    for (int32_t i0 = 0; i0 < mine; i0 += OR_CH) {
+        // entries rep + R (i0 + x), x < OR_CH: slots[x]
+        const int32_t e_lo = rep + nrep * i0, e_hi = rep + nrep * (i0 + OR_CH);  // their range [e_lo, e_hi)
+        for (int tg = 0; tg < 2; tg++) {
+            const uint32_t kw = tg == 0 ? kw0 : kw1;
+            int32_t e = tg == 0 ? kp0 : nb0 + kp1;
+            if (kw && e < e_hi && e + __builtin_popcount(kw) > e_lo) {
+                // e = rep + nrep * qd + r, stepped with e
+                int32_t qd = e >= rep ? (e - rep) / nrep : -((rep - e + nrep - 1) / nrep);
+                int32_t r = e - rep - qd * nrep;
+                for (uint32_t m = kw; m; m &= m - 1) {
+                    if (r == 0 && qd >= i0 && qd < i0 + OR_CH) slots[qd - i0] = s0 + __builtin_ctz(m);
+                    if (++r == nrep) r = 0, qd++;
+                }
+            }
+        }
+        __syncthreads();
+        const int cnt = mine - i0 < OR_CH ? mine - i0 : OR_CH;  // entries this round
+        for (int q = tid; q < cnt * nvec; q += ONE_NT) {
+            const int i = q / nvec, c = q - i * nvec;
+            const int32_t slot = slots[i];
+            const int64_t j = a.cand ? (int64_t)a.cand[(int64_t)bq * a.n + slot] : (int64_t)slot;
+            rs_stage_piece<F32>(a.kI, a.kfp4, (size_t)b * a.N + j, a.dI, c, &krow[i][c * EPV]);
+        }
+        __syncthreads();
+        const int ew = wave * RS_EPW;
+        if (ew < cnt) {
+            double sc = rs_wave_scores<F32>(a.qI, a.w, bq, a.HI, a.dI, qsh, krow, ew, tl[wave]);
+            const int32_t e = rep + nrep * (i0 + ew + lane);
+            if (a.bf16key) sc = bf16_round_key(sc);
+            if (lane < RS_EPW && ew + lane < cnt) {
+                if (e < nb0) a.band_score[row0 + e] = sc;
+                else a.band_score[row1 + (e - nb0)] = sc;
+            }
+        }
+        __syncthreads();  // the staged rows are replaced next round
+    }
+}
 
 // Smallest key in [lk, hk] whose bin is >= target (hk + 1 if none): a 64-way
 // search in a window of +-2048 keys around the estimate lo + target / inv,
@@ -788,7 +1053,13 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     __shared__ uint64_t key_lds[CERT ? 1 : BANDFAST];
     __shared__ int32_t slot_lds[CERT ? 1 : BANDFAST];
     __shared__ int32_t out_lds[CERT ? 1 : ONE_OUT];
+    // certified band rescoring (a.qI set): chunks of the band, query rows, head terms
+    __shared__ __attribute__((aligned(16))) float or_krow[CERT ? OR_CH : 1][RS_MAXD];
+    __shared__ u32x4 or_q[CERT ? 64 : 1][RS_QS];
+    __shared__ double or_tl[CERT ? ONE_NT / 64 : 1][RS_EPW][64];
+    __shared__ int32_t or_slot[CERT ? OR_CH : 1];
     const int bq = blockIdx.x;
+    const int rep = CERT ? (int)blockIdx.y : 0;  // replica: only replica 0 writes the selection
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = (int)a.n;
     const int64_t base = (int64_t)bq * a.n;
@@ -852,6 +1123,18 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
                 c++;
             }
     }
+    // the band rescoring's query rows (heads 0 .. 63), in flight from here
+    u32x4 rq[OR_QPT];
+    const int r_nvec = a.dI * (a.rs_f32 ? 4 : 2) / 16;
+    const int r_nqv = (a.HI < 64 ? a.HI : 64) * r_nvec;
+    if constexpr (CERT) {
+        if (a.qI) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.qI) +
+                                                               (size_t)bq * a.HI * a.dI * (a.rs_f32 ? 4 : 2));
+#pragma unroll
+            for (int i = 0; i < OR_QPT; i++) rq[i] = src[min(tid + ONE_NT * i, r_nqv - 1)];
+        }
+    }
     lo = wave_min(lo);
     hi = wave_max(hi);
     km = wave_max(km);
@@ -877,6 +1160,15 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
 #pragma unroll
     for (int i = 0; i < ONE_SPT; i++)
         if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
+    if constexpr (CERT) {
+        if (a.qI) {
+#pragma unroll
+            for (int i = 0; i < OR_QPT; i++) {
+                const int vq = tid + ONE_NT * i;
+                if (vq < r_nqv) or_q[vq / r_nvec][vq % r_nvec] = rq[i];
+            }
+        }
+    }
     __syncthreads();
     // Suffix counts, top bin first: thread t takes bins NB-1-2t and NB-2-2t;
     // an inclusive scan in thread order gives S = the number of scores in bins
@@ -904,6 +1196,8 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     __syncthreads();
 
     const int64_t nwords = (a.n + 31) / 32;
+    uint32_t kw0 = 0, kw1 = 0;  // this thread's band bits, list positions and list sizes per target
+    int32_t kp0 = 0, kp1 = 0, kn0 = 0, kn1 = 0;
     for (int tg = 0; tg < a.ntgt; tg++) {
         const int K = a.K[tg];
         const int bstar = bstar_sh[tg];
@@ -942,55 +1236,64 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
             wbnd |= (x <= f_hi && x >= f_lo2 ? 1u : 0u) << i;
         }
         bm[tid] = win;
-        // band slots: one block-wide counter update per wave, then each lane
-        // writes the slots of its word at its offset within the wave
-        const uint32_t nbw = (uint32_t)__builtin_popcount(wbnd);
-        const uint32_t incl = wave_incl_scan_u32(nbw);
-        const uint32_t wtot = __builtin_amdgcn_readlane(incl, 63);
-        const uint32_t nin = wave_sum_u32((uint32_t)__builtin_popcount(win));
-        int32_t wbase = 0;
-        if (lane == 0) {
-            if (wtot) wbase = atomicAdd(&band_cnt_sh[tg], (int32_t)wtot);
-            if (nin) atomicAdd(&in_cnt_sh[tg], (int32_t)nin);
-        }
-        wbase = __builtin_amdgcn_readlane(wbase, 0);
-        {
-            int32_t pos = wbase + (int32_t)(incl - nbw);
-            for (uint32_t m = wbnd; m; m &= m - 1) band[pos++] = s0 + __builtin_ctz(m);
-        }
-        __syncthreads();
-        const int32_t in_cnt = in_cnt_sh[tg];
-        const int32_t nb = band_cnt_sh[tg];
         if constexpr (CERT) {
-            uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
-            for (int64_t wd = tid; wd < nwords; wd += ONE_NT) gbm[wd] = bm[wd];
-            if (tg == 0 && a.in_list) {
-                // the IN entries in slot order: thread tid's word at the prefix of the popcounts
-                const uint32_t c = (uint32_t)__builtin_popcount(win);
-                const uint32_t inc = wave_incl_scan_u32(c);
-                if (lane == 63) red[wave] = inc;
-                __syncthreads();
-                uint32_t pos = inc - c;
-#pragma unroll
-                for (int i = 0; i < ONE_NT / 64; i++) pos += i < wave ? red[i] : 0u;
-                int32_t *il = a.in_list + (size_t)bq * K;
-                for (uint32_t m = win; m; m &= m - 1) {
-                    const int sl = s0 + __builtin_ctz(m);
-                    il[pos++] = cp ? cp[sl] : sl;
+            // list positions and counts by one block scan of the packed word
+            // counts (band in the low half, IN in the high half: each total
+            // is at most 32,768): the band list in slot order, the same in
+            // every replica of the query
+            uint32_t tot = 0;
+            const uint32_t cw = (uint32_t)__builtin_popcount(wbnd) | ((uint32_t)__builtin_popcount(win) << 16);
+            const uint32_t pre = block_excl_scan_u32<ONE_NT>(cw, red, tot);
+            const int32_t bpos = (int32_t)(pre & 0xffffu), ipos = (int32_t)(pre >> 16);
+            const int32_t nb = (int32_t)(tot & 0xffffu), in_cnt = (int32_t)(tot >> 16);
+            if (tg == 0) kw0 = wbnd, kp0 = bpos, kn0 = nb;
+            else kw1 = wbnd, kp1 = bpos, kn1 = nb;
+            if (rep == 0) {
+                int32_t pos = bpos;
+                for (uint32_t m = wbnd; m; m &= m - 1) band[pos++] = s0 + __builtin_ctz(m);
+                uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
+                if (tid < nwords) gbm[tid] = win;
+                if (tg == 0 && a.in_list) {
+                    // the IN entries in slot order
+                    int32_t *il = a.in_list + (size_t)bq * K;
+                    int32_t p2 = ipos;
+                    for (uint32_t m = win; m; m &= m - 1) {
+                        const int sl = s0 + __builtin_ctz(m);
+                        il[p2++] = cp ? cp[sl] : sl;
+                    }
+                }
+                if (tid == 0) {
+                    SelTarget t;
+                    t.lo = tlo;
+                    t.hi = thi;
+                    t.K = K;
+                    t.in_cnt = in_cnt;
+                    t.band_cnt = nb;
+                    t.pad = 0;
+                    a.sq[bq].t[tg] = t;
+                    if (tg == 0) a.sq[bq].nvalid = (int32_t)nvalid;
                 }
             }
-            if (tid == 0) {
-                SelTarget t;
-                t.lo = tlo;
-                t.hi = thi;
-                t.K = K;
-                t.in_cnt = in_cnt;
-                t.band_cnt = nb;
-                t.pad = 0;
-                a.sq[bq].t[tg] = t;
-                if (tg == 0) a.sq[bq].nvalid = (int32_t)nvalid;
-            }
         } else {
+            // band slots: one block-wide counter update per wave, then each lane
+            // writes the slots of its word at its offset within the wave
+            const uint32_t nbw = (uint32_t)__builtin_popcount(wbnd);
+            const uint32_t incl = wave_incl_scan_u32(nbw);
+            const uint32_t wtot = __builtin_amdgcn_readlane(incl, 63);
+            const uint32_t nin = wave_sum_u32((uint32_t)__builtin_popcount(win));
+            int32_t wbase = 0;
+            if (lane == 0) {
+                if (wtot) wbase = atomicAdd(&band_cnt_sh[tg], (int32_t)wtot);
+                if (nin) atomicAdd(&in_cnt_sh[tg], (int32_t)nin);
+            }
+            wbase = __builtin_amdgcn_readlane(wbase, 0);
+            {
+                int32_t pos = wbase + (int32_t)(incl - nbw);
+                for (uint32_t m = wbnd; m; m &= m - 1) band[pos++] = s0 + __builtin_ctz(m);
+            }
+            __syncthreads();
+            const int32_t in_cnt = in_cnt_sh[tg];
+            const int32_t nb = band_cnt_sh[tg];
             __threadfence_block();
             __syncthreads();
             int32_t *dst = (tg == 0 ? a.out0 : a.out1) + (size_t)bq * K;
@@ -1000,53 +1303,16 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
         }
         __syncthreads();
     }
-}
-
-// ----------------------------------------------------------------- rescore
-// One wave per BAND entry (both targets' lists back to back), no staging:
-// lane h loads query head h's row and the key row (the same address in every
-// lane) with 16-byte loads into registers, and computes head h's dot product
-// in the definition's order d = 0, 1, ... (products of bf16/fp32 inputs are
-// exact in binary64, so fma = rounded product + add); t_h = w_h * ReLU(d_h)
-// is rounded on its own, and lane 0 sums t_0, t_1, ... from +0.0 out of LDS.
-// Idle blocks exit at once.
-constexpr int RS_NT = 256;
-constexpr int RS_VB = 16;      // 16-byte vectors per row batch
-
-struct RescoreKArgs {
-    const void *qI;
-    int dt;
-    int kfp4;  // key rows in FP4 (queries bf16)
-    const float *w;
-    const void *kI;
-    int Q, HI, dI;
-    int64_t N;
-    const int32_t *cand;
-    int64_t n;
-    int ntgt;
-    const SelQuery *sq;
-    const int32_t *band;
-    double *band_score;
-    int64_t band_cap;
-    int bf16key;  // store the scores rounded to bfloat16 (the ranked value)
-};
-
-// Running binary64 dot over one 16-byte vector of each row.
-template <bool F32>
-__device__ __forceinline__ double dot_vec(double acc, u32x4 q, u32x4 k) {
-#pragma clang fp contract(off)
-    if constexpr (F32) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) acc = __builtin_fma((double)__uint_as_float(q[e]), (double)__uint_as_float(k[e]), acc);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            acc = __builtin_fma((double)__uint_as_float(q[e] << 16), (double)__uint_as_float(k[e] << 16), acc);
-            acc = __builtin_fma((double)__uint_as_float(q[e] & 0xffff0000u), (double)__uint_as_float(k[e] & 0xffff0000u),
-                                acc);
+    if constexpr (CERT) {
+        if (a.qI) {
+            if (a.rs_f32)
+                one_rescore<true>(a, bq, rep, (int)gridDim.y, s0, kw0, kw1, kp0, kp1, kn0, kn1, or_slot, or_krow,
+                                  or_q, or_tl);
+            else
+                one_rescore<false>(a, bq, rep, (int)gridDim.y, s0, kw0, kw1, kp0, kp1, kn0, kn1, or_slot, or_krow,
+                                   or_q, or_tl);
         }
     }
-    return acc;
 }
 
 // Rows of at most RS_ROWB bytes: a block takes RS_EPB consecutive band
@@ -1060,19 +1326,12 @@ __device__ __forceinline__ double dot_vec(double acc, u32x4 q, u32x4 k) {
 // lane e sums entry e's head terms in order.  Two entries per wave spread a
 // query's band over about as many waves as the chip has SIMDs.  Blocks loop
 // over the list when it is longer than the grid.
-constexpr int RS_EPW = 2;                       // entries per wave
-constexpr int RS_EPB = RS_EPW * (RS_NT / 64);  // entries per block
-constexpr int RS_ROWB = 512;                    // longest key row staged (bytes)
-constexpr int RS_QCH = 16;                      // query-row vectors per chunk
-constexpr int RS_MAXD = RS_ROWB / 2;            // longest staged row in elements
-
 template <bool F32>
 __global__ __launch_bounds__(RS_NT, 2) void k_sel_rescore(RescoreKArgs a) {
 #pragma clang fp contract(off)
-    constexpr int QS = RS_ROWB / 16 + 1;  // LDS stride of a query row in 16-byte vectors (padded)
     constexpr int QPT = 64 * (RS_ROWB / 16) / RS_NT;
-    __shared__ __attribute__((aligned(16))) double krow_lds[RS_EPB][RS_MAXD];
-    __shared__ u32x4 qsh[64][QS];
+    __shared__ __attribute__((aligned(16))) float krow_lds[RS_EPB][RS_MAXD];
+    __shared__ u32x4 qsh[64][RS_QS];
     __shared__ double tl[RS_NT / 64][RS_EPW][64];
     constexpr int ESZ = F32 ? 4 : 2;
     constexpr int EPV = 16 / ESZ;  // elements per 16-byte vector
@@ -1109,33 +1368,7 @@ __global__ __launch_bounds__(RS_NT, 2) void k_sel_rescore(RescoreKArgs a) {
                                          ? spec
                                          : (e < nb0 ? a.band[row0 + e] : a.band[row1 + (e - nb0)]);
                 const int64_t j = a.cand ? (int64_t)a.cand[(int64_t)bq * a.n + slot] : (int64_t)slot;
-                double *dst = &krow_lds[i][c * EPV];
-                if (!F32 && a.kfp4) {
-                    // 8 channels: 4 code bytes and their E4M3 scale, decoded exactly
-                    const uint8_t *krow = static_cast<const uint8_t *>(a.kI) +
-                                          ((size_t)b * a.N + j) * (size_t)(a.dI / 2 + a.dI / 16);
-                    const uint32_t cw = *reinterpret_cast<const uint32_t *>(krow + 4 * c);
-                    const uint32_t sb = krow[a.dI / 2 + c / 2];
-                    const uint32_t se = (sb >> 3) & 15u, sm = sb & 7u;
-                    double sc = se ? (double)(8u + sm) * __builtin_ldexp(1.0, (int)se - 10) : (double)sm * 0x1p-9;
-                    if ((sb & 0x7fu) == 0x7fu) sc = 448.0;  // the E4M3 NaN code saturates
-                    if (sb & 0x80u) sc = -sc;
-#pragma unroll
-                    for (int x = 0; x < 8; x++) {
-                        const uint32_t cd = (cw >> (4 * x)) & 15u;
-                        const uint32_t ce = (cd >> 1) & 3u, mb = cd & 1u;
-                        const double mag = ce ? (1.0 + 0.5 * mb) * __builtin_ldexp(1.0, (int)ce - 1) : 0.5 * mb;
-                        dst[x] = ((cd & 8u) ? -mag : mag) * sc;
-                    }
-                } else {
-                    const u32x4 kv = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.kI) +
-                                                                     ((size_t)b * a.N + j) * a.dI * ESZ)[c];
-#pragma unroll
-                    for (int x = 0; x < EPV; x++) {
-                        const uint32_t kw = kv[F32 ? x : x >> 1];
-                        dst[x] = (double)__uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
-                    }
-                }
+                rs_stage_piece<F32>(a.kI, a.kfp4, (size_t)b * a.N + j, a.dI, c, &krow_lds[i][c * EPV]);
             }
         }
         if (!q_staged) {
@@ -1148,68 +1381,7 @@ __global__ __launch_bounds__(RS_NT, 2) void k_sel_rescore(RescoreKArgs a) {
         }
         __syncthreads();
         const int ew = wave * RS_EPW;  // this wave's first entry in the block
-        double sc = 0.0;               // lane e < RS_EPW: running score of entry e0 + ew + e
-        for (int h0 = 0; h0 < a.HI; h0 += 64) {
-            const int h = h0 + lane;
-            const int hc = h < a.HI ? h : a.HI - 1;  // idle lanes recompute the last head, unused
-            const u32x4 *qrow = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.qI) +
-                                                                ((size_t)bq * a.HI + hc) * a.dI * ESZ);
-            const double wh = (double)a.w[(size_t)bq * a.HI + hc];
-            double dot[RS_EPW];
-#pragma unroll
-            for (int e = 0; e < RS_EPW; e++) dot[e] = 0.0;
-            for (int v0 = 0; v0 < nvec; v0 += RS_QCH) {
-                u32x4 qv[RS_QCH];
-                if (h0 == 0) {
-#pragma unroll
-                    for (int u = 0; u < RS_QCH; u++)
-                        if (v0 + u < nvec) qv[u] = qsh[lane][v0 + u];
-                } else {
-#pragma unroll
-                    for (int u = 0; u < RS_QCH; u++)
-                        if (v0 + u < nvec) qv[u] = qrow[v0 + u];
-                }
-#pragma unroll
-                for (int u = 0; u < RS_QCH; u++) {
-                    if (v0 + u >= nvec) break;
-#pragma unroll
-                    for (int x = 0; x < EPV; x += 2) {
-                        const uint32_t qw0 = qv[u][F32 ? x : x >> 1];
-                        const uint32_t qw1 = qv[u][F32 ? x + 1 : x >> 1];
-                        const double qd0 = (double)__uint_as_float(F32 ? qw0 : (qw0 << 16));
-                        const double qd1 = (double)__uint_as_float(F32 ? qw1 : (qw1 & 0xffff0000u));
-#pragma unroll
-                        for (int e = 0; e < RS_EPW; e++) {
-                            const double2 k2 = *reinterpret_cast<const double2 *>(&krow_lds[ew + e][(v0 + u) * EPV + x]);
-                            dot[e] = __builtin_fma(qd0, k2.x, dot[e]);
-                            dot[e] = __builtin_fma(qd1, k2.y, dot[e]);
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < RS_EPW; e++) tl[wave][e][lane] = h < a.HI ? wh * (dot[e] > 0.0 ? dot[e] : 0.0) : 0.0;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < RS_EPW) {
-                // head terms t_h0, t_h0+1, ... added in order (read 16 at a time);
-                // lanes past the last head hold +0.0, and sc + 0.0 == sc (sc is
-                // never -0.0: it starts at +0.0 and a round-to-nearest sum is
-                // -0.0 only if both addends are)
-                const int hn = a.HI - h0 < 64 ? a.HI - h0 : 64;
-                for (int c0 = 0; c0 < hn; c0 += 16) {
-                    double tv[16];
-#pragma unroll
-                    for (int i = 0; i < 16; i++) tv[i] = tl[wave][lane][c0 + i];
-#pragma unroll
-                    for (int i = 0; i < 16; i++) sc = sc + tv[i];
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        double sc = rs_wave_scores<F32>(a.qI, a.w, bq, a.HI, a.dI, qsh, krow_lds, ew, tl[wave]);
         const int32_t e = e0 + ew + lane;
         if (a.bf16key) sc = bf16_round_key(sc);
         if (lane < RS_EPW && e < total) {
@@ -1504,6 +1676,19 @@ size_t sel_workspace(const SelPlan &p, bool own_stats) {
 
 
 
+// Replicas of each query's one-block selection that share its band
+// rescoring (0: the rescoring kernel does it): with at most 64 queries, rows
+// the staged rescoring takes (at most RS_ROWB bytes), certified selection.
+static int one_rescore_replicas(const SelPlan &p, const RescoreArgs *rs) {
+    if (!p.certified || !rs || !small_path(p)) return 0;
+    const int rowb = rs->dI * (rs->dt == CSA2_F32 ? 4 : 2);
+    if (rowb > RS_ROWB) return 0;
+    if (p.BQ <= 16) return 16;
+    if (p.BQ <= 32) return 8;
+    if (p.BQ <= 64) return 4;
+    return 0;
+}
+
 void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats_in,
              const RescoreArgs *rs, int32_t *out0, int32_t *count0, int32_t *out1, void *ws, size_t ws_bytes,
              hipStream_t s, SelHandoff *handoff) {
@@ -1546,7 +1731,21 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         a.band_cap = p.band_cap;
         a.in_list = handoff ? in_list : nullptr;
         a.bf16key = p.certified && p.bf16key ? 1 : 0;
-        if (p.certified) hipLaunchKernelGGL(k_sel_one<true>, dim3(p.BQ), dim3(ONE_NT), 0, s, a);
+        // few queries: the band's binary64 rescoring joins this kernel, split
+        // over replicas of each query's block that repeat its selection (the
+        // chip has CUs to spare; one launch and one kernel boundary fewer)
+        const int reps = one_rescore_replicas(p, rs);
+        if (reps) {
+            a.qI = rs->qI;
+            a.rs_f32 = rs->dt == CSA2_F32 ? 1 : 0;
+            a.kfp4 = rs->dt == CSA2_FP4 ? 1 : 0;
+            a.w = rs->w;
+            a.kI = rs->kI;
+            a.Q = rs->Q;
+            a.N = rs->N;
+            a.band_score = band_score;
+        }
+        if (p.certified) hipLaunchKernelGGL(k_sel_one<true>, dim3(p.BQ, reps ? reps : 1), dim3(ONE_NT), 0, s, a);
         else hipLaunchKernelGGL(k_sel_one<false>, dim3(p.BQ), dim3(ONE_NT), 0, s, a);
         check_launch("selection (one block per query)");
         if (!p.certified) return;
@@ -1570,7 +1769,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
                            p.nwords, band, p.band_cap);
         check_launch("selection classify");
     }
-    if (p.certified) {
+    if (p.certified && !(small_path(p) && one_rescore_replicas(p, rs))) {
         RescoreKArgs r{};
         r.qI = rs->qI;
         r.dt = rs->dt;
