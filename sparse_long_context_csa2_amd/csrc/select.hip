@@ -926,7 +926,6 @@ struct OneArgs {
     int64_t nwords;
     int32_t *band;
     int64_t band_cap;
-    int32_t *in_list;  // certified, nullable: target 0's IN entries in ascending order, [BQ][K0]
     int bf16key;       // certified: the ranked value is the score rounded to bfloat16
     // certified, nullable qI: the band's binary64 scores computed here, the
     // band split over the gridDim.y replicas of each query's block (else the
@@ -1237,14 +1236,14 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
         }
         bm[tid] = win;
         if constexpr (CERT) {
-            // list positions and counts by one block scan of the packed word
-            // counts (band in the low half, IN in the high half: each total
-            // is at most 32,768): the band list in slot order, the same in
-            // every replica of the query
+            // band list positions and the counts by one block scan of the
+            // packed word counts (band in the low half, IN in the high half:
+            // each total is at most 32,768): the band list in slot order, the
+            // same in every replica of the query
             uint32_t tot = 0;
             const uint32_t cw = (uint32_t)__builtin_popcount(wbnd) | ((uint32_t)__builtin_popcount(win) << 16);
             const uint32_t pre = block_excl_scan_u32<ONE_NT>(cw, red, tot);
-            const int32_t bpos = (int32_t)(pre & 0xffffu), ipos = (int32_t)(pre >> 16);
+            const int32_t bpos = (int32_t)(pre & 0xffffu);
             const int32_t nb = (int32_t)(tot & 0xffffu), in_cnt = (int32_t)(tot >> 16);
             if (tg == 0) kw0 = wbnd, kp0 = bpos, kn0 = nb;
             else kw1 = wbnd, kp1 = bpos, kn1 = nb;
@@ -1253,15 +1252,6 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
                 for (uint32_t m = wbnd; m; m &= m - 1) band[pos++] = s0 + __builtin_ctz(m);
                 uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
                 if (tid < nwords) gbm[tid] = win;
-                if (tg == 0 && a.in_list) {
-                    // the IN entries in slot order
-                    int32_t *il = a.in_list + (size_t)bq * K;
-                    int32_t p2 = ipos;
-                    for (uint32_t m = win; m; m &= m - 1) {
-                        const int sl = s0 + __builtin_ctz(m);
-                        il[p2++] = cp ? cp[sl] : sl;
-                    }
-                }
                 if (tid == 0) {
                     SelTarget t;
                     t.lo = tlo;
@@ -1670,7 +1660,6 @@ size_t sel_workspace(const SelPlan &p, bool own_stats) {
     c.take<uint32_t>((size_t)p.ntgt * p.BQ * p.nwords);
     c.take<int32_t>((size_t)p.ntgt * p.BQ * p.band_cap);
     if (p.certified) c.take<double>((size_t)p.ntgt * p.BQ * p.band_cap);
-    if (sel_handoff_supported(p)) c.take<int32_t>((size_t)p.BQ * p.K0);  // IN list of the top-k target
     return c.used;
 }
 
@@ -1701,7 +1690,6 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     uint32_t *bitmap = c.take<uint32_t>((size_t)p.ntgt * p.BQ * p.nwords);
     int32_t *band = c.take<int32_t>((size_t)p.ntgt * p.BQ * p.band_cap);
     double *band_score = p.certified ? c.take<double>((size_t)p.ntgt * p.BQ * p.band_cap) : nullptr;
-    int32_t *in_list = sel_handoff_supported(p) ? c.take<int32_t>((size_t)p.BQ * p.K0) : nullptr;
     if (c.used > ws_bytes) throw Error(CSA2_EWORKSPACE, "selection workspace too small");
     if (handoff && !sel_handoff_supported(p)) throw Error(CSA2_EINTERNAL, "selection hand-off not supported");
     if (p.certified && (!rs || !rs->sumwq)) throw Error(CSA2_EINTERNAL, "certified selection needs query norms");
@@ -1729,7 +1717,6 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         a.nwords = p.nwords;
         a.band = band;
         a.band_cap = p.band_cap;
-        a.in_list = handoff ? in_list : nullptr;
         a.bf16key = p.certified && p.bf16key ? 1 : 0;
         // few queries: the band's binary64 rescoring joins this kernel, split
         // over replicas of each query's block that repeat its selection (the
@@ -1809,7 +1796,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     }
     int tg0 = 0;
     if (handoff) {
-        *handoff = SelHandoff{sq, in_list, p.K0, bitmap, p.nwords, band, band_score, p.band_cap, cand, p.n, out0, count0};
+        *handoff = SelHandoff{sq, bitmap, p.nwords, band, band_score, p.band_cap, cand, p.n, out0, count0};
         if (p.ntgt == 1) return;
         tg0 = 1;  // the pool is finished here
     }
