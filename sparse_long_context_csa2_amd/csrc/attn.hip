@@ -249,12 +249,11 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
 
 // ------------------------------------------- selection finish (per block)
 // The certified top-k's last step, finished where the entries are consumed.
-// A query's selected set is its IN entries (certainly kept: the selection
-// kernel's IN bitmap) and the best rr = min(K - |IN|, |BAND|) band entries by
-// (binary64 score descending, slot ascending).  The splits take positions
-// 0 .. |IN| - 1 from the IN slots in slot order (each block scans the bitmap)
-// and |IN| .. |IN| + rr - 1 from the chosen band entries in slot order; so
-// only the blocks whose split
+// A query's selected set is its IN entries (certainly kept, in ascending
+// order from the selection kernel) and the best rr = min(K - |IN|, |BAND|)
+// band entries by (binary64 score descending, slot ascending).  The splits
+// take positions 0 .. |IN| - 1 from the IN list and |IN| .. |IN| + rr - 1 from
+// the chosen band entries in slot order; so only the blocks whose split
 // reaches past |IN| (usually one per query) rank the band, and one block per
 // query (the split holding position |IN|) writes the ascending index list:
 // the IN bitmap with the chosen band bits set, compacted.  Nothing crosses
@@ -577,37 +576,11 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_split(const uint16_t *__re
         const int nw = (int)sel.nwords;
         const uint32_t *inbm = sel.bitmap + (size_t)bq * sel.nwords;
 #pragma unroll
-        for (int u = 0; u < SPW; u++) inw[u] = tid * SPW + u < nw ? inbm[tid * SPW + u] : 0u;
-        // this split's IN entries: positions e_begin .. of the IN slots in
-        // slot order (thread t holds bitmap words t SPW ..), the rest -1
-        for (int e = tid; e < ROWS; e += NT) jsh[e] = -1;
-        {
-            uint32_t c = 0;
-#pragma unroll
-            for (int u = 0; u < SPW; u++) c += (uint32_t)__builtin_popcount(inw[u]);
-            const uint32_t incl = wave_incl_scan_u32(c);
-            if (lane == 63) sred[wave] = incl;
-            __syncthreads();
-            int32_t pos = (int32_t)(incl - c);
-#pragma unroll
-            for (int i = 0; i < NW; i++) pos += i < wave ? (int32_t)sred[i] : 0;
-            const int32_t p_end = min(e_begin + ne, in_cnt);
-            const int32_t *cq = sel.cand ? sel.cand + (size_t)bq * sel.n : nullptr;
-#pragma unroll
-            for (int u = 0; u < SPW; u++) {
-                const int32_t cu = __builtin_popcount(inw[u]);
-                if (pos < p_end && pos + cu > e_begin) {
-                    for (uint32_t bb = inw[u]; bb; bb &= bb - 1, pos++) {
-                        if (pos >= e_begin && pos < p_end) {
-                            const int32_t sl = (tid * SPW + u) * 32 + __builtin_ctz(bb);
-                            jsh[pos - e_begin] = cq ? cq[sl] : sl;
-                        }
-                    }
-                } else {
-                    pos += cu;
-                }
-            }
-            __syncthreads();  // sred is reused below
+        for (int u = 0; u < SPW; u++) inw[u] = (out_blk && tid * SPW + u < nw) ? inbm[tid * SPW + u] : 0u;
+        const int32_t *il = sel.in_list + (size_t)bq * sel.in_cap;
+        for (int e = tid; e < ROWS; e += NT) {
+            const int p = e_begin + e;
+            jsh[e] = (e < ne && p < in_cnt) ? il[p] : -1;
         }
         const bool band_blk = rr > 0 && e_begin + ne > in_cnt;
         if (band_blk || (out_blk && rr > 0)) {

@@ -34,10 +34,12 @@ struct SelQuery {
 };
 // What a certified selection leaves for its top-k target when the final pick
 // and compaction are left to the consumer (the attention kernel): the IN
-// bitmap, the band list with its binary64 scores, and where the ascending
-// index list and its count go.
+// entries in ascending order, the IN bitmap, the band list with its binary64
+// scores, and where the ascending index list and its count go.
 struct SelHandoff {
     const SelQuery *sq;
+    const int32_t *in_list;  // [BQ][in_cap] IN entries of target 0, ascending
+    int64_t in_cap;
     const uint32_t *bitmap;  // [BQ][nwords] IN bits of target 0
     int64_t nwords;
     const int32_t *band;     // [BQ][band_cap] band slots of target 0

@@ -792,12 +792,11 @@ constexpr int RS_MAXD = RS_ROWB / 2;            // longest staged row in element
 constexpr int RS_QS = RS_ROWB / 16 + 1;        // LDS stride of a staged query row in 16-byte vectors (padded)
 
 
-// Piece c of key row `row` as fp32 values, exactly: 16 bytes of bf16 or fp32
-// values, or (FP4 rows) 8 channels from 4 code bytes and their E4M3 scale
-// byte (a code times a scale has at most 7 significant bits, within fp32's
-// range).  The dot products widen them to binary64.
+// Piece c of key row `row` as exact binary64 values: 16 bytes of bf16 or
+// fp32 values, or (FP4 rows) 8 channels from 4 code bytes and their E4M3
+// scale byte.
 template <bool F32>
-__device__ __forceinline__ void rs_stage_piece(const void *kI, int kfp4, size_t row, int dI, int c, float *dst) {
+__device__ __forceinline__ void rs_stage_piece(const void *kI, int kfp4, size_t row, int dI, int c, double *dst) {
     constexpr int ESZ = F32 ? 4 : 2;
     constexpr int EPV = 16 / ESZ;  // elements per 16-byte vector
     if (!F32 && kfp4) {
@@ -813,33 +812,33 @@ __device__ __forceinline__ void rs_stage_piece(const void *kI, int kfp4, size_t 
             const uint32_t cd = (cw >> (4 * x)) & 15u;
             const uint32_t ce = (cd >> 1) & 3u, mb = cd & 1u;
             const double mag = ce ? (1.0 + 0.5 * mb) * __builtin_ldexp(1.0, (int)ce - 1) : 0.5 * mb;
-            dst[x] = (float)(((cd & 8u) ? -mag : mag) * sc);
+            dst[x] = ((cd & 8u) ? -mag : mag) * sc;
         }
     } else {
         const u32x4 kv = reinterpret_cast<const u32x4 *>(static_cast<const char *>(kI) + row * dI * ESZ)[c];
 #pragma unroll
         for (int x = 0; x < EPV; x++) {
             const uint32_t kw = kv[F32 ? x : x >> 1];
-            dst[x] = __uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
+            dst[x] = (double)__uint_as_float(F32 ? kw : ((x & 1) ? (kw & 0xffff0000u) : (kw << 16)));
         }
     }
 }
 
 // Binary64 scores of the staged entries ew .. ew + RS_EPW - 1 of query bq
-// (their key rows in krow as fp32, the first 64 heads' query rows in
+// (their key rows in krow as binary64, the first 64 heads' query rows in
 // qsh; heads past 64 read from memory): lane h runs head h's dot products
 // of the RS_EPW entries as independent chains in the definition's order
 // d = 0, 1, ..., t_h = w_h * ReLU(d_h) goes through the wave's LDS rows tl,
 // and lane e < RS_EPW sums entry e's terms in head order from +0.0.
 // Returns lane e's score (not rounded to a key), 0 in the other lanes.
-template <bool F32>
+// QCH query vectors are held at a time.
+template <bool F32, int QCH = 16>
 __device__ double rs_wave_scores(const void *qI, const float *w, int bq, int HI, int dI,
-                                 const u32x4 (*qsh)[RS_QS], const float (*krow_lds)[RS_MAXD], int ew,
+                                 const u32x4 (*qsh)[RS_QS], const double (*krow_lds)[RS_MAXD], int ew,
                                  double (*tl)[64]) {
 #pragma clang fp contract(off)
     constexpr int ESZ = F32 ? 4 : 2;
     constexpr int EPV = 16 / ESZ;
-    constexpr int KF = EPV / 4;  // fp32 key vectors per 16-byte query vector
     const int lane = threadIdx.x & 63;
     const int nvec = dI * ESZ / 16;
     double sc = 0.0;  // lane e < RS_EPW: running score of entry ew + e
@@ -852,34 +851,34 @@ __device__ double rs_wave_scores(const void *qI, const float *w, int bq, int HI,
         double dot[RS_EPW];
 #pragma unroll
         for (int e = 0; e < RS_EPW; e++) dot[e] = 0.0;
-        // vector u's query values and the entries' key values, one vector
-        // ahead of the multiply-adds (two register sets, so that the LDS
-        // reads of the next vector are in flight while this one is used)
-        u32x4 qa, qb;
-        f32x4 ka[RS_EPW][KF], kb[RS_EPW][KF];
-        auto load = [&](int u, u32x4 &qq, f32x4 (&kk)[RS_EPW][KF]) {
-            qq = h0 == 0 ? qsh[lane][u] : qrow[u];
+        for (int v0 = 0; v0 < nvec; v0 += QCH) {
+            u32x4 qv[QCH];
+            if (h0 == 0) {
 #pragma unroll
-            for (int e = 0; e < RS_EPW; e++)
+                for (int u = 0; u < QCH; u++)
+                    if (v0 + u < nvec) qv[u] = qsh[lane][v0 + u];
+            } else {
 #pragma unroll
-                for (int x = 0; x < KF; x++) kk[e][x] = *reinterpret_cast<const f32x4 *>(&krow_lds[ew + e][u * EPV + 4 * x]);
-        };
-        auto step = [&](const u32x4 &qq, const f32x4 (&kk)[RS_EPW][KF]) {
-#pragma unroll
-            for (int i = 0; i < EPV; i++) {
-                const uint32_t qw = qq[F32 ? i : i >> 1];
-                const double qd = (double)__uint_as_float(F32 ? qw : ((i & 1) ? (qw & 0xffff0000u) : (qw << 16)));
-#pragma unroll
-                for (int e = 0; e < RS_EPW; e++) dot[e] = __builtin_fma(qd, (double)kk[e][i >> 2][i & 3], dot[e]);
+                for (int u = 0; u < QCH; u++)
+                    if (v0 + u < nvec) qv[u] = qrow[v0 + u];
             }
-        };
-        load(0, qa, ka);
-        for (int u = 0; u < nvec; u += 2) {
-            if (u + 1 < nvec) load(u + 1, qb, kb);
-            step(qa, ka);
-            if (u + 1 >= nvec) break;
-            if (u + 2 < nvec) load(u + 2, qa, ka);
-            step(qb, kb);
+#pragma unroll
+            for (int u = 0; u < QCH; u++) {
+                if (v0 + u >= nvec) break;
+#pragma unroll
+                for (int x = 0; x < EPV; x += 2) {
+                    const uint32_t qw0 = qv[u][F32 ? x : x >> 1];
+                    const uint32_t qw1 = qv[u][F32 ? x + 1 : x >> 1];
+                    const double qd0 = (double)__uint_as_float(F32 ? qw0 : (qw0 << 16));
+                    const double qd1 = (double)__uint_as_float(F32 ? qw1 : (qw1 & 0xffff0000u));
+#pragma unroll
+                    for (int e = 0; e < RS_EPW; e++) {
+                        const double2 k2 = *reinterpret_cast<const double2 *>(&krow_lds[ew + e][(v0 + u) * EPV + x]);
+                        dot[e] = __builtin_fma(qd0, k2.x, dot[e]);
+                        dot[e] = __builtin_fma(qd1, k2.y, dot[e]);
+                    }
+                }
+            }
         }
 #pragma unroll
         for (int e = 0; e < RS_EPW; e++) tl[e][lane] = h < HI ? wh * (dot[e] > 0.0 ? dot[e] : 0.0) : 0.0;
@@ -926,6 +925,7 @@ struct OneArgs {
     int64_t nwords;
     int32_t *band;
     int64_t band_cap;
+    int32_t *in_list;  // certified, nullable: target 0's IN entries in ascending order, [BQ][K0]
     int bf16key;       // certified: the ranked value is the score rounded to bfloat16
     // certified, nullable qI: the band's binary64 scores computed here, the
     // band split over the gridDim.y replicas of each query's block (else the
@@ -973,7 +973,7 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t c, uint32_t *re
 template <bool F32>
 __device__ void one_rescore(const OneArgs &a, int bq, int rep, int nrep, int s0, uint32_t kw0, uint32_t kw1,
                             int32_t kp0, int32_t kp1, int32_t nb0, int32_t nb1, int32_t *slots,
-                            float (*krow)[RS_MAXD], u32x4 (*qsh)[RS_QS], double (*tl)[RS_EPW][64]) {
+                            double (*krow)[RS_MAXD], u32x4 (*qsh)[RS_QS], double (*tl)[RS_EPW][64]) {
     constexpr int ESZ = F32 ? 4 : 2;
     constexpr int EPV = 16 / ESZ;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1010,7 +1010,7 @@ __device__ void one_rescore(const OneArgs &a, int bq, int rep, int nrep, int s0,
         __syncthreads();
         const int ew = wave * RS_EPW;
         if (ew < cnt) {
-            double sc = rs_wave_scores<F32>(a.qI, a.w, bq, a.HI, a.dI, qsh, krow, ew, tl[wave]);
+            double sc = rs_wave_scores<F32, 4>(a.qI, a.w, bq, a.HI, a.dI, qsh, krow, ew, tl[wave]);
             const int32_t e = rep + nrep * (i0 + ew + lane);
             if (a.bf16key) sc = bf16_round_key(sc);
             if (lane < RS_EPW && ew + lane < cnt) {
@@ -1053,7 +1053,7 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     __shared__ int32_t slot_lds[CERT ? 1 : BANDFAST];
     __shared__ int32_t out_lds[CERT ? 1 : ONE_OUT];
     // certified band rescoring (a.qI set): chunks of the band, query rows, head terms
-    __shared__ __attribute__((aligned(16))) float or_krow[CERT ? OR_CH : 1][RS_MAXD];
+    __shared__ __attribute__((aligned(16))) double or_krow[CERT ? OR_CH : 1][RS_MAXD];
     __shared__ u32x4 or_q[CERT ? 64 : 1][RS_QS];
     __shared__ double or_tl[CERT ? ONE_NT / 64 : 1][RS_EPW][64];
     __shared__ int32_t or_slot[CERT ? OR_CH : 1];
@@ -1236,14 +1236,14 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
         }
         bm[tid] = win;
         if constexpr (CERT) {
-            // band list positions and the counts by one block scan of the
-            // packed word counts (band in the low half, IN in the high half:
-            // each total is at most 32,768): the band list in slot order, the
-            // same in every replica of the query
+            // list positions and counts by one block scan of the packed word
+            // counts (band in the low half, IN in the high half: each total
+            // is at most 32,768): the band list in slot order, the same in
+            // every replica of the query
             uint32_t tot = 0;
             const uint32_t cw = (uint32_t)__builtin_popcount(wbnd) | ((uint32_t)__builtin_popcount(win) << 16);
             const uint32_t pre = block_excl_scan_u32<ONE_NT>(cw, red, tot);
-            const int32_t bpos = (int32_t)(pre & 0xffffu);
+            const int32_t bpos = (int32_t)(pre & 0xffffu), ipos = (int32_t)(pre >> 16);
             const int32_t nb = (int32_t)(tot & 0xffffu), in_cnt = (int32_t)(tot >> 16);
             if (tg == 0) kw0 = wbnd, kp0 = bpos, kn0 = nb;
             else kw1 = wbnd, kp1 = bpos, kn1 = nb;
@@ -1252,6 +1252,15 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
                 for (uint32_t m = wbnd; m; m &= m - 1) band[pos++] = s0 + __builtin_ctz(m);
                 uint32_t *gbm = a.bitmap + ((size_t)tg * gridDim.x + bq) * a.nwords;
                 if (tid < nwords) gbm[tid] = win;
+                if (tg == 0 && a.in_list) {
+                    // the IN entries in slot order
+                    int32_t *il = a.in_list + (size_t)bq * K;
+                    int32_t p2 = ipos;
+                    for (uint32_t m = win; m; m &= m - 1) {
+                        const int sl = s0 + __builtin_ctz(m);
+                        il[p2++] = cp ? cp[sl] : sl;
+                    }
+                }
                 if (tid == 0) {
                     SelTarget t;
                     t.lo = tlo;
@@ -1320,7 +1329,7 @@ template <bool F32>
 __global__ __launch_bounds__(RS_NT, 2) void k_sel_rescore(RescoreKArgs a) {
 #pragma clang fp contract(off)
     constexpr int QPT = 64 * (RS_ROWB / 16) / RS_NT;
-    __shared__ __attribute__((aligned(16))) float krow_lds[RS_EPB][RS_MAXD];
+    __shared__ __attribute__((aligned(16))) double krow_lds[RS_EPB][RS_MAXD];
     __shared__ u32x4 qsh[64][RS_QS];
     __shared__ double tl[RS_NT / 64][RS_EPW][64];
     constexpr int ESZ = F32 ? 4 : 2;
@@ -1660,6 +1669,7 @@ size_t sel_workspace(const SelPlan &p, bool own_stats) {
     c.take<uint32_t>((size_t)p.ntgt * p.BQ * p.nwords);
     c.take<int32_t>((size_t)p.ntgt * p.BQ * p.band_cap);
     if (p.certified) c.take<double>((size_t)p.ntgt * p.BQ * p.band_cap);
+    if (sel_handoff_supported(p)) c.take<int32_t>((size_t)p.BQ * p.K0);  // IN list of the top-k target
     return c.used;
 }
 
@@ -1690,6 +1700,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     uint32_t *bitmap = c.take<uint32_t>((size_t)p.ntgt * p.BQ * p.nwords);
     int32_t *band = c.take<int32_t>((size_t)p.ntgt * p.BQ * p.band_cap);
     double *band_score = p.certified ? c.take<double>((size_t)p.ntgt * p.BQ * p.band_cap) : nullptr;
+    int32_t *in_list = sel_handoff_supported(p) ? c.take<int32_t>((size_t)p.BQ * p.K0) : nullptr;
     if (c.used > ws_bytes) throw Error(CSA2_EWORKSPACE, "selection workspace too small");
     if (handoff && !sel_handoff_supported(p)) throw Error(CSA2_EINTERNAL, "selection hand-off not supported");
     if (p.certified && (!rs || !rs->sumwq)) throw Error(CSA2_EINTERNAL, "certified selection needs query norms");
@@ -1717,6 +1728,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
         a.nwords = p.nwords;
         a.band = band;
         a.band_cap = p.band_cap;
+        a.in_list = handoff ? in_list : nullptr;
         a.bf16key = p.certified && p.bf16key ? 1 : 0;
         // few queries: the band's binary64 rescoring joins this kernel, split
         // over replicas of each query's block that repeat its selection (the
@@ -1796,7 +1808,7 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
     }
     int tg0 = 0;
     if (handoff) {
-        *handoff = SelHandoff{sq, bitmap, p.nwords, band, band_score, p.band_cap, cand, p.n, out0, count0};
+        *handoff = SelHandoff{sq, in_list, p.K0, bitmap, p.nwords, band, band_score, p.band_cap, cand, p.n, out0, count0};
         if (p.ntgt == 1) return;
         tg0 = 1;  // the pool is finished here
     }
