@@ -962,48 +962,43 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t c, uint32_t *re
     return pre + inc - c;
 }
 
-// The band rescoring inside the one-block selection.  Every replica of a
-// query's block classified the same slots, so each holds the same band lists
-// (target 0's, then target 1's, each in slot order); entry e is rescored by
-// replica e mod R, in rounds of OR_CH of its entries.  Each thread places its
-// own band slots that fall in the round, the round's key rows are staged in
-// LDS as binary64, and each wave computes RS_EPW entries' scores in the
-// definition's order (rs_wave_scores), as the rescoring kernel does.  The
-// first 64 heads' query rows are in qsh already.
+// The band rescoring inside the one-block selection, with ONE_NT / 64
+// replicas of each query's block: every replica classified the same slots,
+// so each holds the same band lists (target 0's, then target 1's, each in
+// slot order, at positions from the block scan).  Replica r rescores the
+// band entries of wave r's words (2048 slots): the wave lists them in LDS
+// (slot, target, position) by a wave scan, the key rows are staged in LDS as
+// binary64 OR_CH at a time, and each wave computes RS_EPW entries' scores in
+// the definition's order (rs_wave_scores), as the rescoring kernel does.
+// The first 64 heads' query rows are in qsh already.
 template <bool F32>
-__device__ void one_rescore(const OneArgs &a, int bq, int rep, int nrep, int s0, uint32_t kw0, uint32_t kw1,
-                            int32_t kp0, int32_t kp1, int32_t nb0, int32_t nb1, int32_t *slots,
-                            double (*krow)[RS_MAXD], u32x4 (*qsh)[RS_QS], double (*tl)[RS_EPW][64]) {
+__device__ void one_rescore(const OneArgs &a, int bq, int rep, int s0, uint32_t kw0, uint32_t kw1, int32_t kp0,
+                            int32_t kp1, uint32_t *ents, int32_t *nent_sh, double (*krow)[RS_MAXD],
+                            u32x4 (*qsh)[RS_QS], double (*tl)[RS_EPW][64]) {
     constexpr int ESZ = F32 ? 4 : 2;
     constexpr int EPV = 16 / ESZ;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = bq / a.Q;
     const int nvec = a.dI * ESZ / 16;
-    const int32_t total = nb0 + nb1;
-    const int32_t mine = total > rep ? (total - rep + nrep - 1) / nrep : 0;  // entries rep, rep + R, ...
-    if (mine == 0) return;
     const size_t row0 = (size_t)bq * a.band_cap, row1 = ((size_t)gridDim.x + bq) * a.band_cap;
-    for (int32_t i0 = 0; i0 < mine; i0 += OR_CH) {
-        // entries rep + R (i0 + x), x < OR_CH: slots[x]
-        const int32_t e_lo = rep + nrep * i0, e_hi = rep + nrep * (i0 + OR_CH);  // their range [e_lo, e_hi)
-        for (int tg = 0; tg < 2; tg++) {
-            const uint32_t kw = tg == 0 ? kw0 : kw1;
-            int32_t e = tg == 0 ? kp0 : nb0 + kp1;
-            if (kw && e < e_hi && e + __builtin_popcount(kw) > e_lo) {
-                // e = rep + nrep * qd + r, stepped with e
-                int32_t qd = e >= rep ? (e - rep) / nrep : -((rep - e + nrep - 1) / nrep);
-                int32_t r = e - rep - qd * nrep;
-                for (uint32_t m = kw; m; m &= m - 1) {
-                    if (r == 0 && qd >= i0 && qd < i0 + OR_CH) slots[qd - i0] = s0 + __builtin_ctz(m);
-                    if (++r == nrep) r = 0, qd++;
-                }
-            }
-        }
-        __syncthreads();
-        const int cnt = mine - i0 < OR_CH ? mine - i0 : OR_CH;  // entries this round
+    if (wave == rep) {
+        // entry: slot | target << 15 | position << 16 (slots and positions < 32,768)
+        const uint32_t c0 = (uint32_t)__builtin_popcount(kw0), c1 = (uint32_t)__builtin_popcount(kw1);
+        const uint32_t incl = wave_incl_scan_u32(c0 + c1);
+        uint32_t o = incl - c0 - c1;
+        int32_t p0 = kp0, p1 = kp1;
+        for (uint32_t m = kw0; m; m &= m - 1) ents[o++] = (uint32_t)(s0 + __builtin_ctz(m)) | ((uint32_t)p0++ << 16);
+        for (uint32_t m = kw1; m; m &= m - 1)
+            ents[o++] = (uint32_t)(s0 + __builtin_ctz(m)) | (1u << 15) | ((uint32_t)p1++ << 16);
+        if (lane == 63) *nent_sh = (int32_t)incl;
+    }
+    __syncthreads();
+    const int32_t nent = *nent_sh;
+    for (int32_t i0 = 0; i0 < nent; i0 += OR_CH) {
+        const int cnt = nent - i0 < OR_CH ? nent - i0 : OR_CH;  // entries this round
         for (int q = tid; q < cnt * nvec; q += ONE_NT) {
             const int i = q / nvec, c = q - i * nvec;
-            const int32_t slot = slots[i];
+            const int32_t slot = (int32_t)(ents[i0 + i] & 0x7fffu);
             const int64_t j = a.cand ? (int64_t)a.cand[(int64_t)bq * a.n + slot] : (int64_t)slot;
             rs_stage_piece<F32>(a.kI, a.kfp4, (size_t)b * a.N + j, a.dI, c, &krow[i][c * EPV]);
         }
@@ -1011,11 +1006,10 @@ __device__ void one_rescore(const OneArgs &a, int bq, int rep, int nrep, int s0,
         const int ew = wave * RS_EPW;
         if (ew < cnt) {
             double sc = rs_wave_scores<F32, 4>(a.qI, a.w, bq, a.HI, a.dI, qsh, krow, ew, tl[wave]);
-            const int32_t e = rep + nrep * (i0 + ew + lane);
             if (a.bf16key) sc = bf16_round_key(sc);
             if (lane < RS_EPW && ew + lane < cnt) {
-                if (e < nb0) a.band_score[row0 + e] = sc;
-                else a.band_score[row1 + (e - nb0)] = sc;
+                const uint32_t e = ents[i0 + ew + lane];
+                a.band_score[((e >> 15) & 1u ? row1 : row0) + (e >> 16)] = sc;
             }
         }
         __syncthreads();  // the staged rows are replaced next round
@@ -1056,7 +1050,8 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     __shared__ __attribute__((aligned(16))) double or_krow[CERT ? OR_CH : 1][RS_MAXD];
     __shared__ u32x4 or_q[CERT ? 64 : 1][RS_QS];
     __shared__ double or_tl[CERT ? ONE_NT / 64 : 1][RS_EPW][64];
-    __shared__ int32_t or_slot[CERT ? OR_CH : 1];
+    __shared__ uint32_t or_ents[CERT ? 2 * ONE_N / (ONE_NT / 64) : 1];  // a replica's band entries
+    __shared__ int32_t or_nent;
     const int bq = blockIdx.x;
     const int rep = CERT ? (int)blockIdx.y : 0;  // replica: only replica 0 writes the selection
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1195,8 +1190,8 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     __syncthreads();
 
     const int64_t nwords = (a.n + 31) / 32;
-    uint32_t kw0 = 0, kw1 = 0;  // this thread's band bits, list positions and list sizes per target
-    int32_t kp0 = 0, kp1 = 0, kn0 = 0, kn1 = 0;
+    uint32_t kw0 = 0, kw1 = 0;  // this thread's band bits and their first list positions per target
+    int32_t kp0 = 0, kp1 = 0;
     for (int tg = 0; tg < a.ntgt; tg++) {
         const int K = a.K[tg];
         const int bstar = bstar_sh[tg];
@@ -1245,8 +1240,8 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
             const uint32_t pre = block_excl_scan_u32<ONE_NT>(cw, red, tot);
             const int32_t bpos = (int32_t)(pre & 0xffffu), ipos = (int32_t)(pre >> 16);
             const int32_t nb = (int32_t)(tot & 0xffffu), in_cnt = (int32_t)(tot >> 16);
-            if (tg == 0) kw0 = wbnd, kp0 = bpos, kn0 = nb;
-            else kw1 = wbnd, kp1 = bpos, kn1 = nb;
+            if (tg == 0) kw0 = wbnd, kp0 = bpos;
+            else kw1 = wbnd, kp1 = bpos;
             if (rep == 0) {
                 int32_t pos = bpos;
                 for (uint32_t m = wbnd; m; m &= m - 1) band[pos++] = s0 + __builtin_ctz(m);
@@ -1305,11 +1300,9 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     if constexpr (CERT) {
         if (a.qI) {
             if (a.rs_f32)
-                one_rescore<true>(a, bq, rep, (int)gridDim.y, s0, kw0, kw1, kp0, kp1, kn0, kn1, or_slot, or_krow,
-                                  or_q, or_tl);
+                one_rescore<true>(a, bq, rep, s0, kw0, kw1, kp0, kp1, or_ents, &or_nent, or_krow, or_q, or_tl);
             else
-                one_rescore<false>(a, bq, rep, (int)gridDim.y, s0, kw0, kw1, kp0, kp1, kn0, kn1, or_slot, or_krow,
-                                   or_q, or_tl);
+                one_rescore<false>(a, bq, rep, s0, kw0, kw1, kp0, kp1, or_ents, &or_nent, or_krow, or_q, or_tl);
         }
     }
 }
@@ -1676,16 +1669,14 @@ size_t sel_workspace(const SelPlan &p, bool own_stats) {
 
 
 // Replicas of each query's one-block selection that share its band
-// rescoring (0: the rescoring kernel does it): with at most 64 queries, rows
-// the staged rescoring takes (at most RS_ROWB bytes), certified selection.
+// rescoring (0: the rescoring kernel does it): one per wave of the block
+// (replica r takes wave r's words) with at most 16 queries, rows the staged
+// rescoring takes (at most RS_ROWB bytes), certified selection.
 static int one_rescore_replicas(const SelPlan &p, const RescoreArgs *rs) {
     if (!p.certified || !rs || !small_path(p)) return 0;
     const int rowb = rs->dI * (rs->dt == CSA2_F32 ? 4 : 2);
     if (rowb > RS_ROWB) return 0;
-    if (p.BQ <= 16) return 16;
-    if (p.BQ <= 32) return 8;
-    if (p.BQ <= 64) return 4;
-    return 0;
+    return p.BQ <= 16 ? ONE_NT / 64 : 0;
 }
 
 void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats_in,
