@@ -6,6 +6,12 @@ import oracle
 
 ATOL_BF16, RTOL_BF16 = 1e-2, 2e-2   # bf16 / FP4 attention outputs
 ATOL_F32, RTOL_F32 = 1e-5, 1e-5     # fp32 configuration
+# lse = m + ln l of bf16 / FP4 attention: no bf16 rounding on its path, only
+# fp32 arithmetic (the logits' fp32 accumulation over D channels of exact
+# products, then the fp32 sum and logarithm), so its tolerance is an fp32 one:
+# rtol 1e-5 is about 170 fp32 ulps, a random-walk accumulation over 512 terms
+# with a factor 7 to spare; atol covers lse near 0.
+ATOL_LSE, RTOL_LSE = 1e-4, 1e-5
 
 
 def dev(t):
@@ -75,4 +81,5 @@ def run_group(b, d, q_pos=None):
             assert np.array_equal(host(g["pool"]).numpy(), r["pool"]), f"layer {li}: pool differs"
             g_pool, r_pool = g["pool"], r["pool"]
         assert_close(g["out"], r["out"], atol, rtol, f"layer {li} ({mode}) output")
-        assert_close(g["lse"], r["lse"], atol, rtol, f"layer {li} ({mode}) lse")
+        latol, lrtol = (ATOL_F32, RTOL_F32) if spec.kv_fmt == "f32" else (ATOL_LSE, RTOL_LSE)
+        assert_close(g["lse"], r["lse"], latol, lrtol, f"layer {li} ({mode}) lse")

@@ -21,7 +21,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import ATOL_BF16, RTOL_BF16, assert_close, dev, host, run_group
+from gpu_helpers import ATOL_BF16, ATOL_LSE, RTOL_BF16, RTOL_LSE, assert_close, dev, host, run_group
 from sparse_long_context_csa2_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -58,7 +58,7 @@ def test_decode_128k_benchmark_inputs(b):
     assert np.array_equal(host(L.idx).numpy(), r["idx"])
     assert np.array_equal(host(L.count).numpy(), r["count"])
     assert_close(L.out, r["out"], ATOL_BF16, RTOL_BF16, "output")
-    assert_close(L.lse, r["lse"], ATOL_BF16, RTOL_BF16, "lse")
+    assert_close(L.lse, r["lse"], ATOL_LSE, RTOL_LSE, "lse")
 
 
 def test_decode_128k_fp4_full_plus_five_reuse(b):
@@ -115,7 +115,7 @@ def test_prefill_chunk_sampled_rows(b):
     assert np.array_equal(host(L.idx)[:, rows].numpy(), r["idx"])
     assert np.array_equal(host(L.count)[:, rows].numpy(), r["count"])
     assert_close(host(L.out)[:, rows], r["out"], ATOL_BF16, RTOL_BF16, "prefill output rows")
-    assert_close(host(L.lse)[:, rows], r["lse"], ATOL_BF16, RTOL_BF16, "prefill lse rows")
+    assert_close(host(L.lse)[:, rows], r["lse"], ATOL_LSE, RTOL_LSE, "prefill lse rows")
 
 
 def test_decode_128k_fp4_indexer_keys(b):
@@ -149,4 +149,4 @@ def test_swa_branch_merged_decode_shape(b):
     out, lse = b.swa_attn(qd, dev(swa), dev(pos), W, scale, csa_out=co, csa_lse=cl, out=co)
     torch.cuda.synchronize()
     assert_close(out, ro, ATOL_BF16, RTOL_BF16, "merged out")
-    assert_close(lse, rl, ATOL_BF16, RTOL_BF16, "merged lse")
+    assert_close(lse, rl, ATOL_LSE, RTOL_LSE, "merged lse")

@@ -7,8 +7,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (ATOL_BF16, ATOL_F32, RTOL_BF16, RTOL_F32, assert_close, assert_scores_within_bound, dev,
-                         host)
+from gpu_helpers import (ATOL_BF16, ATOL_F32, ATOL_LSE, RTOL_BF16, RTOL_F32, RTOL_LSE, assert_close,
+                         assert_scores_within_bound, dev, host)
 from sparse_long_context_csa2_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -156,7 +156,7 @@ def test_sparse_attn_matches_oracle(b, B, Q, H, D, N, k, fmt, pad):
     ro, rl = oracle.sparse_attn(q, kv, idx, scale, D=D)
     atol, rtol = (ATOL_F32, RTOL_F32) if fmt == "f32" else (ATOL_BF16, RTOL_BF16)
     assert_close(out, ro, atol, rtol, "attention output")
-    assert_close(lse, rl, atol, rtol, "lse")
+    assert_close(lse, rl, *((ATOL_F32, RTOL_F32) if fmt == "f32" else (ATOL_LSE, RTOL_LSE)), "lse")
 
 
 @pytest.mark.parametrize("e", [24, -24])
@@ -177,7 +177,7 @@ def test_sparse_attn_split_partials_extreme_magnitudes(b, e):
     torch.cuda.synchronize()
     ro, rl = oracle.sparse_attn(q, kv, idx, scale, D=D)
     assert_close(host(out).double() / f, np.asarray(ro) / f, ATOL_BF16, RTOL_BF16, "attention output / 2^e")
-    assert_close(lse, rl, ATOL_BF16, RTOL_BF16, "lse")
+    assert_close(lse, rl, ATOL_LSE, RTOL_LSE, "lse")
 
 
 def test_sparse_attn_empty_rows_and_batch_invariance(b):
