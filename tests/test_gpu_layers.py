@@ -1,8 +1,10 @@
 """Layer-mode parity (FULL / REINDEX / REUSE) of csa2_layer against the oracle:
 index sets and pools bit-exact, outputs within tolerance."""
+import numpy as np
 import pytest
 import torch
 
+import oracle
 from gpu_helpers import dev, host, run_group
 from sparse_long_context_csa2_amd import synth
 
@@ -108,3 +110,29 @@ def test_fp4_indexer_keys_full_pool_reindex(b, N):
     spec = synth.Decode(B=2, Q=1, N=N, HI=64, dI=128, H=64, D=512, k=512, kv_fmt="fp4", P=2048, seed=13,
                         idx_dtype="fp4", layers=["FULL", "REINDEX", "REUSE"])
     run_group(b, synth.make_decode(spec))
+
+
+@pytest.mark.parametrize("score_fmt", ["f64", "bf16"])
+def test_selection_paths_agree_across_batch_sizes(b, score_fmt):
+    """Up to 16 queries the band's binary64 rescoring runs inside the one-block
+    selection kernel (16 replicas of each query's block); with more queries a
+    separate rescoring kernel does it.  17 queries and their first 16 alone
+    must select the same sets and pools, and give the same outputs bit for bit."""
+    spec = synth.Decode(B=17, Q=1, N=6000, HI=64, dI=128, H=64, D=512, k=512, P=1024, seed=21, layers=["FULL"],
+                        score_fmt=score_fmt)
+    d = synth.make_decode(spec)
+    lay = d["layers"][0]
+
+    def run(nb):
+        return b.layer("FULL", q=dev(lay["q"][:nb]), kv=dev(d["kv"][:nb]), k=spec.k, scale=spec.scale,
+                       qI=dev(lay["qI"][:nb]), w=dev(lay["w"][:nb]), kI=dev(d["kI"][:nb]), m=spec.m, P=spec.P,
+                       score_fmt=score_fmt)
+
+    g17, g16 = run(17), run(16)
+    torch.cuda.synchronize()
+    for key in ("idx", "count", "pool", "out", "lse"):
+        assert torch.equal(host(g17[key])[:16], host(g16[key])), key
+    r = oracle.layer("FULL", q=lay["q"], kv=d["kv"], k=spec.k, scale=spec.scale, qI=lay["qI"], w=lay["w"], kI=d["kI"],
+                     m=spec.m, P=spec.P, score_key=score_fmt)
+    assert np.array_equal(host(g17["idx"]).numpy(), r["idx"])
+    assert np.array_equal(host(g17["pool"]).numpy(), r["pool"])
