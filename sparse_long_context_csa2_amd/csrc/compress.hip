@@ -100,16 +100,20 @@ __global__ __launch_bounds__(256) void k_compress_pool(const void *__restrict__ 
 // ---------------------------------------------------- bf16: matrix cores
 // For bf16 rows the projection runs on the matrix cores and the pooling is
 // fused behind it, so Z never goes through memory.  Block = EPB = 64 / m
-// consecutive entries x 64 channels; it needs the token rows of their
-// windows, first(e0) .. first(e0) + (EPB + 1) m - 1 (at most 80), and
-// computes Z for 80 rows from there: wave w takes channels c0 + 16 w ..
-// + 15, its W^T fragments for all D held in registers (from a transposed copy
-// of W), the 5 row tiles' X fragments read per 32-deep step.  Each Z element
-// is one matrix-core dot product over d in a fixed order, whatever the
-// block, so an entry comes out bitwise the same from a chunk with a halo as
-// from the whole context.  Z goes to LDS; then each thread pools entries
-// for its channels as the fp32 kernel does.
+// consecutive entries x 128 channels (eight waves); it needs the token rows
+// of their windows, first(e0) .. first(e0) + (EPB + 1) m - 1 (at most 80),
+// copied once into LDS (zero rows outside the context), and computes Z for
+// those 80 rows: wave w takes channels c0 + 16 w .. + 15, its W^T fragments
+// for all D held in registers (from a transposed copy of W), the 5 row
+// tiles' X fragments read from LDS per 32-deep step.  Each Z element is one
+// matrix-core dot product over d in a fixed order, whatever the block, so an
+// entry comes out bitwise the same from a chunk with a halo as from the
+// whole context.  Z goes to LDS; then each thread pools entries for its
+// channel as the fp32 kernel does, the window's values read from the staged
+// rows.
 constexpr int CZ_ROWS = 80;  // 5 tiles of 16 rows: EPB m + m <= 64 + 16
+constexpr int CZ_CH = 128;   // channels of a block
+constexpr int CZ_NT = 64 * (CZ_CH / 16);
 
 __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t *__restrict__ w, int D,
                                                         uint16_t *__restrict__ wt) {
@@ -124,19 +128,40 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t *__restri
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_compress_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wt,
-                                                       const float *__restrict__ bias, int64_t rows, int64_t n_out,
-                                                       int m, int halo, uint16_t *__restrict__ out) {
+__global__ __launch_bounds__(CZ_NT) void k_compress_mfma(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wt,
+                                                         const float *__restrict__ bias, int64_t rows, int64_t n_out,
+                                                         int m, int halo, uint16_t *__restrict__ out) {
     constexpr int KS = D / 32;
     constexpr int RT = CZ_ROWS / 16;
-    constexpr int ZS = 64 + 1;
+    constexpr int XS = D + 8;       // LDS stride of a staged row (16-bit elements)
+    constexpr int ZS = CZ_CH + 1;
+    constexpr int PPR = D / 8;      // 16-byte pieces of a row
+    constexpr int XP = CZ_ROWS * PPR, XPT = (XP + CZ_NT - 1) / CZ_NT;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[CZ_ROWS * XS];
     __shared__ float zs[CZ_ROWS * ZS];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
     const int epb = 64 / m;
     const int64_t e0 = (int64_t)blockIdx.y * epb;
-    const int c0 = blockIdx.x * 64;
+    const int c0 = blockIdx.x * CZ_CH;
     const int64_t r0 = halo ? e0 * m : (e0 - 1) * m;  // token row of window position 0 of entry e0
+    // the window rows, 16 bytes a thread per round (rows outside the context are zero)
+    {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        u32x4 v[XPT];
+#pragma unroll
+        for (int i = 0; i < XPT; i++) {
+            const int pc = tid + CZ_NT * i;
+            const int lr = pc / PPR, cc = pc % PPR;
+            const int64_t r = r0 + lr;
+            v[i] = (pc < XP && r >= 0 && r < rows) ? *reinterpret_cast<const u32x4 *>(x + (size_t)r * D + 8 * cc) : zero;
+        }
+#pragma unroll
+        for (int i = 0; i < XPT; i++) {
+            const int pc = tid + CZ_NT * i;
+            if (pc < XP) *reinterpret_cast<u32x4 *>(xs + (pc / PPR) * XS + (pc % PPR) * 8) = v[i];
+        }
+    }
     // W^T fragments of this wave's 16 channels: B[d][c] = W[d][c] = Wt[c][d]
     u32x4 bw[KS];
     {
@@ -144,33 +169,18 @@ __global__ __launch_bounds__(256) void k_compress_mfma(const uint16_t *__restric
 #pragma unroll
         for (int s2 = 0; s2 < KS; s2++) bw[s2] = *reinterpret_cast<const u32x4 *>(wr + 32 * s2);
     }
+    __syncthreads();
     f32x4 acc[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; rt++) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const uint16_t *xr[RT];
-    bool ok[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; rt++) {
-        const int64_t r = r0 + 16 * rt + col;
-        ok[rt] = r >= 0 && r < rows;
-        xr[rt] = x + (size_t)(ok[rt] ? r : 0) * D + 8 * kg;
-    }
-    // X fragments two steps ahead of the matrix cores (three register sets,
-    // named statically: the loop is fully unrolled, so bw stays in registers)
-    u32x4 a[3][RT];
-    auto load_a = [&](int set, int s2) {
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++) a[set][rt] = ok[rt] ? *reinterpret_cast<const u32x4 *>(xr[rt] + 32 * s2) : zero;
-    };
-    load_a(0, 0);
-    load_a(1, 1);
 #pragma unroll
     for (int s2 = 0; s2 < KS; s2++) {
-        if (s2 + 2 < KS) load_a((s2 + 2) % 3, s2 + 2);
+        u32x4 a[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++) a[rt] = *reinterpret_cast<const u32x4 *>(xs + (16 * rt + col) * XS + 32 * s2 + 8 * kg);
 #pragma unroll
         for (int rt = 0; rt < RT; rt++)
-            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s2 % 3][rt]),
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[rt]),
                                                              __builtin_bit_cast(bf16x8, bw[s2]), acc[rt], 0, 0, 0);
     }
     // Z[row 16 rt + 4 kg + i][channel 16 wave + col] -> LDS
@@ -179,9 +189,9 @@ __global__ __launch_bounds__(256) void k_compress_mfma(const uint16_t *__restric
 #pragma unroll
         for (int i = 0; i < 4; i++) zs[(16 * rt + 4 * kg + i) * ZS + 16 * wave + col] = acc[rt][i];
     __syncthreads();
-    // pooling: thread -> channel c0 + (tid % 64), entries e0 + tid / 64 + 4 j
-    const int cl = threadIdx.x & 63, c = c0 + cl;
-    for (int el = threadIdx.x >> 6; el < epb; el += 4) {
+    // pooling: thread -> channel c0 + (tid % CZ_CH), entries e0 + tid / CZ_CH + (CZ_NT / CZ_CH) j
+    const int cl = tid % CZ_CH, c = c0 + cl;
+    for (int el = tid / CZ_CH; el < epb; el += CZ_NT / CZ_CH) {
         const int64_t i = e0 + el;
         if (i >= n_out) break;
         const int lr0 = el * m;  // local row of window position 0 (rows from r0)
@@ -200,7 +210,7 @@ __global__ __launch_bounds__(256) void k_compress_mfma(const uint16_t *__restric
             if (t < 0) continue;
             const float p = expf(l[r] - mx);
             den += p;
-            a = fmaf(p, bf16_to_f32(x[(size_t)t * D + c]), a);
+            a = fmaf(p, bf16_to_f32(xs[(lr0 + r) * XS + c]), a);
         }
         out[(size_t)i * D + c] = f32_to_bf16_rne(a / den);
     }
@@ -229,12 +239,12 @@ void compress_run(const void *x, int dt, int64_t n_out, int D, int m, int halo, 
                            static_cast<const uint16_t *>(wz), D, wt);
         check_launch("compression weights transpose");
         const int epb = 64 / m;
-        const dim3 g(D / 64, (unsigned)((n_out + epb - 1) / epb));
+        const dim3 g(D / CZ_CH, (unsigned)((n_out + epb - 1) / epb));
         if (D == 512)
-            hipLaunchKernelGGL(k_compress_mfma<512>, g, dim3(256), 0, s, static_cast<const uint16_t *>(x), wt, bias,
+            hipLaunchKernelGGL(k_compress_mfma<512>, g, dim3(CZ_NT), 0, s, static_cast<const uint16_t *>(x), wt, bias,
                                rows, n_out, m, halo, static_cast<uint16_t *>(out));
         else
-            hipLaunchKernelGGL(k_compress_mfma<128>, g, dim3(256), 0, s, static_cast<const uint16_t *>(x), wt, bias,
+            hipLaunchKernelGGL(k_compress_mfma<128>, g, dim3(CZ_NT), 0, s, static_cast<const uint16_t *>(x), wt, bias,
                                rows, n_out, m, halo, static_cast<uint16_t *>(out));
         check_launch("compression (matrix cores)");
         return;
