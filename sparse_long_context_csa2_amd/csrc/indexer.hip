@@ -70,6 +70,12 @@ __device__ void reduce_tile_stat(float smin, float smax, uint32_t nval, float km
 typedef float __attribute__((ext_vector_type(2))) idx_f32x2;
 typedef __bf16 __attribute__((ext_vector_type(2))) idx_bf16x2;  // converted to with round-to-nearest-even
 
+// ReLU of a matrix-core result as one integer maximum on its bits: a float
+// whose sign bit is set is a negative integer, so max(bits, 0) keeps x >= +0
+// and gives +0 for negatives (the float maximum would first canonicalize x
+// for NaNs, a second instruction per value).
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <int DI>
 __device__ __forceinline__ u32x4 fp4_keys_to_bf16x8(uint32_t word, uint32_t sbyte) {
     // scale = pow2 * f: the conversion instruction applies the power of two,
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
 #pragma unroll
         for (int ht = 0; ht < HT; ht++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
+            for (int r = 0; r < 4; r++) part = fmaf(wv[ht][r], relu_bits(acc[ht][r]), part);
         part = bfly32(bfly16(part, OpAdd{}), OpAdd{});
         // squared norm of key row (l%16), from the B fragments already in registers
         float ss = 0.f;
@@ -420,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
 #pragma unroll
             for (int ht = 0; ht < HT; ht++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) p = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), p);
+                for (int r = 0; r < 4; r++) p = fmaf(wv[ht][r], relu_bits(acc[ht][r]), p);
             part[g] = p;
             // keep each group's reload where it is: hoisting them all would need a second buffer
             __builtin_amdgcn_sched_barrier(0);
@@ -678,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t *__rest
 #pragma unroll
             for (int ht = 0; ht < HT; ht++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.f), part);
+                for (int r = 0; r < 4; r++) part = fmaf(wv[ht][r], relu_bits(acc[ht][r]), part);
             part = bfly32(bfly16(part, OpAdd{}), OpAdd{});
             const bool valid = g * 16 < rem_vis;
             if (kg == 0 && g * 16 < rem_n) srow[g * 16] = valid ? part : NEG_INF;
