@@ -588,6 +588,7 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t *__rest
     __shared__ __attribute__((aligned(16))) uint16_t qs[2][HI * QRS];
     __shared__ float wsh[2][HI];
     __shared__ f32x4 stp[PF_QT][4];             // per query and wave: smin, smax, kmax2, count
+    __shared__ int64_t nvis_sh[PF_QT];          // per query: visible slots (one 64-bit division each, once)
     const int tile = blockIdx.x;
     const int qtiles = (Q + PF_QT - 1) / PF_QT;
     const int b = blockIdx.y / qtiles;
@@ -646,11 +647,12 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t *__rest
         kn[g] = bfly32(bfly16(ss, OpAdd{}), OpAdd{});
     }
     put_q(0, qr[0], wr[0]);
+    if ((int)threadIdx.x < nq) nvis_sh[threadIdx.x] = visible_entries(q_pos, bq0 + threadIdx.x, m, N);
 
     auto score_query = [&](int qi) {
         const int buf = qi & 1;
         const int bq = bq0 + qi;
-        const int64_t nvis = visible_entries(q_pos, bq, m, N);
+        const int64_t nvis = nvis_sh[qi];
         u32x4 qa[HT][KS];
 #pragma unroll
         for (int ht = 0; ht < HT; ht++)
