@@ -907,6 +907,12 @@ __device__ __forceinline__ void copy16_to_lds(const uint16_t *src, uint16_t *dst
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
+// A block barrier that orders the block's own LDS reads and writes only:
+// __syncthreads() is a workgroup fence, which also waits for the global->LDS
+// row copies still in flight (they count as LDS writes), so a barrier in the
+// middle of a tile would wait for the next tile's rows.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int D, int HPW, int HH>
 __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__restrict__ q,
                                                            const uint16_t *__restrict__ kv, int Q, int H, int64_t N,
@@ -923,12 +929,19 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
     constexpr int PST = TROWS + 8;     // P row stride
     constexpr int QS = D + 8;
     static_assert(D == 512, "one bf16 row is one 64-lane load of 16 bytes");
-    static_assert(HB * QS <= 2 * TROWS * LS, "query staging fits the row buffers");
-    __shared__ __attribute__((aligned(16))) uint16_t rows_lds[2][TROWS * LS];
+    static_assert(HB * QS <= TROWS * LS, "query staging fits a row buffer");
+    // two row buffers (and entry lists) as separate LDS variables, each named
+    // statically below: the compiler then knows that reading one does not
+    // alias the global->LDS copies in flight into the other, and does not wait
+    // for them (with one array indexed by the tile's parity it waited for the
+    // next tile's rows before every tile)
+    __shared__ __attribute__((aligned(16))) uint16_t rows_a[TROWS * LS];
+    __shared__ __attribute__((aligned(16))) uint16_t rows_b[TROWS * LS];
     __shared__ __attribute__((aligned(16))) uint16_t p_lds[HB * PST];
     __shared__ float mx_sh[4][HB];
     __shared__ float l_sh[4][HB];
-    __shared__ __attribute__((aligned(16))) int32_t jsh[2][TROWS];
+    __shared__ __attribute__((aligned(16))) int32_t jsh_a[TROWS];
+    __shared__ __attribute__((aligned(16))) int32_t jsh_b[TROWS];
 
     // block L on XCD L % 8: consecutive queries (which share most of their
     // rows) on one XCD, the head groups of a query beside them
@@ -953,7 +966,7 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
         u32x4 qst[QPT];
 #pragma unroll
         for (int i = 0; i < QPT; i++) qst[i] = qsrc[QP % NT == 0 ? tid + NT * i : min(tid + NT * i, QP - 1)];
-        uint16_t *qs = &rows_lds[0][0];
+        uint16_t *qs = rows_a;
 #pragma unroll
         for (int i = 0; i < QPT; i++) {
             const int pc = tid + NT * i;
@@ -962,7 +975,7 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
     }
     for (int e = tid; e < TROWS; e += NT) {
         const int j = e < k ? irow[e] : -1;
-        jsh[0][e] = (j >= 0 && j < N) ? j : -1;
+        jsh_a[e] = (j >= 0 && j < N) ? j : -1;
     }
     __syncthreads();
     u32x4 qf[HT][KS];
@@ -970,25 +983,25 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
     for (int ht = 0; ht < HT; ht++)
 #pragma unroll
         for (int s2 = 0; s2 < KS; s2++)
-            qf[ht][s2] = *reinterpret_cast<const u32x4 *>(&rows_lds[0][0] + (hw0 + 16 * ht + col) * QS + 32 * s2 + 8 * kg);
+            qf[ht][s2] = *reinterpret_cast<const u32x4 *>(rows_a + (hw0 + 16 * ht + col) * QS + 32 * s2 + 8 * kg);
     __syncthreads();  // the row buffers are free
 
-    // rows of tile t into buffer b: wave w copies rows w, w + NW, ...; an entry
-    // of -1 copies row 0 (masked later)
-    auto issue = [&](int b, const int32_t *js) {
+    // rows of a tile into buffer dst: wave w copies rows w, w + NW, ...; an
+    // entry of -1 copies row 0 (masked later)
+    auto issue = [&](uint16_t *dst, const int32_t *js) {
 #pragma unroll
         for (int r = wave; r < TROWS; r += NW) {
             const int j = __builtin_amdgcn_readfirstlane(js[r]);
             const uint16_t *src = kvb + (size_t)(j >= 0 ? j : 0) * D + 8 * lane;
-            copy16_to_lds(src, &rows_lds[b][r * LS]);
+            copy16_to_lds(src, dst + r * LS);
         }
     };
-    issue(0, jsh[0]);
-    int jn = -1;  // next tile's entry of this thread (tid < TROWS)
-    if (tid < TROWS && TROWS + tid < k) {
-        const int j = irow[TROWS + tid];
-        jn = (j >= 0 && j < N) ? j : -1;
-    }
+    issue(rows_a, jsh_a);
+    // next tile's entry of this thread (tid < TROWS), as loaded: range-checked
+    // only when it goes to LDS after the tile's wait, so that checking it does
+    // not wait for the row copies issued before it
+    int jn = -1;
+    if (tid < TROWS && TROWS + tid < k) jn = irow[TROWS + tid];
 
     f32x4 oacc[DT][HT];
 #pragma unroll
@@ -1002,22 +1015,19 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
         l_run[ht] = 0.f;
     }
 
-    for (int t = 0; t < ntl; t++) {
-        const int cur = t & 1;
+    // tile t from rows / jcur while tile t + 1 is copied into nrows / jnext
+    auto step = [&](int t, const uint16_t *__restrict__ rows, const int32_t *__restrict__ jcur,
+                    uint16_t *__restrict__ nrows, int32_t *__restrict__ jnext) __attribute__((always_inline)) {
         // this tile's rows (and the next tile's entries) have landed
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (tid < TROWS) jsh[cur ^ 1][tid] = jn;
+        if (tid < TROWS) jnext[tid] = (jn >= 0 && jn < N) ? jn : -1;
         __syncthreads();
         if (t + 1 < ntl) {
-            issue(cur ^ 1, jsh[cur ^ 1]);
+            issue(nrows, jnext);
             jn = -1;
             const int e = (t + 2) * TROWS + tid;
-            if (tid < TROWS && e < k) {
-                const int j = irow[e];
-                jn = (j >= 0 && j < N) ? j : -1;
-            }
+            if (tid < TROWS && e < k) jn = irow[e];
         }
-        const uint16_t *rows = rows_lds[cur];
 
         // S^T for rows 16 rq + 4 kg + i, heads hw0 + 16 ht + col
         f32x4 sacc[HT];
@@ -1032,7 +1042,7 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
                 for (int ht = 0; ht < HT; ht++) sacc[ht] = mma<CSA2_BF16>(a0, qf[ht][s2], sacc[ht]);
             }
         }
-        const int4 jv = *reinterpret_cast<const int4 *>(&jsh[cur][16 * rq + 4 * kg]);
+        const int4 jv = *reinterpret_cast<const int4 *>(&jcur[16 * rq + 4 * kg]);
         const int jj[4] = {jv.x, jv.y, jv.z, jv.w};
 #pragma unroll
         for (int ht = 0; ht < HT; ht++) {
@@ -1046,7 +1056,7 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
             mt = bfly32(bfly16(mt, OpMax{}), OpMax{});
             if (kg == 0) mx_sh[rq][hw0 + 16 * ht + col] = mt;
         }
-        __syncthreads();
+        lds_barrier();
         float alpha[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ht++) {
@@ -1068,7 +1078,7 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
             ls = bfly32(bfly16(ls, OpAdd{}), OpAdd{});
             if (kg == 0) l_sh[rq][hd] = ls;
         }
-        __syncthreads();
+        lds_barrier();
         // O^T[channel][head] += C^T P^T for channels rq DQ + 16 dt + (lane rows)
         // (the accumulators are rescaled only when some head's maximum moved:
         // after the first tiles that is rare, and multiplying by 1 is exact)
@@ -1113,13 +1123,17 @@ __global__ __launch_bounds__(256 * HH, 1) void k_attn_tiles(const uint16_t *__re
                 for (int ht = 0; ht < HT; ht++) oacc[dt][ht] = mma<CSA2_BF16>(av, pb[ht], oacc[dt][ht]);
             }
         }
+    };
+    for (int t = 0; t < ntl; t++) {
+        const bool odd = t & 1;
+        step(t, odd ? rows_b : rows_a, odd ? jsh_b : jsh_a, odd ? rows_a : rows_b, odd ? jsh_a : jsh_b);
     }
 
     // ---- output: out / l in bf16, staged as [head][channel] in the free row
     // buffer, written as whole rows; lse = m + ln l
     __syncthreads();
     constexpr int OS = D + 8;
-    uint16_t *stage = &rows_lds[0][0];
+    uint16_t *stage = rows_a;
 #pragma unroll
     for (int ht = 0; ht < HT; ht++) {
         const int hd = hw0 + 16 * ht + col;
