@@ -190,7 +190,9 @@ CSA2_API int csa2_index_score(const void *qI, const float *w, const void *kI, in
  *   entries, which the pool produced by csa2_layer is -- not checked).
  *   A slot a query may not select (past its visible count, or an empty
  *   candidate) is given as a -inf score, which is how csa2_index_score marks
- *   invisible entries; there is no separate per-query valid count.
+ *   invisible entries; there is no separate per-query valid count.  Scores
+ *   must not be NaN (a NaN has no place in the order; the result is then
+ *   unspecified).
  * idx [B,Q,k] int32 out; count [B,Q] int32 out or NULL.  1 <= k.
  * The result is bit-exact (pure comparison, no arithmetic on the scores).
  * ------------------------------------------------------------------------- */

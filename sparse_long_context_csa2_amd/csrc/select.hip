@@ -53,6 +53,29 @@ __device__ __forceinline__ int sel_bin(float v, float lo, float inv) {
     return (int)t;
 }
 
+// Counts the scores v[] (-inf: no score; finite ones within [lo, hi]) into
+// hist[0 .. NB-1] by sel_bin, where inv = NB / (hi - lo) or 0.  When inv is
+// finite and > 0 (block-uniform; then hi - lo is finite too, else inv would
+// be 0), v - lo lies in [0, hi - lo] and (v - lo) inv is never NaN for a
+// finite v: clamped to [-1, NB-1] and truncated it is sel_bin's bin for every
+// finite score and -1 for -inf, so no branch per score (the -inf ones go to
+// the spare word hist[-1]).  Otherwise (no finite score, a range of one value
+// or one whose width or inverse overflows) each score takes sel_bin itself.
+template <int NV>
+__device__ __forceinline__ void sel_count(const float (&v)[NV], float lo, float inv, uint32_t *hist) {
+    if (inv > 0.f && inv <= __FLT_MAX__) {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const float t = (v[i] - lo) * inv;
+            atomicAdd(&hist[(int)fminf(fmaxf(t, -1.f), (float)(NB - 1))], 1u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; i++)
+            if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
+    }
+}
+
 __device__ __forceinline__ bool slot_score(const float *scores, const int32_t *cand, int64_t base, int64_t slot,
                                            int64_t n, float &v) {
     if (slot >= n) return false;
@@ -192,7 +215,8 @@ __global__ __launch_bounds__(256) void k_sel_range(const TileStat *__restrict__ 
 __global__ __launch_bounds__(256) void k_sel_hist(const float *__restrict__ scores, const int32_t *__restrict__ cand,
                                                   int64_t n, const SelQuery *__restrict__ sq,
                                                   uint32_t *__restrict__ qhist) {
-    __shared__ uint32_t hist[NB];
+    __shared__ uint32_t hist_w[NB + 1];
+    uint32_t *hist = hist_w + 1;  // hist[-1]: the spare word of sel_count
     const int bq = blockIdx.y;
     for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
     const float lo = sq[bq].lo, inv = sq[bq].inv;
@@ -216,9 +240,7 @@ __global__ __launch_bounds__(256) void k_sel_hist(const float *__restrict__ scor
                 if (sl < n && cand[base + sl] < 0) v[i] = NEG_INF;
             }
         }
-#pragma unroll
-        for (int i = 0; i < CH / 256; i++)
-            if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
+        sel_count(v, lo, inv, hist);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < NB; i += 256) {
@@ -1035,7 +1057,8 @@ __device__ uint32_t edge_key(uint32_t lk, uint32_t hk, int target, float lo, flo
 template <bool CERT>
 __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     static_assert(NB == 2 * ONE_NT, "a thread takes two bins of the suffix scan");
-    __shared__ uint32_t hist[NB];
+    __shared__ uint32_t hist_w[NB + 1];
+    uint32_t *hist = hist_w + 1;  // hist[-1]: the spare word of sel_count
     __shared__ uint32_t bm[ONE_N / 32];
     __shared__ uint32_t red[ONE_NT / 64];
     __shared__ f32x4 rred[ONE_NT / 64];
@@ -1151,9 +1174,7 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     const float inv = (nvalid > 0 && hi - lo > 0.f) ? (float)NB / (hi - lo) : 0.f;
 
     // histogram from registers
-#pragma unroll
-    for (int i = 0; i < ONE_SPT; i++)
-        if (v[i] != NEG_INF) atomicAdd(&hist[sel_bin(v[i], lo, inv)], 1u);
+    sel_count(v, lo, inv, hist);
     if constexpr (CERT) {
         if (a.qI) {
 #pragma unroll
