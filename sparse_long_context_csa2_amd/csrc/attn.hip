@@ -36,13 +36,10 @@ __device__ __forceinline__ uint32_t e2m1_bits(uint32_t c) {
     const uint32_t mag = e ? (((e + 126u) << 23) | (mb << 22)) : (mb ? 0x3f000000u : 0u);
     return mag | ((c & 8u) << 28);
 }
-// FP4 row scale byte -> float: its E4M3 ("FN") value (bias 7; exponent field
-// 0 is m * 2^-9), except the NaN code S.1111.111, which saturates to +-448.
+// FP4 row scale byte -> float: its E4M3 ("FN") value, the NaN code
+// S.1111.111 saturating to +-448 (branch-free, see e4m3_mag_bits).
 __device__ __forceinline__ float e4m3_val(uint32_t s) {
-    const uint32_t e = (s >> 3) & 15u, mt = s & 7u;
-    float mag = e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0.001953125f;
-    if ((s & 0x7fu) == 0x7fu) mag = 448.f;
-    return (s & 0x80u) ? -mag : mag;
+    return __uint_as_float(e4m3_mag_bits(s) | ((s & 0x80u) << 24));
 }
 __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
     const _Float16 ha = (_Float16)a, hb = (_Float16)b;
@@ -85,14 +82,9 @@ typedef _Float16 __attribute__((ext_vector_type(2))) f16x2;
 // its mantissa (1 + m/8, at most 3 bits); every product has <= 5 significant
 // bits and a magnitude in [2^-10, 2688], so both steps are exact.
 __device__ __forceinline__ u32x4 fp4_word_to_f16x8(uint32_t word, uint32_t sbyte) {
-    const float s = e4m3_val(sbyte);
-    const uint32_t sb = __float_as_uint(s);
-    float pow2 = __uint_as_float(sb & 0x7f800000u);
-    uint32_t fbits = 0x3c00u | ((sb >> 13) & 0x3ffu) | ((sb >> 16) & 0x8000u);
-    if (s == 0.f) {
-        pow2 = 1.f;
-        fbits = 0u;
-    }
+    const uint32_t mag = e4m3_mag_bits(sbyte);
+    const float pow2 = __uint_as_float(mag ? mag & 0x7f800000u : 0x3f800000u);
+    const uint32_t fbits = mag ? 0x3c00u | ((mag >> 13) & 0x3ffu) | ((sbyte & 0x80u) << 8) : 0u;
     const f16x2 f = __builtin_bit_cast(f16x2, fbits | (fbits << 16));
     const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 0) * f;
     const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, pow2, 1) * f;

@@ -63,6 +63,19 @@ struct Carve {
 };
 
 // ------------------------------------------------------------ device bits
+// FP4 row scale byte (E4M3FN: bias 7, exponent field 0 = m 2^-9) -> its
+// magnitude as binary32 bits, the NaN code S.1111.111 taken as 448 = 2^8 x 1.75
+// (one corrupt byte must not turn a row into NaNs).  Both encodings are formed
+// and one is selected, so the decode has no branch: written as a conditional
+// value it compiled to a divergent branch per scale byte.
+__device__ __forceinline__ uint32_t e4m3_mag_bits(uint32_t sbyte) {
+    const uint32_t e = (sbyte >> 3) & 15u;
+    const uint32_t m = (sbyte & 0x7fu) == 0x7fu ? 6u : (sbyte & 7u);
+    const uint32_t nbits = ((e + 120u) << 23) | (m << 20);           // exponent field >= 1
+    const uint32_t sbits = __float_as_uint((float)m * 0.001953125f);  // exponent field 0
+    return e ? nbits : sbits;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
 // Round-to-nearest-even fp32 -> bf16 bits (inputs are finite).

@@ -81,14 +81,9 @@ __device__ __forceinline__ u32x4 fp4_keys_to_bf16x8(uint32_t word, uint32_t sbyt
     // scale = pow2 * f: the conversion instruction applies the power of two,
     // an fp32 multiply the mantissa factor f = +-1.mmm (at most 4 significant
     // bits); every product is exact, and so is its bf16 rounding
-    // (the E4M3 NaN code S.1111.111 saturates to +-448)
-    const uint32_t e = (sbyte >> 3) & 15u, mt = sbyte & 7u;
-    float sc = e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0.001953125f;
-    if ((sbyte & 0x7fu) == 0x7fu) sc = 448.f;
-    if (sbyte & 0x80u) sc = -sc;
-    const uint32_t sb = __float_as_uint(sc);
-    const float pow2 = __uint_as_float(sb & 0x7f800000u);
-    const float f = sc == 0.f ? 0.f : __uint_as_float((sb & 0x807fffffu) | 0x3f800000u);
+    const uint32_t mag = e4m3_mag_bits(sbyte);
+    const float pow2 = __uint_as_float(mag & 0x7f800000u);
+    const float f = mag ? __uint_as_float((mag & 0x007fffffu) | 0x3f800000u | ((sbyte & 0x80u) << 24)) : 0.f;
     u32x4 r;
     idx_f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, pow2, 0);
     idx_f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, pow2, 1);
