@@ -58,16 +58,21 @@ __device__ __forceinline__ int sel_bin(float v, float lo, float inv) {
 // finite and > 0 (block-uniform; then hi - lo is finite too, else inv would
 // be 0), v - lo lies in [0, hi - lo] and (v - lo) inv is never NaN for a
 // finite v: clamped to [-1, NB-1] and truncated it is sel_bin's bin for every
-// finite score and -1 for -inf, so no branch per score (the -inf ones go to
-// the spare word hist[-1]).  Otherwise (no finite score, a range of one value
-// or one whose width or inverse overflows) each score takes sel_bin itself.
+// finite score and -1 for -inf, so no branch per score.  A -inf goes to the
+// lane's own spare word hist[NB + lane] (hist holds NB + 64 words): slots with
+// no score (past n, outside the candidates, not yet visible) can be most of a
+// block's, and one shared spare word would serialize their atomics.
+// Otherwise (no finite score, a range of one value or one whose width or
+// inverse overflows) each score takes sel_bin itself.
+constexpr int NB_SPARE = 64;
 template <int NV>
 __device__ __forceinline__ void sel_count(const float (&v)[NV], float lo, float inv, uint32_t *hist) {
     if (inv > 0.f && inv <= __FLT_MAX__) {
+        const int spare = NB + (int)(threadIdx.x & 63);
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const float t = (v[i] - lo) * inv;
-            atomicAdd(&hist[(int)fminf(fmaxf(t, -1.f), (float)(NB - 1))], 1u);
+            const int bn = (int)fminf(fmaxf((v[i] - lo) * inv, -1.f), (float)(NB - 1));
+            atomicAdd(&hist[bn < 0 ? spare : bn], 1u);
         }
     } else {
 #pragma unroll
@@ -215,8 +220,7 @@ __global__ __launch_bounds__(256) void k_sel_range(const TileStat *__restrict__ 
 __global__ __launch_bounds__(256) void k_sel_hist(const float *__restrict__ scores, const int32_t *__restrict__ cand,
                                                   int64_t n, const SelQuery *__restrict__ sq,
                                                   uint32_t *__restrict__ qhist) {
-    __shared__ uint32_t hist_w[NB + 1];
-    uint32_t *hist = hist_w + 1;  // hist[-1]: the spare word of sel_count
+    __shared__ uint32_t hist[NB + NB_SPARE];  // bins, then sel_count's spare words
     const int bq = blockIdx.y;
     for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
     const float lo = sq[bq].lo, inv = sq[bq].inv;
@@ -1057,8 +1061,7 @@ __device__ uint32_t edge_key(uint32_t lk, uint32_t hk, int target, float lo, flo
 template <bool CERT>
 __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     static_assert(NB == 2 * ONE_NT, "a thread takes two bins of the suffix scan");
-    __shared__ uint32_t hist_w[NB + 1];
-    uint32_t *hist = hist_w + 1;  // hist[-1]: the spare word of sel_count
+    __shared__ uint32_t hist[NB + NB_SPARE];  // bins, then sel_count's spare words
     __shared__ uint32_t bm[ONE_N / 32];
     __shared__ uint32_t red[ONE_NT / 64];
     __shared__ f32x4 rred[ONE_NT / 64];
@@ -1173,8 +1176,8 @@ __global__ __launch_bounds__(ONE_NT) void k_sel_one(OneArgs a) {
     }
     const float inv = (nvalid > 0 && hi - lo > 0.f) ? (float)NB / (hi - lo) : 0.f;
 
-    // histogram from registers
-    sel_count(v, lo, inv, hist);
+    // histogram from registers (a thread whose slots all lie past n has none)
+    if (s0 < n) sel_count(v, lo, inv, hist);
     if constexpr (CERT) {
         if (a.qI) {
 #pragma unroll
