@@ -175,6 +175,41 @@ __global__ __launch_bounds__(256) void k_attn_combine(const uint16_t *__restrict
 
 // ------------------------------------------------------------ VALU kernel
 // Any head count, dim and format: one block per (query, head), fp32 math.
+// The logits of entries t0, t0 + 256, ... and O = sum p C over a fixed KV
+// element type (FMT), so that the unrolled loops keep their row loads in
+// flight together; loads are unconditional (a skipped entry reads row 0) and
+// only the arithmetic is masked.
+template <int FMT>
+__device__ __forceinline__ float valu_logits(const float *qs, const uint8_t *kvb, int64_t rb, int D, int64_t N,
+                                             const int32_t *irow, int k, float scale, float *as) {
+    float mx = NEG_INF;
+    for (int t = threadIdx.x; t < k; t += 256) {
+        const int32_t j = irow[t];
+        const bool ok = j >= 0 && j < N;
+        const uint8_t *row = kvb + (size_t)(ok ? j : 0) * rb;
+        float dot = 0.f;
+#pragma unroll 8
+        for (int d = 0; d < D; d++) dot = fmaf(qs[d], kv_elem(row, FMT, D, d), dot);
+        const float a = ok ? scale * dot : NEG_INF;
+        as[t] = a;
+        mx = fmaxf(mx, a);
+    }
+    return mx;
+}
+template <int FMT>
+__device__ __forceinline__ float valu_out(const uint8_t *kvb, int64_t rb, int D, int64_t N, const int32_t *irow,
+                                          int k, const float *as, int d) {
+    float acc = 0.f;
+#pragma unroll 8
+    for (int t = 0; t < k; t++) {
+        const int32_t j = irow[t];
+        const bool ok = j >= 0 && j < N;
+        const float v = kv_elem(kvb + (size_t)(ok ? j : 0) * rb, FMT, D, d);
+        if (ok && as[t] != 0.f) acc = fmaf(as[t], v, acc);
+    }
+    return acc;
+}
+
 __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, int q_dt,
                                                    const uint8_t *__restrict__ kv, int kv_dt, int Q, int H, int D,
                                                    int64_t N, const int32_t *__restrict__ idx, int k, float scale,
@@ -192,19 +227,9 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
                                  : bf16_to_f32(static_cast<const uint16_t *>(q)[qoff + d]);
     __syncthreads();
     const int32_t *irow = idx + (size_t)bq * k;
-    float mx = NEG_INF;
-    for (int t = threadIdx.x; t < k; t += 256) {
-        const int32_t j = irow[t];
-        float a = NEG_INF;
-        if (j >= 0 && j < N) {
-            const uint8_t *row = kvb + (size_t)j * rb;
-            float dot = 0.f;
-            for (int d = 0; d < D; d++) dot = fmaf(qs[d], kv_elem(row, kv_dt, D, d), dot);
-            a = scale * dot;
-        }
-        as[t] = a;
-        mx = fmaxf(mx, a);
-    }
+    float mx = kv_dt == CSA2_F32    ? valu_logits<CSA2_F32>(qs, kvb, rb, D, N, irow, k, scale, as)
+               : kv_dt == CSA2_BF16 ? valu_logits<CSA2_BF16>(qs, kvb, rb, D, N, irow, k, scale, as)
+                                    : valu_logits<CSA2_FP4>(qs, kvb, rb, D, N, irow, k, scale, as);
     red[threadIdx.x] = mx;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
@@ -227,11 +252,9 @@ __global__ __launch_bounds__(256) void k_attn_valu(const void *__restrict__ q, i
     }
     const float Z = red[0];
     for (int d = threadIdx.x; d < D; d += 256) {
-        float acc = 0.f;
-        for (int t = 0; t < k; t++) {
-            const int32_t j = irow[t];
-            if (j >= 0 && j < N && as[t] != 0.f) acc = fmaf(as[t], kv_elem(kvb + (size_t)j * rb, kv_dt, D, d), acc);
-        }
+        const float acc = kv_dt == CSA2_F32    ? valu_out<CSA2_F32>(kvb, rb, D, N, irow, k, as, d)
+                          : kv_dt == CSA2_BF16 ? valu_out<CSA2_BF16>(kvb, rb, D, N, irow, k, as, d)
+                                               : valu_out<CSA2_FP4>(kvb, rb, D, N, irow, k, as, d);
         const float v = Z > 0.f ? acc / Z : 0.f;
         if (q_dt == CSA2_F32) static_cast<float *>(out)[qoff + d] = v;
         else static_cast<uint16_t *>(out)[qoff + d] = f32_to_bf16_rne(v);

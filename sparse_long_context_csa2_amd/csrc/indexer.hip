@@ -471,6 +471,25 @@ __global__ __launch_bounds__(256, 2) void k_index_stream(const uint16_t *__restr
 // ---------------------------------------------------------------- VALU path
 // Any head count / dim / dtype: one slot per thread, fp32 FMA in sequential
 // order, query heads staged in LDS as fp32.
+// One slot's score: fp32 FMAs in sequential order (d, then h), the key
+// element type fixed per instantiation so that the unrolled loop has its key
+// loads in flight together rather than one dependent load per step.
+template <bool F32>
+__device__ __forceinline__ void valu_slot_score(const float *qs, const float *wq, const void *kI, size_t base, int HI,
+                                                int dI, float &s, float &ss) {
+    for (int h = 0; h < HI; h++) {
+        float dot = 0.f;
+#pragma unroll 8
+        for (int d = 0; d < dI; d++) {
+            const float kv = F32 ? static_cast<const float *>(kI)[base + d]
+                                 : bf16_to_f32(static_cast<const uint16_t *>(kI)[base + d]);
+            dot = fmaf(qs[h * dI + d], kv, dot);
+            if (h == 0) ss = fmaf(kv, kv, ss);
+        }
+        s = fmaf(wq[h], fmaxf(dot, 0.f), s);
+    }
+}
+
 __global__ __launch_bounds__(256) void k_index_valu(const void *__restrict__ qI, int dt, const float *__restrict__ w,
                                                     const void *__restrict__ kI, int Q, int HI, int dI, int64_t N,
                                                     const int64_t *__restrict__ q_pos, int m,
@@ -495,16 +514,8 @@ __global__ __launch_bounds__(256) void k_index_valu(const void *__restrict__ qI,
     float s = 0.f, ss = 0.f;
     if (valid) {
         const size_t base = ((size_t)b * N + j) * dI;
-        for (int h = 0; h < HI; h++) {
-            float dot = 0.f;
-            for (int d = 0; d < dI; d++) {
-                float kv = dt == CSA2_F32 ? static_cast<const float *>(kI)[base + d]
-                                          : bf16_to_f32(static_cast<const uint16_t *>(kI)[base + d]);
-                dot = fmaf(qs[h * dI + d], kv, dot);
-                if (h == 0) ss = fmaf(kv, kv, ss);
-            }
-            s = fmaf(w[(size_t)bq * HI + h], fmaxf(dot, 0.f), s);
-        }
+        if (dt == CSA2_F32) valu_slot_score<true>(qs, w + (size_t)bq * HI, kI, base, HI, dI, s, ss);
+        else valu_slot_score<false>(qs, w + (size_t)bq * HI, kI, base, HI, dI, s, ss);
     }
     if (slot < n) scores[(int64_t)bq * n + slot] = valid ? s : NEG_INF;
     reduce_tile_stat(valid ? s : POS_INF, valid ? s : NEG_INF, valid ? 1u : 0u, valid ? ss : 0.f,
