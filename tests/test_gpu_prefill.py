@@ -108,3 +108,24 @@ def test_prefill_full_layer_with_pool(b, score_fmt):
     q_pos = torch.arange(T - spec.Q, T, dtype=torch.int64).view(1, spec.Q).repeat(spec.B, 1)
     q_pos[0] -= 777
     run_group(b, d, q_pos=q_pos)
+
+
+@pytest.mark.parametrize("idx_dtype,kv_fmt,score_fmt", [
+    ("bf16", "bf16", "f64"),
+    ("bf16", "bf16", "bf16"),
+    ("f32", "f32", "f64"),
+])
+def test_many_queries_band_rescoring(b, idx_dtype, kv_fmt, score_fmt):
+    """320 query rows (2 x 160 causal tokens): the band rescoring's grid has
+    one block per query, which walks its band in rounds.  A Full layer with a
+    pool (two targets' bands) and a Reindex layer over that pool (slots mapped
+    through the candidates): idx, pool and count bit-exact, outputs within
+    tolerance."""
+    from gpu_helpers import run_group
+    spec = synth.Decode(B=2, Q=160, N=1500, HI=64, dI=128, H=16, D=128, k=150, P=400, seed=93,
+                        idx_dtype=idx_dtype, kv_fmt=kv_fmt, layers=["FULL", "REINDEX"], score_fmt=score_fmt)
+    d = synth.make_decode(spec)
+    T = spec.N * spec.m
+    q_pos = torch.arange(T - spec.Q, T, dtype=torch.int64).view(1, spec.Q).repeat(spec.B, 1)
+    q_pos[1] -= 333
+    run_group(b, d, q_pos=q_pos)
