@@ -988,11 +988,12 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t c, uint32_t *re
     return pre + inc - c;
 }
 
-// The band rescoring inside the one-block selection, with ONE_NT / 64
-// replicas of each query's block: every replica classified the same slots,
-// so each holds the same band lists (target 0's, then target 1's, each in
-// slot order, at positions from the block scan).  Replica r rescores the
-// band entries of wave r's words (2048 slots): the wave lists them in LDS
+// The band rescoring inside the one-block selection, with F * ONE_NT / 64
+// replicas of each query's block (F = 1, 2 or 4): every replica classified
+// the same slots, so each holds the same band lists (target 0's, then target
+// 1's, each in slot order, at positions from the block scan).  Replica r
+// rescores the band entries of lanes r % F of F equal lane ranges of wave
+// r / F (2048 / F slots): that wave lists them in LDS
 // (slot, target, position) by a wave scan, the key rows are staged in LDS as
 // binary64 OR_CH at a time, and each wave computes RS_EPW entries' scores in
 // the definition's order (rs_wave_scores), as the rescoring kernel does.
@@ -1007,14 +1008,20 @@ __device__ void one_rescore(const OneArgs &a, int bq, int rep, int s0, uint32_t 
     const int b = bq / a.Q;
     const int nvec = a.dI * ESZ / 16;
     const size_t row0 = (size_t)bq * a.band_cap, row1 = ((size_t)gridDim.x + bq) * a.band_cap;
-    if (wave == rep) {
+    // replica rep takes the band entries of lanes [l0, l0 + 64 / F) of wave
+    // rep / F (F = replicas per wave, gridDim.y / 16): their slots
+    const int F = (int)gridDim.y / (ONE_NT / 64);
+    const int l0 = (rep % F) * (64 / F);
+    if (wave == rep / F) {
         // entry: slot | target << 15 | position << 16 (slots and positions < 32,768)
-        const uint32_t c0 = (uint32_t)__builtin_popcount(kw0), c1 = (uint32_t)__builtin_popcount(kw1);
+        const bool mine = lane >= l0 && lane < l0 + 64 / F;
+        const uint32_t c0 = mine ? (uint32_t)__builtin_popcount(kw0) : 0u;
+        const uint32_t c1 = mine ? (uint32_t)__builtin_popcount(kw1) : 0u;
         const uint32_t incl = wave_incl_scan_u32(c0 + c1);
         uint32_t o = incl - c0 - c1;
         int32_t p0 = kp0, p1 = kp1;
-        for (uint32_t m = kw0; m; m &= m - 1) ents[o++] = (uint32_t)(s0 + __builtin_ctz(m)) | ((uint32_t)p0++ << 16);
-        for (uint32_t m = kw1; m; m &= m - 1)
+        for (uint32_t m = mine ? kw0 : 0u; m; m &= m - 1) ents[o++] = (uint32_t)(s0 + __builtin_ctz(m)) | ((uint32_t)p0++ << 16);
+        for (uint32_t m = mine ? kw1 : 0u; m; m &= m - 1)
             ents[o++] = (uint32_t)(s0 + __builtin_ctz(m)) | (1u << 15) | ((uint32_t)p1++ << 16);
         if (lane == 63) *nent_sh = (int32_t)incl;
     }
@@ -1694,13 +1701,18 @@ size_t sel_workspace(const SelPlan &p, bool own_stats) {
 
 // Replicas of each query's one-block selection that share its band
 // rescoring (0: the rescoring kernel does it): one per wave of the block
-// (replica r takes wave r's words) with at most 16 queries, rows the staged
+// (replica r takes wave r's words), or per half or quarter of a wave's lanes
+// with at most 8 or 4 queries, with at most 16 queries, rows the staged
 // rescoring takes (at most RS_ROWB bytes), certified selection.
 static int one_rescore_replicas(const SelPlan &p, const RescoreArgs *rs) {
     if (!p.certified || !rs || !small_path(p)) return 0;
     const int rowb = rs->dI * (rs->dt == CSA2_F32 ? 4 : 2);
     if (rowb > RS_ROWB) return 0;
-    return p.BQ <= 16 ? ONE_NT / 64 : 0;
+    if (p.BQ > 16) return 0;
+    // one replica per wave's slots, or per half or quarter of a wave's lanes
+    // when there are few queries, so that the grid still fills the chip
+    const int f = p.BQ <= 4 ? 4 : (p.BQ <= 8 ? 2 : 1);
+    return f * (ONE_NT / 64);
 }
 
 void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const TileStat *stats_in,

@@ -115,9 +115,10 @@ def test_fp4_indexer_keys_full_pool_reindex(b, N):
 @pytest.mark.parametrize("score_fmt", ["f64", "bf16"])
 def test_selection_paths_agree_across_batch_sizes(b, score_fmt):
     """Up to 16 queries the band's binary64 rescoring runs inside the one-block
-    selection kernel (16 replicas of each query's block); with more queries a
-    separate rescoring kernel does it.  17 queries and their first 16 alone
-    must select the same sets and pools, and give the same outputs bit for bit."""
+    selection kernel (16 replicas of each query's block, 32 with at most 8
+    queries, 64 with at most 4); with more queries a separate rescoring kernel
+    does it.  17 queries and their first 16, 8 and 4 alone must select the
+    same sets and pools, and give the same outputs bit for bit."""
     spec = synth.Decode(B=17, Q=1, N=6000, HI=64, dI=128, H=64, D=512, k=512, P=1024, seed=21, layers=["FULL"],
                         score_fmt=score_fmt)
     d = synth.make_decode(spec)
@@ -128,10 +129,12 @@ def test_selection_paths_agree_across_batch_sizes(b, score_fmt):
                        qI=dev(lay["qI"][:nb]), w=dev(lay["w"][:nb]), kI=dev(d["kI"][:nb]), m=spec.m, P=spec.P,
                        score_fmt=score_fmt)
 
-    g17, g16 = run(17), run(16)
-    torch.cuda.synchronize()
-    for key in ("idx", "count", "pool", "out", "lse"):
-        assert torch.equal(host(g17[key])[:16], host(g16[key])), key
+    g17 = run(17)
+    for nb in (16, 8, 4):
+        g = run(nb)
+        torch.cuda.synchronize()
+        for key in ("idx", "count", "pool", "out", "lse"):
+            assert torch.equal(host(g17[key])[:nb], host(g[key])), (nb, key)
     r = oracle.layer("FULL", q=lay["q"], kv=d["kv"], k=spec.k, scale=spec.scale, qI=lay["qI"], w=lay["w"], kI=d["kI"],
                      m=spec.m, P=spec.P, score_key=score_fmt)
     assert np.array_equal(host(g17["idx"]).numpy(), r["idx"])
