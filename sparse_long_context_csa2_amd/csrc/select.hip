@@ -217,6 +217,7 @@ __global__ __launch_bounds__(256) void k_sel_range(const TileStat *__restrict__ 
 // Each 8192-slot chunk counts its scores' bins in LDS (slot CH c + t + 256 i
 // in thread t: coalesced loads, all in flight before the counting) and adds
 // its nonzero bins to the query's histogram.
+template <int CPB>
 __global__ __launch_bounds__(256) void k_sel_hist(const float *__restrict__ scores, const int32_t *__restrict__ cand,
                                                   int64_t n, const SelQuery *__restrict__ sq,
                                                   uint32_t *__restrict__ qhist) {
@@ -226,10 +227,11 @@ __global__ __launch_bounds__(256) void k_sel_hist(const float *__restrict__ scor
     const float lo = sq[bq].lo, inv = sq[bq].inv;
     const int64_t base = (int64_t)bq * n;
     __syncthreads();
-    // HIST_CPB consecutive chunks per block into one LDS histogram, so that
-    // fewer partial histograms are added into the query's
-    for (int c = 0; c < HIST_CPB; c++) {
-        const int64_t s0 = ((int64_t)blockIdx.x * HIST_CPB + c) * CH + threadIdx.x;
+    // CPB consecutive chunks per block into one LDS histogram, so that fewer
+    // partial histograms are added into the query's (one chunk per block when
+    // there are too few chunks to fill the chip otherwise)
+    for (int c = 0; c < CPB; c++) {
+        const int64_t s0 = ((int64_t)blockIdx.x * CPB + c) * CH + threadIdx.x;
         if (s0 - threadIdx.x >= n) break;
         float v[CH / 256];
 #pragma unroll
@@ -355,7 +357,7 @@ __device__ __forceinline__ float f32_up(double d) {
 // The counts meet per block first and reach the query record with one atomic
 // update per block and target: the records are shared by every block of a
 // query, and per-wave updates of one address queue up.
-constexpr int CLS_WPT = 4;
+constexpr int CLS_WPT_MAX = 4;  // words per thread (1 when there are too few words to fill the chip otherwise)
 
 __device__ __forceinline__ void load_word_scores(const float *sp, const int32_t *cp, int64_t s0, int64_t n,
                                                  float *v) {
@@ -384,6 +386,7 @@ __device__ __forceinline__ void load_word_scores(const float *sp, const int32_t 
     }
 }
 
+template <int CLS_WPT>
 __global__ __launch_bounds__(256) void k_sel_classify(const float *__restrict__ scores,
                                                       const int32_t *__restrict__ cand, int64_t n, int ntgt,
                                                       SelQuery *__restrict__ sq, uint32_t *__restrict__ bitmap,
@@ -1785,14 +1788,23 @@ void sel_run(const SelPlan &p, const float *scores, const int32_t *cand, const T
                            p.certified ? rs->sumwq : nullptr, p.certified ? rs->HI : 0, p.certified ? rs->dI : 0,
                            p.certified ? ebuf : nullptr, p.certified && p.bf16key ? 1 : 0);
         check_launch("selection range");
-        hipLaunchKernelGGL(k_sel_hist, dim3((p.nchunks + HIST_CPB - 1) / HIST_CPB, p.BQ), dim3(256), 0, s, scores,
-                           cand, p.n, sq, qhist);
+        // few queries: smaller blocks of work, so that the grid still fills the chip
+        const bool few = (int64_t)p.BQ * ((p.nchunks + HIST_CPB - 1) / HIST_CPB) < 256;
+        if (few)
+            hipLaunchKernelGGL(k_sel_hist<1>, dim3(p.nchunks, p.BQ), dim3(256), 0, s, scores, cand, p.n, sq, qhist);
+        else
+            hipLaunchKernelGGL(k_sel_hist<HIST_CPB>, dim3((p.nchunks + HIST_CPB - 1) / HIST_CPB, p.BQ), dim3(256), 0,
+                               s, scores, cand, p.n, sq, qhist);
         check_launch("selection histogram");
         hipLaunchKernelGGL(k_sel_find, dim3(p.BQ), dim3(256), 0, s, qhist, p.K0, p.K1, p.certified ? ebuf : nullptr, sq);
         check_launch("selection find");
-        const int nblk = (int)((p.nwords + 256 * CLS_WPT - 1) / (256 * CLS_WPT));
-        hipLaunchKernelGGL(k_sel_classify, dim3(nblk, p.BQ), dim3(256), 0, s, scores, cand, p.n, p.ntgt, sq, bitmap,
-                           p.nwords, band, p.band_cap);
+        const int nblk4 = (int)((p.nwords + 256 * CLS_WPT_MAX - 1) / (256 * CLS_WPT_MAX));
+        if ((int64_t)p.BQ * nblk4 < 256)
+            hipLaunchKernelGGL(k_sel_classify<1>, dim3((unsigned)((p.nwords + 255) / 256), p.BQ), dim3(256), 0, s,
+                               scores, cand, p.n, p.ntgt, sq, bitmap, p.nwords, band, p.band_cap);
+        else
+            hipLaunchKernelGGL(k_sel_classify<CLS_WPT_MAX>, dim3(nblk4, p.BQ), dim3(256), 0, s, scores, cand, p.n,
+                               p.ntgt, sq, bitmap, p.nwords, band, p.band_cap);
         check_launch("selection classify");
     }
     if (p.certified && !(small_path(p) && one_rescore_replicas(p, rs))) {
