@@ -666,7 +666,7 @@ __device__ void finish_target(uint32_t *bm, int64_t nwords, int64_t n, int32_t K
                               const int32_t *list, const double *bs, const float *scores_q,
                               const int32_t *cand_q, int32_t *dst, int32_t *count_dst, uint64_t *key_lds,
                               int32_t *slot_lds, int32_t *out_lds, int out_cap, uint32_t *red,
-                              bool preloaded = false) {
+                              bool preloaded = false, bool bm_global = false) {
     const int32_t r = K - in_cnt;
     auto exact_key = [&](int32_t i) -> uint64_t { return dkey(bs ? bs[i] : (double)scores_q[list[i]]); };
     if (r > 0 && nb > 0 && r < nb && nb > 256 && nb <= 2 * NT) {
@@ -744,9 +744,10 @@ __device__ void finish_target(uint32_t *bm, int64_t nwords, int64_t n, int32_t K
             }
         }
     }
-    // the picks (global atomics when the bitmap is not in LDS) are complete and
-    // visible before the bitmap is read
-    __threadfence();
+    // the picks are complete and visible before the bitmap is read: LDS
+    // atomics by the barrier alone; global ones (a bitmap too large for LDS)
+    // after a device fence, which costs microseconds and is skipped otherwise
+    if (bm_global) __threadfence();
     __syncthreads();
     compact_bits<NT>(bm, nwords, K, cand_q, dst, count_dst, out_lds, out_cap, red);
 }
@@ -1655,7 +1656,7 @@ __global__ __launch_bounds__(FIN_NT) void k_sel_finish(FinishArgs a) {
             __syncthreads();
         }
         finish_target<FIN_NT>(bm, a.nwords, a.n, t.K, t.in_cnt, t.band_cnt, list, bs, sq_scores, cq, dst, cdst,
-                              key_lds, slot_lds, out_lds, FIN_OUT, red);
+                              key_lds, slot_lds, out_lds, FIN_OUT, red, false, bm == gbm);
     }
 }
 
