@@ -1014,7 +1014,7 @@ __device__ void one_rescore(const OneArgs &a, int bq, int rep, int s0, uint32_t 
     const size_t row0 = (size_t)bq * a.band_cap, row1 = ((size_t)gridDim.x + bq) * a.band_cap;
     // replica rep takes the band entries of lanes [l0, l0 + 64 / F) of wave
     // rep / F (F = replicas per wave, gridDim.y / 16): their slots
-    const int F = (int)gridDim.y / (ONE_NT / 64);
+    const int F = max(1, (int)gridDim.y / (ONE_NT / 64));
     const int l0 = (rep % F) * (64 / F);
     if (wave == rep / F) {
         // entry: slot | target << 15 | position << 16 (slots and positions < 32,768)
