@@ -732,9 +732,13 @@ __global__ __launch_bounds__(256, 2) void k_index_prefill(const uint16_t *__rest
         t.nvalid = (uint32_t)(stp[qi][0][3] + stp[qi][1][3] + stp[qi][2][3] + stp[qi][3][3]);
         stats[(size_t)(bq0 + qi) * ntiles + tile] = t;
     }
-    if (sumwq && tile == 0) {
+    // sum_h |w_h| ||q_h|| of the block's query tokens, one per key tile: the
+    // block of tile x takes token x (and x + ntiles, ...).  All of them in the
+    // first tile's block held that block, and with it the launch, back by a
+    // serial loop over 32 tokens.
+    if (sumwq) {
         __shared__ double dred[256 / 16];
-        for (int qi = 0; qi < nq; qi++) {
+        for (int qi = tile; qi < nq; qi += (int)gridDim.x) {
             const double v = block_sumwq<256>(qI, CSA2_BF16, w, HI, DI, bq0 + qi, dred);
             if (threadIdx.x == 0) sumwq[bq0 + qi] = v;
         }
