@@ -178,6 +178,35 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
     for (int ht = 0; ht < HT; ht++)
 #pragma unroll
         for (int r = 0; r < 4; r++) wv[ht][r] = w[(size_t)bq * HI + ht * 16 + 4 * kg + r];
+    // sum_h |w_h| ||q_h|| in binary64 from the query fragments in registers,
+    // while the key rows are in flight: in the query's first tile, wave x takes
+    // head tiles x, x + 4, ..., and thread 0 adds the tiles' terms after the
+    // tile statistics' barrier (a block-wide pass over the query rows at the
+    // end of that tile held the launch open).  Fixed order: lane partials,
+    // then kg pairs, then a butterfly over col, then ht.
+    __shared__ double swq_sh[HT];
+    if (sumwq && tile == 0) {
+        const int wu = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) {
+            if (ht % 4 != wu) continue;
+            double q2 = 0.0;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; s2++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const double x0 = (double)bf16_to_f32((uint16_t)(qa[ht][s2][e] & 0xffffu));
+                    const double x1 = (double)bf16_to_f32((uint16_t)(qa[ht][s2][e] >> 16));
+                    q2 = fma(x0, x0, q2);
+                    q2 = fma(x1, x1, q2);
+                }
+            q2 += __shfl_xor(q2, 16);
+            q2 += __shfl_xor(q2, 32);
+            double t = fabs((double)w[(size_t)bq * HI + ht * 16 + col]) * sqrt(q2);
+            for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o);
+            if (lane == 0) swq_sh[ht] = t;
+        }
+    }
 
     float smin = POS_INF, smax = NEG_INF, kmax2 = 0.f;
     uint32_t nval = 0;
@@ -222,11 +251,12 @@ __global__ __launch_bounds__(256, 2) void k_index_mfma(const uint16_t *__restric
             nval += (kg == 0);
         }
     }
-    reduce_tile_stat(smin, smax, nval, kmax2, stats + (size_t)bq * ntiles + tile);
-    if (sumwq && tile == 0) {
-        __shared__ double dred[256 / 16];
-        const double v = block_sumwq<256>(qI, CSA2_BF16, w, HI, DI, bq, dred);
-        if (threadIdx.x == 0) sumwq[bq] = v;
+    reduce_tile_stat(smin, smax, nval, kmax2, stats + (size_t)bq * ntiles + tile);  // ends with a barrier
+    if (sumwq && tile == 0 && threadIdx.x == 0) {
+        double acc = 0.0;
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++) acc += swq_sh[ht];
+        sumwq[bq] = acc;
     }
 }
 
