@@ -37,6 +37,7 @@ sys.path.insert(0, HERE)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, published
+SPIN_CYCLES = 2_000_000      # torch.cuda._sleep ahead of a timed batch: about 1 ms at the shader clock
 COPY_BYTES = 1 << 30         # counter calibration: bytes read and written by one plain copy
 C2 = dict(B=16, Q=1, N=32768, HI=64, dI=128, H=64, D=512, k=2048, m=4, ctx_tokens=131072)
 WORKLOADS = ["decode-128k", "tiny-c1", "decode-128k-fp4-group", "hier-1m", "prefill-c5", "decode-128k-fp4idx",
@@ -61,15 +62,22 @@ def parse():
 # ------------------------------------------------------------------ timing
 
 def event_time(torch, fn, reps):
-    """Mean duration (ms) of fn(i) bracketed by HIP events on the current stream."""
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        starts[i].record()
-        fn(i)
-        ends[i].record()
+    """Mean duration (ms) per call of fn(i) over `reps` calls issued back to
+    back between two HIP events on the current stream (the gaps between
+    launches included).  A spin kernel queued ahead of the first event keeps
+    the GPU busy while the host queues the calls, so that host-side call
+    overhead does not show up as idle time, and the events' own cost is paid
+    once rather than per call."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps
+    torch.cuda._sleep(SPIN_CYCLES)
+    start.record()
+    for i in range(reps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
 
 
 def wall_time(torch, fn, warmup, steps):
